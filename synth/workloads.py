@@ -1,0 +1,119 @@
+"""The five synthetic mixed-step workloads and their seeded structure draws.
+
+Shared, as input data only, by the oracle harness and the HIP harness.  Nothing here schedules,
+rotates or attends: a workload is a list of running decodes (with the context each already has
+in the cache), a FCFS list of prompts, a token budget, a block pool and the head geometry.
+
+Structure draws use ``numpy.random.Generator(PCG64(seed))`` in a fixed order: decode contexts,
+then prompt lengths, then the physical free-list permutation.  Contexts are integer-uniform on
+inclusive ranges; prompt lengths in the log-normal workload are ``exp(N(ln 6000, 0.5))`` rounded
+half-to-even and clipped to ``[1, 16384]``.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    dtype: str                  # "f32" or "bf16": storage type of q, k, v, caches and output
+    Hq: int
+    Hkv: int
+    D: int
+    block_size: int
+    budget: int                 # token budget per step
+    decode_ctx: tuple           # tokens already cached for each running decode
+    prompts: tuple              # (prompt_len, cached_len) in FCFS order
+    num_blocks: int
+    free_list: tuple | None     # physical block allocation order; None = 0..num_blocks-1
+    steps: int | None           # None: run until every prompt has had its last chunk
+    seed: int
+    max_steps: int = 64
+
+    @property
+    def group(self) -> int:
+        return self.Hq // self.Hkv
+
+    @property
+    def num_decodes(self) -> int:
+        return len(self.decode_ctx)
+
+    def request_ids(self):
+        """Request indices: decodes 0..nd-1 in order, then prompts in FCFS order."""
+        nd = len(self.decode_ctx)
+        return list(range(nd)), list(range(nd, nd + len(self.prompts)))
+
+    def max_position(self) -> int:
+        """An upper bound on any absolute position the run can touch."""
+        s = self.max_steps if self.steps is None else self.steps
+        m = max([c + s for c in self.decode_ctx] + [L + s for L, _ in self.prompts] + [1])
+        return m + 1
+
+
+def _pool_size(decode_ctx, prompts, bs, steps) -> int:
+    n = sum(-(-(c + steps) // bs) for c in decode_ctx)
+    n += sum(-(-(L + steps) // bs) for L, _ in prompts)
+    return n + 8
+
+
+def _make(name, dtype, Hq, Hkv, D, bs, budget, decode_ctx, prompts, steps, seed, rng,
+          identity_free_list=False, max_steps=64):
+    decode_ctx = tuple(int(c) for c in decode_ctx)
+    prompts = tuple((int(L), int(c)) for L, c in prompts)
+    s = max_steps if steps is None else steps
+    nb = _pool_size(decode_ctx, prompts, bs, s)
+    free = None if identity_free_list else tuple(int(b) for b in rng.permutation(nb))
+    return Workload(name, dtype, Hq, Hkv, D, bs, budget, decode_ctx, prompts, nb, free, steps,
+                    seed, max_steps)
+
+
+def config1() -> Workload:
+    """Budget-8 worked example: 3 decodes (16/20/24 cached) and one 12-token prompt, fp32."""
+    rng = np.random.Generator(np.random.PCG64(1001))
+    return _make("cfg1_worked_example_f32", "f32", 4, 4, 64, 16, 8, (16, 20, 24), ((12, 0),),
+                 4, 1001, rng, identity_free_list=True)
+
+
+def config2() -> Workload:
+    """7B-like layer: 32/32 heads, D 128, block 16; 64 decodes U{512..4096}; 4096 prompt; B 512."""
+    rng = np.random.Generator(np.random.PCG64(1002))
+    ctx = rng.integers(512, 4096, size=64, endpoint=True)
+    return _make("cfg2_7b_b512_bf16", "bf16", 32, 32, 128, 16, 512, ctx, ((4096, 0),), 10,
+                 1002, rng)
+
+
+def config3() -> Workload:
+    """13B-like layer: 40/40 heads; 32 decodes at 2048; one 4096 prompt; B 544 (C = 512)."""
+    rng = np.random.Generator(np.random.PCG64(1003))
+    return _make("cfg3_13b_b544_bf16", "bf16", 40, 40, 128, 16, 544, [2048] * 32, ((4096, 0),),
+                 9, 1003, rng)
+
+
+def config4() -> Workload:
+    """GQA 34B-like layer: 56/8 heads; 128 decodes U{1024..8192}; 8 log-normal prompts; B 2048."""
+    rng = np.random.Generator(np.random.PCG64(1004))
+    ctx = rng.integers(1024, 8192, size=128, endpoint=True)
+    z = rng.normal(math.log(6000.0), 0.5, size=8)
+    lens = np.clip(np.rint(np.exp(z)), 1, 16384).astype(np.int64)
+    return _make("cfg4_gqa34b_b2048_bf16", "bf16", 56, 8, 128, 16, 2048, ctx,
+                 tuple((int(L), 0) for L in lens), None, 1004, rng, max_steps=64)
+
+
+def config5() -> Workload:
+    """Long context: 64/8 heads, block 32; 256 decodes U{1024..32768}; a 2048-token chunk after
+    a 262,144-token cached prefix; B 8192."""
+    rng = np.random.Generator(np.random.PCG64(1005))
+    ctx = rng.integers(1024, 32768, size=256, endpoint=True)
+    return _make("cfg5_longctx_b8192_bf16", "bf16", 64, 8, 128, 32, 8192, ctx,
+                 ((262144 + 2048, 262144),), 1, 1005, rng)
+
+
+CONFIGS = {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}
+
+
+def get(i: int) -> Workload:
+    return CONFIGS[i]()
