@@ -1,0 +1,288 @@
+"""Thin ctypes binding of libcb.so (include/cb.h).  Argument marshalling only.
+
+Every function here has the name of the C entry point it calls and forwards to it: torch tensors
+become raw pointers (host or device), the HIP stream defaults to torch's current stream on the
+tensor's device, and a non-zero status becomes a ``CbError``.  No part of the step is computed in
+Python: scheduling runs in the C++ builder and all device work in the library's HIP kernels.
+Loading fails loudly when libcb.so has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libcb.so")
+
+CB_OK, CB_ERR_INVALID, CB_ERR_DECODE_OVER_BUDGET, CB_ERR_OUT_OF_BLOCKS, CB_ERR_CAPACITY, CB_ERR_HIP = (
+    0, -1, -2, -3, -4, -5)
+CB_F32, CB_BF16 = 0, 1
+
+_i32, _i64, _sz, _vp, _f32, _f64 = (ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t,
+                                    ctypes.c_void_p, ctypes.c_float, ctypes.c_double)
+_pi32 = ctypes.POINTER(ctypes.c_int32)
+
+
+class CbError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {_lib().cb_status_string(status).decode()} (status {status})")
+
+
+class cb_sched_config(ctypes.Structure):
+    _fields_ = [("block_size", _i32), ("num_blocks", _i32), ("free_list", _pi32), ("max_chunk", _i32)]
+
+
+class cb_step(ctypes.Structure):
+    _fields_ = [("cap_seqs", _i32), ("cap_tokens", _i32), ("cap_blocks", _i32),
+                ("seq_ids", _pi32), ("cu_seqlens_q", _pi32), ("context_lens", _pi32),
+                ("cu_blocks", _pi32), ("block_table", _pi32), ("positions", _pi32),
+                ("slot_mapping", _pi32),
+                ("num_seqs", _i32), ("num_decodes", _i32), ("num_tokens", _i32),
+                ("num_prefill_tokens", _i32), ("unused_tokens", _i32), ("max_q_len", _i32),
+                ("max_context_len", _i32), ("max_decode_context_len", _i32),
+                ("num_blocks_emitted", _i32)]
+
+
+_LIB = None
+
+EXPORTS = {
+    "cb_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "cb_sched_create": (ctypes.c_int, [ctypes.POINTER(cb_sched_config), ctypes.POINTER(_vp)]),
+    "cb_sched_destroy": (None, [_vp]),
+    "cb_sched_clone": (ctypes.c_int, [_vp, ctypes.POINTER(_vp)]),
+    "cb_sched_add_running": (ctypes.c_int, [_vp, _i32, _pi32]),
+    "cb_sched_add_prompt": (ctypes.c_int, [_vp, _i32, _i32, _pi32]),
+    "cb_sched_get_blocks": (ctypes.c_int, [_vp, _i32, _pi32, _i32, _pi32]),
+    "cb_sched_pending_prompts": (ctypes.c_int, [_vp, _pi32]),
+    "cb_sched_free_blocks": (ctypes.c_int, [_vp, _pi32]),
+    "cb_build_step": (ctypes.c_int, [_vp, _i32, ctypes.POINTER(cb_step)]),
+    "cb_rope_cos_sin": (ctypes.c_int, [ctypes.POINTER(ctypes.c_float), _i32, _i32, _f64]),
+    "cb_rope_kv_append": (ctypes.c_int, [_vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp,
+                                         _vp, _vp, _vp, _i32, _vp, _vp, _vp, _i64]),
+    "cb_attn_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32]),
+    "cb_mixed_paged_attention": (ctypes.c_int, [_vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                                _i32, _i32, _i32, _i32, _f32, _vp, _vp, _vp, _vp,
+                                                _vp, _vp, _vp, _vp, _vp, _sz]),
+    "cb_mixed_paged_attention_timed": (ctypes.c_int, [_vp, _i32, _i32, _i32, _i32, _i32, _i32,
+                                                      _i32, _i32, _i32, _i32, _i32, _f32, _vp,
+                                                      _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                                      _sz, ctypes.POINTER(_vp)]),
+}
+
+
+def _lib():
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run `python -m chunked_prefill_mixed_decode_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in EXPORTS.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = lib
+    return _LIB
+
+
+def _check(status: int, where: str):
+    if status != CB_OK:
+        raise CbError(status, where)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _i32ptr(t):
+    return ctypes.cast(ctypes.c_void_p(t.data_ptr()), _pi32)
+
+
+def _stream(t, stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.float32:
+        return CB_F32
+    if dt == torch.bfloat16:
+        return CB_BF16
+    raise ValueError(f"unsupported element type {dt}")
+
+
+# ---- host builder ------------------------------------------------------------------------------
+
+class Sched:
+    """Owner of one ``cb_sched`` (freed with the object)."""
+
+    def __init__(self, handle):
+        self.handle = handle
+
+    def __del__(self):
+        if getattr(self, "handle", None) and _LIB is not None:
+            _LIB.cb_sched_destroy(self.handle)
+            self.handle = None
+
+
+def cb_sched_create(block_size: int, num_blocks: int, free_list=None, max_chunk: int = 0) -> Sched:
+    cfg = cb_sched_config(block_size, num_blocks, None, max_chunk)
+    keep = None
+    if free_list is not None:
+        keep = (ctypes.c_int32 * len(free_list))(*free_list)
+        cfg.free_list = ctypes.cast(keep, _pi32)
+    h = _vp()
+    _check(_lib().cb_sched_create(ctypes.byref(cfg), ctypes.byref(h)), "cb_sched_create")
+    return Sched(h)
+
+
+def cb_sched_clone(s: Sched) -> Sched:
+    h = _vp()
+    _check(_lib().cb_sched_clone(s.handle, ctypes.byref(h)), "cb_sched_clone")
+    return Sched(h)
+
+
+def cb_sched_add_running(s: Sched, context_len: int) -> int:
+    rid = ctypes.c_int32()
+    _check(_lib().cb_sched_add_running(s.handle, context_len, ctypes.byref(rid)), "cb_sched_add_running")
+    return rid.value
+
+
+def cb_sched_add_prompt(s: Sched, prompt_len: int, cached_len: int = 0) -> int:
+    rid = ctypes.c_int32()
+    _check(_lib().cb_sched_add_prompt(s.handle, prompt_len, cached_len, ctypes.byref(rid)),
+           "cb_sched_add_prompt")
+    return rid.value
+
+
+def cb_sched_get_blocks(s: Sched, req_id: int) -> list[int]:
+    n = ctypes.c_int32()
+    st = _lib().cb_sched_get_blocks(s.handle, req_id, None, 0, ctypes.byref(n))
+    if st not in (CB_OK, CB_ERR_CAPACITY):
+        _check(st, "cb_sched_get_blocks")
+    buf = (ctypes.c_int32 * max(n.value, 1))()
+    _check(_lib().cb_sched_get_blocks(s.handle, req_id, buf, n.value, ctypes.byref(n)), "cb_sched_get_blocks")
+    return list(buf[:n.value])
+
+
+def cb_sched_pending_prompts(s: Sched) -> int:
+    n = ctypes.c_int32()
+    _check(_lib().cb_sched_pending_prompts(s.handle, ctypes.byref(n)), "cb_sched_pending_prompts")
+    return n.value
+
+
+def cb_sched_free_blocks(s: Sched) -> int:
+    n = ctypes.c_int32()
+    _check(_lib().cb_sched_free_blocks(s.handle, ctypes.byref(n)), "cb_sched_free_blocks")
+    return n.value
+
+
+STEP_ARRAYS = ("seq_ids", "cu_seqlens_q", "context_lens", "cu_blocks", "block_table",
+               "positions", "slot_mapping")
+STEP_SCALARS = ("num_seqs", "num_decodes", "num_tokens", "num_prefill_tokens", "unused_tokens",
+                "max_q_len", "max_context_len", "max_decode_context_len", "num_blocks_emitted")
+
+
+class StepBuffers:
+    """Host int32 arrays that cb_build_step fills, packed in one flat buffer (pinned when a GPU is
+    present) so that a step's metadata reaches the device in a single asynchronous copy."""
+
+    def __init__(self, cap_seqs: int, cap_tokens: int, cap_blocks: int, pin: bool | None = None):
+        if pin is None:
+            pin = torch.cuda.is_available()
+        self.cap = (cap_seqs, cap_tokens, cap_blocks)
+        sizes = {"seq_ids": cap_seqs, "cu_seqlens_q": cap_seqs + 1, "context_lens": cap_seqs,
+                 "cu_blocks": cap_seqs + 1, "block_table": max(cap_blocks, 1),
+                 "positions": max(cap_tokens, 1), "slot_mapping": max(cap_tokens, 1)}
+        self.offsets = {}
+        off = 0
+        for k in STEP_ARRAYS:
+            self.offsets[k] = off
+            off += (sizes[k] + 63) // 64 * 64          # 256-byte aligned sub-arrays
+        self.flat = torch.zeros(off, dtype=torch.int32, pin_memory=pin)
+        self.arrays = {k: self.flat[self.offsets[k]:self.offsets[k] + sizes[k]] for k in STEP_ARRAYS}
+        self.step = cb_step()
+        for k, t in self.arrays.items():
+            setattr(self.step, k, _i32ptr(t))
+
+
+@dataclasses.dataclass
+class StepMeta:
+    """Scalars of a built step plus views of its host arrays (valid until the next build)."""
+    num_seqs: int
+    num_decodes: int
+    num_tokens: int
+    num_prefill_tokens: int
+    unused_tokens: int
+    max_q_len: int
+    max_context_len: int
+    max_decode_context_len: int
+    num_blocks_emitted: int
+    host: dict
+
+    def lengths(self) -> dict:
+        return {"seq_ids": self.num_seqs, "cu_seqlens_q": self.num_seqs + 1,
+                "context_lens": self.num_seqs, "cu_blocks": self.num_seqs + 1,
+                "block_table": self.num_blocks_emitted, "positions": self.num_tokens,
+                "slot_mapping": self.num_tokens}
+
+
+def cb_build_step(s: Sched, token_budget: int, buf: StepBuffers) -> StepMeta:
+    st = buf.step
+    st.cap_seqs, st.cap_tokens, st.cap_blocks = buf.cap
+    _check(_lib().cb_build_step(s.handle, token_budget, ctypes.byref(st)), "cb_build_step")
+    scal = {k: getattr(st, k) for k in STEP_SCALARS}
+    meta = StepMeta(**scal, host={})
+    meta.host = {k: buf.arrays[k][:n] for k, n in meta.lengths().items()}
+    return meta
+
+
+# ---- rotary table (host) ------------------------------------------------------------------------
+
+def cb_rope_cos_sin(max_pos: int, D: int, base: float = 10000.0) -> torch.Tensor:
+    out = torch.empty((max_pos, D), dtype=torch.float32)
+    _check(_lib().cb_rope_cos_sin(ctypes.cast(ctypes.c_void_p(out.data_ptr()), ctypes.POINTER(ctypes.c_float)),
+                                  max_pos, D, base), "cb_rope_cos_sin")
+    return out
+
+
+# ---- device ops ----------------------------------------------------------------------------------
+
+def cb_rope_kv_append(q, k, v, positions, slot_mapping, cos_sin, q_out, k_cache, v_cache,
+                      stream=None):
+    """q, q_out [T, Hq, D] (q may be None); k, v [T, Hkv, D]; caches [nb, Hkv, bs, D]."""
+    T, Hkv, D = k.shape
+    Hq = q.shape[1] if q is not None else 0
+    nb, _, bs, _ = k_cache.shape
+    _check(_lib().cb_rope_kv_append(
+        _stream(k, stream), dtype_code(k.dtype), T, max(Hq, 1), Hkv, D, bs, _ptr(q), _ptr(k), _ptr(v),
+        _ptr(positions), _ptr(slot_mapping), _ptr(cos_sin), cos_sin.shape[0], _ptr(q_out),
+        _ptr(k_cache), _ptr(v_cache), nb), "cb_rope_kv_append")
+
+
+def cb_attn_workspace_bytes(num_seqs, num_decodes, T, max_q_len, max_decode_ctx, max_ctx, Hq, Hkv, D) -> int:
+    return int(_lib().cb_attn_workspace_bytes(num_seqs, num_decodes, T, max_q_len, max_decode_ctx,
+                                              max_ctx, Hq, Hkv, D))
+
+
+def cb_mixed_paged_attention(q, k_cache, v_cache, cu_seqlens_q, context_lens, cu_blocks,
+                             block_table, out, workspace, *, num_seqs, num_decodes, max_q_len,
+                             max_decode_ctx, max_ctx, scale, stream=None, events=None):
+    """q, out [T, Hq, D]; caches [nb, Hkv, bs, D]; int32 metadata on the device."""
+    T, Hq, D = q.shape
+    _, Hkv, bs, _ = k_cache.shape
+    args = (_stream(q, stream), dtype_code(q.dtype), num_seqs, num_decodes, T, max_q_len,
+            max_decode_ctx, max_ctx, Hq, Hkv, D, bs, scale, _ptr(q), _ptr(k_cache), _ptr(v_cache),
+            _ptr(cu_seqlens_q), _ptr(context_lens), _ptr(cu_blocks), _ptr(block_table), _ptr(out),
+            _ptr(workspace), workspace.numel() * workspace.element_size() if workspace is not None else 0)
+    if events is None:
+        _check(_lib().cb_mixed_paged_attention(*args), "cb_mixed_paged_attention")
+    else:
+        ev = (_vp * 4)(*[ctypes.c_void_p(e.cuda_event) if e is not None else None for e in events])
+        _check(_lib().cb_mixed_paged_attention_timed(*args, ev), "cb_mixed_paged_attention_timed")

@@ -1,0 +1,664 @@
+// Mixed paged attention for one chunked-prefill step on gfx950.
+//
+// "Chunked Prefill 的 Token 预算" §02 and §07: a chunk row at position c + i attends keys
+// 0..c + i (cached prefix plus its own chunk up to itself).  "Chunked Prefill: Ending the Great
+// Stall" §05: each chunk is an ordinary causal attention over the prefix and the chunk, computed
+// without materialising the score matrix; §01 and "Splitting Prefill From Decode Inside a Step"
+// ("Two kernels with different limiting resources"): decode rows stream the whole cache and are
+// bandwidth-bound, chunk rows are dense matrix work and compute-bound.
+//
+// Three kernels on the caller's stream:
+//   decode_kernel  rows [0, nd): one wave per (decode, KV head, 16-head block, key partition).
+//                  S^T = K Q^T on 16x16x32 MFMA with K loaded from HBM straight into operand
+//                  registers; online softmax in the lane that owns the head; O^T += V^T P^T with
+//                  V transposed through LDS.  Writes float32 partials (m, l, unnormalised o).
+//   chunk_kernel   rows [nd, T): one 256-thread workgroup per (chunk, query block, KV head,
+//                  key split).  Rows of a tile are (position, head-in-group) pairs, so all query
+//                  heads of a GQA group share one K/V tile.  K and V^T tiles of 64 keys staged
+//                  in LDS; S^T = K Q^T and O^T += V^T P^T on 32x32x16 MFMA; causal mask only
+//                  where a key can exceed the row's position.  One split: normalised output
+//                  written directly; several: float32 partials.
+//   combine_kernel log-sum-exp merge of the partials of each (row, head) into out.
+// Softmax runs in base 2 with scale * log2(e) folded into the scores.
+#include <algorithm>
+
+#include "cb.h"
+#include "common.h"
+
+namespace cb {
+namespace {
+
+constexpr int kChunkRows = 128;   // rows per chunk tile: 4 waves x 32
+constexpr int kChunkKeys = 64;    // keys per LDS tile
+constexpr int kDecodeKeys = 32;   // keys per decode iteration
+constexpr int kMaxSplit = 8;
+
+struct Plan {
+  int32_t G = 1, head_blocks = 1;
+  int32_t part = 256, max_parts = 0;
+  int32_t bmq = 128, q_blocks = 0, n_chunk = 0, nsplit = 1;
+  size_t dec_o = 0, dec_ml = 0, chk_o = 0, chk_ml = 0, total = 0;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+// Partitioning decisions, shared by the workspace query and the launch so they always agree.
+Plan make_plan(int32_t num_seqs, int32_t nd, int32_t T, int32_t max_q_len, int32_t max_dctx,
+               int32_t max_ctx, int32_t Hq, int32_t Hkv, int32_t D) {
+  Plan p;
+  p.G = Hq / Hkv;
+  p.head_blocks = (p.G + 15) / 16;
+  if (nd > 0) {
+    const int32_t want = (std::max(max_dctx, 1) + 15) / 16;   // ~16 partitions per longest row
+    while (p.part < want && p.part < 4096) p.part *= 2;
+    p.max_parts = (std::max(max_dctx, 1) + p.part - 1) / p.part;
+  }
+  p.bmq = kChunkRows / p.G;
+  p.n_chunk = num_seqs - nd;
+  if (p.n_chunk > 0) {
+    p.q_blocks = (std::max(max_q_len, 1) + p.bmq - 1) / p.bmq;
+    const int64_t tiles = static_cast<int64_t>(p.n_chunk) * p.q_blocks * Hkv;
+    while (p.nsplit < kMaxSplit && tiles * p.nsplit < 512 &&
+           max_ctx / (2 * p.nsplit) >= 2 * kChunkKeys)
+      p.nsplit *= 2;
+  }
+  size_t off = 0;
+  const size_t dec_rows = static_cast<size_t>(nd) * Hq * p.max_parts;
+  p.dec_o = off;  off = align256(off + dec_rows * D * sizeof(float));
+  p.dec_ml = off; off = align256(off + dec_rows * 2 * sizeof(float));
+  const size_t chk_rows = p.nsplit > 1 ? static_cast<size_t>(T - nd) * Hq * p.nsplit : 0;
+  p.chk_o = off;  off = align256(off + chk_rows * D * sizeof(float));
+  p.chk_ml = off; off = align256(off + chk_rows * 2 * sizeof(float));
+  p.total = off;
+  return p;
+}
+
+struct AttnArgs {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* cu_q;
+  const int32_t* ctx_lens;
+  const int32_t* cu_blocks;
+  const int32_t* block_table;
+  void* out;
+  float* dec_o;
+  float* dec_ml;
+  float* chk_o;
+  float* chk_ml;
+  int32_t num_seqs, nd, T, Hq, Hkv, G, bs;
+  int32_t part, max_parts, head_blocks;
+  int32_t bmq, q_blocks, n_chunk, nsplit;
+  float scale_log2;
+};
+
+// ---------------------------------------------------------------------------------------------
+// Decode rows.
+// ---------------------------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(64) void decode_kernel(AttnArgs a) {
+  constexpr int KS = D / 32;          // 32-slot contraction steps over the head dimension
+  constexpr int DT = D / 16;          // 16-dim output tiles
+  constexpr int DC = D / 8;           // 8-element chunks per row
+  constexpr int QUADS = (kDecodeKeys / 4) * DC / 64;   // 4-key quads per lane per iteration
+  constexpr int VPAD = 16 / sizeof(T);
+  __shared__ __attribute__((aligned(16))) T sVt[D][kDecodeKeys + VPAD];
+
+  const int lane = threadIdx.x;
+  int64_t item = blockIdx.x;
+  const int32_t p = static_cast<int32_t>(item % a.max_parts); item /= a.max_parts;
+  const int32_t hb = static_cast<int32_t>(item % a.head_blocks); item /= a.head_blocks;
+  const int32_t g = static_cast<int32_t>(item % a.Hkv);
+  const int32_t s = static_cast<int32_t>(item / a.Hkv);
+  const int32_t ctx = a.ctx_lens[s];
+  const int32_t k_lo = p * a.part;
+  if (k_lo >= ctx) return;
+  const int32_t k_hi = min(ctx, k_lo + a.part);
+  const int32_t gh = min(16, a.G - 16 * hb);
+  const int32_t h0 = g * a.G + 16 * hb;
+  const int32_t col = lane & 15;      // head owned by this lane in S^T / P^T / O^T
+  const int32_t grp = lane >> 4;      // slot group
+
+  const T* q = static_cast<const T*>(a.q);
+  const T* kc = static_cast<const T*>(a.k_cache);
+  const T* vc = static_cast<const T*>(a.v_cache);
+  const int32_t* btab = a.block_table + a.cu_blocks[s];
+  const int32_t bs = a.bs;
+
+  Frag<T> qf[KS];
+  {
+    const T* qrow = q + (static_cast<int64_t>(s) * a.Hq + h0 + col) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (col < gh) qf[ks].load(qrow + 32 * ks + 8 * grp);
+      else qf[ks].zero();
+    }
+  }
+
+  float m_run = kNegInf, l_run = 0.f;
+  f32x4 o[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int vchunk = lane % DC;
+  const int vquad0 = lane / DC;
+
+  for (int32_t key0 = k_lo; key0 < k_hi; key0 += kDecodeKeys) {
+    Frag<T> kf[2][KS];
+#pragma unroll
+    for (int kg = 0; kg < 2; ++kg) {
+      const int32_t key = key0 + 16 * kg + col;
+      if (key < k_hi) {
+        const T* kp = kc + ((static_cast<int64_t>(btab[key / bs]) * a.Hkv + g) * bs + key % bs) * D;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) kf[kg][ks].load(kp + 32 * ks + 8 * grp);
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) kf[kg][ks].zero();
+      }
+    }
+    Frag<T> vf[QUADS][4];
+#pragma unroll
+    for (int i = 0; i < QUADS; ++i) {
+      const int quad = vquad0 + (64 / DC) * i;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int32_t key = key0 + 4 * quad + e;
+        if (key < k_hi) {
+          const T* vp = vc + ((static_cast<int64_t>(btab[key / bs]) * a.Hkv + g) * bs + key % bs) * D;
+          vf[i][e].load(vp + 8 * vchunk);
+        } else {
+          vf[i][e].zero();
+        }
+      }
+    }
+
+    // S^T[key, head] for the 32 keys: lane holds keys 16 kg + 4 grp + r of head col.
+    f32x4 st[2];
+#pragma unroll
+    for (int kg = 0; kg < 2; ++kg) {
+      st[kg] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) mma16_k32(st[kg], kf[kg][ks], qf[ks]);
+    }
+    float sv[8];
+    float mx = kNegInf;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int32_t key = key0 + 16 * (j >> 2) + 4 * grp + (j & 3);
+      const float x = key < k_hi ? st[j >> 2][j & 3] * a.scale_log2 : kNegInf;
+      sv[j] = x;
+      mx = fmaxf(mx, x);
+    }
+    mx = wave_xor_max(mx, 16);
+    mx = wave_xor_max(mx, 32);
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = m_new == kNegInf ? 0.f : m_new;
+    const float alpha = exp2f(m_run - m_use);
+    float pv[8], psum = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      pv[j] = exp2f(sv[j] - m_use);
+      psum += pv[j];
+    }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+    Frag<T> pf;   // P^T slot 8 grp + j <-> key 16 (j / 4) + 4 grp + j % 4 (same order as sv)
+    pf.set_all(pv);
+
+    // V^T into LDS: key 16 b + 4 a + c goes to slot 8 a + 4 b + c of its dimension row.
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < QUADS; ++i) {
+      const int quad = vquad0 + (64 / DC) * i;
+      const int slot0 = 8 * (quad & 3) + 4 * (quad >> 2);
+#pragma unroll
+      for (int d = 0; d < 8; ++d) {
+        T* dst = &sVt[8 * vchunk + d][slot0];
+        if constexpr (sizeof(T) == 2) {
+          const uint32_t* w0 = &vf[i][0].u.x;
+          const uint32_t* w1 = &vf[i][1].u.x;
+          const uint32_t* w2 = &vf[i][2].u.x;
+          const uint32_t* w3 = &vf[i][3].u.x;
+          const int sh = 16 * (d & 1);
+          const uint32_t lo = ((w0[d >> 1] >> sh) & 0xffffu) | (((w1[d >> 1] >> sh) & 0xffffu) << 16);
+          const uint32_t hi = ((w2[d >> 1] >> sh) & 0xffffu) | (((w3[d >> 1] >> sh) & 0xffffu) << 16);
+          *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
+        } else {
+          *reinterpret_cast<float4*>(dst) =
+              make_float4(vf[i][0].get(d), vf[i][1].get(d), vf[i][2].get(d), vf[i][3].get(d));
+        }
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      Frag<T> vt;
+      vt.load(&sVt[16 * dt + col][8 * grp]);
+      mma16_k32(o[dt], vt, pf);
+    }
+  }
+
+  float l_tot = wave_xor_sum(l_run, 16);
+  l_tot = wave_xor_sum(l_tot, 32);
+  if (col < gh) {
+    const int64_t prow = (static_cast<int64_t>(s) * a.Hq + h0 + col) * a.max_parts + p;
+    float* po = a.dec_o + prow * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      *reinterpret_cast<float4*>(po + 16 * dt + 4 * grp) = make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
+    if (grp == 0) *reinterpret_cast<float2*>(a.dec_ml + 2 * prow) = make_float2(m_run, l_tot);
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Chunk rows.
+// ---------------------------------------------------------------------------------------------
+template <typename T>
+__device__ __forceinline__ void store4(T* dst, float x0, float x1, float x2, float x3);
+template <>
+__device__ __forceinline__ void store4<bf16_t>(bf16_t* dst, float x0, float x1, float x2, float x3) {
+  const uint32_t lo = f32_to_bf16_bits(x0) | (static_cast<uint32_t>(f32_to_bf16_bits(x1)) << 16);
+  const uint32_t hi = f32_to_bf16_bits(x2) | (static_cast<uint32_t>(f32_to_bf16_bits(x3)) << 16);
+  *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
+}
+template <>
+__device__ __forceinline__ void store4<float>(float* dst, float x0, float x1, float x2, float x3) {
+  *reinterpret_cast<float4*>(dst) = make_float4(x0, x1, x2, x3);
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void chunk_kernel(AttnArgs a, int32_t n_tiles, int32_t per_xcd) {
+  constexpr int KS = D / 16;          // 16-slot contraction steps over the head dimension
+  constexpr int MT = D / 32;          // 32-dim output tiles
+  constexpr int DC = D / 8;           // 8-element chunks per key row
+  constexpr int KPAD = 16 / sizeof(T);
+  constexpr int VPAD = 16 / sizeof(T);
+  constexpr int KLOADS = kChunkKeys * DC / 256;            // K chunks per thread per tile
+  constexpr int VPAIRS = (kChunkKeys / 4) * DC;            // (quad, chunk) pairs per tile
+  constexpr int VLOADS = (VPAIRS + 255) / 256;
+  __shared__ __attribute__((aligned(16))) T sK[kChunkKeys][D + KPAD];
+  __shared__ __attribute__((aligned(16))) T sVt[D][kChunkKeys + VPAD];
+
+  // XCD-aware order: workgroup b runs on XCD b % 8; give each XCD a contiguous run of logical
+  // tiles so that the tiles sharing one (chunk, KV head) K/V stream share that XCD's L2.
+  const int32_t bid = blockIdx.x;
+  const int32_t tile = (bid & 7) * per_xcd + (bid >> 3);
+  if (tile >= n_tiles) return;
+  int32_t t = tile;
+  const int32_t sp = t % a.nsplit; t /= a.nsplit;
+  const int32_t qb = t % a.q_blocks; t /= a.q_blocks;
+  const int32_t g = t % a.Hkv;
+  const int32_t s = a.nd + t / a.Hkv;
+
+  const int32_t row0 = a.cu_q[s];
+  const int32_t d = a.cu_q[s + 1] - row0;
+  if (qb * a.bmq >= d) return;
+  const int32_t ctx = a.ctx_lens[s];
+  const int32_t c = ctx - d;
+  const int32_t kv_end = c + min(d, (qb + 1) * a.bmq);        // past the block's last position
+  const int32_t tiles_total = (kv_end + kChunkKeys - 1) / kChunkKeys;
+  const int32_t tiles_per = (tiles_total + a.nsplit - 1) / a.nsplit;
+  const int32_t kt_lo = sp * tiles_per;
+  const int32_t kt_hi = min(tiles_total, kt_lo + tiles_per);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int col = lane & 31;          // query row of this lane in S^T / P^T / O^T
+  const int half = lane >> 5;         // slot group
+  const int rr = 32 * wave + col;     // row within the tile
+  const int32_t pos_local = qb * a.bmq + rr / a.G;
+  const int32_t head = g * a.G + rr % a.G;
+  const bool valid = rr < a.bmq * a.G && pos_local < d;
+  const int32_t qpos = valid ? c + pos_local : 0x7fffffff;      // padding rows see everything
+
+  const T* q = static_cast<const T*>(a.q);
+  const T* kc = static_cast<const T*>(a.k_cache);
+  const T* vc = static_cast<const T*>(a.v_cache);
+  const int32_t* btab = a.block_table + a.cu_blocks[s];
+  const int32_t bs = a.bs;
+
+  Frag<T> qf[KS];
+  {
+    const T* qrow = q + (static_cast<int64_t>(row0 + pos_local) * a.Hq + head) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (valid) qf[ks].load(qrow + 16 * ks + 8 * half);
+      else qf[ks].zero();
+    }
+  }
+
+  float m_run = kNegInf, l_run = 0.f;
+  f32x16 o[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) o[mt] = f32x16{};
+
+  Frag<T> kreg[KLOADS];
+  Frag<T> vreg[VLOADS][4];
+  auto gload = [&](int32_t kt) {
+    const int32_t k0 = kt * kChunkKeys;
+#pragma unroll
+    for (int i = 0; i < KLOADS; ++i) {
+      const int cid = tid + 256 * i;
+      const int32_t key = k0 + cid / DC;
+      if (key < kv_end) {
+        const T* kp = kc + ((static_cast<int64_t>(btab[key / bs]) * a.Hkv + g) * bs + key % bs) * D;
+        kreg[i].load(kp + 8 * (cid % DC));
+      } else {
+        kreg[i].zero();
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < VLOADS; ++i) {
+      const int pid = tid + 256 * i;
+      const int quad = pid / DC, ch = pid % DC;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int32_t key = k0 + 4 * quad + e;
+        if (pid < VPAIRS && key < kv_end) {
+          const T* vp = vc + ((static_cast<int64_t>(btab[key / bs]) * a.Hkv + g) * bs + key % bs) * D;
+          vreg[i][e].load(vp + 8 * ch);
+        } else {
+          vreg[i][e].zero();
+        }
+      }
+    }
+  };
+  auto lstore = [&]() {
+#pragma unroll
+    for (int i = 0; i < KLOADS; ++i) {
+      const int cid = tid + 256 * i;
+      kreg[i].store(&sK[cid / DC][8 * (cid % DC)]);
+    }
+#pragma unroll
+    for (int i = 0; i < VLOADS; ++i) {
+      const int pid = tid + 256 * i;
+      if (pid >= VPAIRS) continue;
+      const int quad = pid / DC, ch = pid % DC;
+      // key 16 u + k goes to column 16 u + sigma(k), sigma swapping the middle two 4-key quads
+      const int qq = quad & 3;
+      const int slot0 = 16 * (quad >> 2) + 4 * (qq == 1 ? 2 : (qq == 2 ? 1 : qq));
+#pragma unroll
+      for (int dd = 0; dd < 8; ++dd) {
+        T* dst = &sVt[8 * ch + dd][slot0];
+        if constexpr (sizeof(T) == 2) {
+          const uint32_t* w0 = &vreg[i][0].u.x;
+          const uint32_t* w1 = &vreg[i][1].u.x;
+          const uint32_t* w2 = &vreg[i][2].u.x;
+          const uint32_t* w3 = &vreg[i][3].u.x;
+          const int sh = 16 * (dd & 1);
+          const uint32_t lo = ((w0[dd >> 1] >> sh) & 0xffffu) | (((w1[dd >> 1] >> sh) & 0xffffu) << 16);
+          const uint32_t hi = ((w2[dd >> 1] >> sh) & 0xffffu) | (((w3[dd >> 1] >> sh) & 0xffffu) << 16);
+          *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
+        } else {
+          *reinterpret_cast<float4*>(dst) =
+              make_float4(vreg[i][0].get(dd), vreg[i][1].get(dd), vreg[i][2].get(dd), vreg[i][3].get(dd));
+        }
+      }
+    }
+  };
+
+  if (kt_lo < kt_hi) gload(kt_lo);
+  for (int32_t kt = kt_lo; kt < kt_hi; ++kt) {
+    __syncthreads();
+    lstore();
+    __syncthreads();
+    if (kt + 1 < kt_hi) gload(kt + 1);
+    const int32_t k0 = kt * kChunkKeys;
+    const bool need_mask = k0 + kChunkKeys - 1 > c + qb * a.bmq;   // some key may pass a row
+
+    f32x16 st[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      st[h] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        Frag<T> kf;
+        kf.load(&sK[32 * h + col][16 * ks + 8 * half]);
+        mma32_k16(st[h], kf, qf[ks]);
+      }
+    }
+    float mx = kNegInf;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float x = st[h][r] * a.scale_log2;
+        if (need_mask) {
+          const int32_t key = k0 + 32 * h + acc32_row(lane, r);
+          if (key > qpos) x = kNegInf;
+        }
+        st[h][r] = x;
+        mx = fmaxf(mx, x);
+      }
+    }
+    mx = wave_xor_max(mx, 32);
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = m_new == kNegInf ? 0.f : m_new;
+    const float alpha = exp2f(m_run - m_use);
+    float psum = 0.f;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float e = exp2f(st[h][r] - m_use);
+        st[h][r] = e;
+        psum += e;
+      }
+    }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) o[mt] *= alpha;
+#pragma unroll
+    for (int ps = 0; ps < 4; ++ps) {          // 16-key contraction steps
+      float pv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) pv[j] = st[ps >> 1][8 * (ps & 1) + j];
+      Frag<T> pf;
+      pf.set_all(pv);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        Frag<T> vt;
+        vt.load(&sVt[32 * mt + col][16 * ps + 8 * half]);
+        mma32_k16(o[mt], vt, pf);
+      }
+    }
+  }
+
+  const float l_tot = wave_xor_sum(l_run, 32);
+  if (!valid) return;
+  const int32_t row = row0 + pos_local;
+  if (a.nsplit == 1) {
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    T* orow = static_cast<T*>(a.out) + (static_cast<int64_t>(row) * a.Hq + head) * D;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4)
+        store4<T>(orow + 32 * mt + 8 * r4 + 4 * half, o[mt][4 * r4] * inv, o[mt][4 * r4 + 1] * inv,
+                  o[mt][4 * r4 + 2] * inv, o[mt][4 * r4 + 3] * inv);
+  } else {
+    const int64_t prow = (static_cast<int64_t>(row - a.nd) * a.Hq + head) * a.nsplit + sp;
+    float* po = a.chk_o + prow * D;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4)
+        *reinterpret_cast<float4*>(po + 32 * mt + 8 * r4 + 4 * half) =
+            make_float4(o[mt][4 * r4], o[mt][4 * r4 + 1], o[mt][4 * r4 + 2], o[mt][4 * r4 + 3]);
+    if (half == 0) *reinterpret_cast<float2*>(a.chk_ml + 2 * prow) = make_float2(m_run, l_tot);
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Merge of split partials: m = max m_p, w_p = 2^(m_p - m), out = sum w_p o_p / sum w_p l_p.
+// ---------------------------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(256) void combine_kernel(AttnArgs a, int32_t n_dec_rows, int32_t n_items) {
+  constexpr int PER = D / 64;
+  const int lane = threadIdx.x & 63;
+  const int64_t w = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (w >= n_items) return;
+  const int32_t ri = static_cast<int32_t>(w / a.Hq);
+  const int32_t h = static_cast<int32_t>(w % a.Hq);
+  int32_t row, P;
+  const float* po;
+  const float* pml;
+  if (ri < n_dec_rows) {
+    row = ri;
+    P = min((a.ctx_lens[row] + a.part - 1) / a.part, a.max_parts);   // never past the workspace
+    const int64_t base = (static_cast<int64_t>(row) * a.Hq + h) * a.max_parts;
+    po = a.dec_o + base * D;
+    pml = a.dec_ml + base * 2;
+  } else {
+    row = a.nd + (ri - n_dec_rows);
+    P = a.nsplit;
+    const int64_t base = (static_cast<int64_t>(row - a.nd) * a.Hq + h) * a.nsplit;
+    po = a.chk_o + base * D;
+    pml = a.chk_ml + base * 2;
+  }
+  float m = kNegInf;
+  for (int32_t i = 0; i < P; ++i) m = fmaxf(m, pml[2 * i]);
+  const float m_use = m == kNegInf ? 0.f : m;
+  float L = 0.f;
+  float acc[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) acc[j] = 0.f;
+  for (int32_t i = 0; i < P; ++i) {
+    const float wgt = exp2f(pml[2 * i] - m_use);
+    L += wgt * pml[2 * i + 1];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) acc[j] += wgt * po[static_cast<int64_t>(i) * D + lane + 64 * j];
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  T* orow = static_cast<T*>(a.out) + (static_cast<int64_t>(row) * a.Hq + h) * D;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const float x = acc[j] * inv;
+    if constexpr (sizeof(T) == 2) {
+      reinterpret_cast<uint16_t*>(orow)[lane + 64 * j] = f32_to_bf16_bits(x);
+    } else {
+      orow[lane + 64 * j] = x;
+    }
+  }
+}
+
+template <typename T, int D>
+int launch_all(hipStream_t st, const AttnArgs& a, const Plan& p, void* const* events) {
+  auto rec = [&](int i) {
+    if (events && events[i]) (void)hipEventRecord(static_cast<hipEvent_t>(events[i]), st);
+  };
+  rec(0);
+  if (a.nd > 0) {
+    const int64_t grid = static_cast<int64_t>(a.nd) * a.Hkv * a.head_blocks * a.max_parts;
+    if (grid > 0x7fffffff) return CB_ERR_INVALID;
+    decode_kernel<T, D><<<dim3(static_cast<uint32_t>(grid)), dim3(64), 0, st>>>(a);
+    if (hipGetLastError() != hipSuccess) return CB_ERR_HIP;
+  }
+  rec(1);
+  if (a.n_chunk > 0) {
+    const int64_t n_tiles = static_cast<int64_t>(a.n_chunk) * a.q_blocks * a.Hkv * a.nsplit;
+    const int64_t per_xcd = (n_tiles + 7) / 8;
+    if (per_xcd * 8 > 0x7fffffff) return CB_ERR_INVALID;
+    chunk_kernel<T, D><<<dim3(static_cast<uint32_t>(per_xcd * 8)), dim3(256), 0, st>>>(
+        a, static_cast<int32_t>(n_tiles), static_cast<int32_t>(per_xcd));
+    if (hipGetLastError() != hipSuccess) return CB_ERR_HIP;
+  }
+  rec(2);
+  const int32_t n_chunk_rows = a.nsplit > 1 ? a.T - a.nd : 0;
+  const int64_t items = static_cast<int64_t>(a.nd + n_chunk_rows) * a.Hq;
+  if (items > 0) {
+    const int64_t grid = (items + 3) / 4;
+    if (grid > 0x7fffffff) return CB_ERR_INVALID;
+    combine_kernel<T, D><<<dim3(static_cast<uint32_t>(grid)), dim3(256), 0, st>>>(
+        a, a.nd, static_cast<int32_t>(items));
+    if (hipGetLastError() != hipSuccess) return CB_ERR_HIP;
+  }
+  rec(3);
+  return CB_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool valid_shape(int32_t num_seqs, int32_t nd, int32_t T, int32_t max_q_len, int32_t max_dctx,
+                 int32_t max_ctx, int32_t Hq, int32_t Hkv, int32_t D) {
+  if (num_seqs < 0 || nd < 0 || nd > num_seqs || T < num_seqs || T - nd < num_seqs - nd) return false;
+  if (Hq < 1 || Hkv < 1 || Hq % Hkv || Hq / Hkv > kChunkRows) return false;
+  if (D != 64 && D != 128) return false;
+  if (max_q_len < 0 || max_dctx < 0 || max_ctx < 0) return false;
+  if (num_seqs > nd && (max_q_len < 1 || max_ctx < 1)) return false;
+  if (nd > 0 && max_dctx < 1) return false;
+  return true;
+}
+
+}  // namespace
+}  // namespace cb
+
+extern "C" size_t cb_attn_workspace_bytes(int32_t num_seqs, int32_t num_decodes, int32_t T,
+                                          int32_t max_q_len, int32_t max_decode_ctx,
+                                          int32_t max_ctx, int32_t Hq, int32_t Hkv, int32_t D) {
+  if (!cb::valid_shape(num_seqs, num_decodes, T, max_q_len, max_decode_ctx, max_ctx, Hq, Hkv, D))
+    return 0;
+  return cb::make_plan(num_seqs, num_decodes, T, max_q_len, max_decode_ctx, max_ctx, Hq, Hkv, D).total;
+}
+
+extern "C" int cb_mixed_paged_attention_timed(
+    void* stream, int32_t dtype, int32_t num_seqs, int32_t num_decodes, int32_t T,
+    int32_t max_q_len, int32_t max_decode_ctx, int32_t max_ctx, int32_t Hq, int32_t Hkv,
+    int32_t D, int32_t block_size, float scale, const void* q, const void* k_cache,
+    const void* v_cache, const int32_t* cu_seqlens_q, const int32_t* context_lens,
+    const int32_t* cu_blocks, const int32_t* block_table, void* out, void* workspace,
+    size_t workspace_bytes, void* const* events) {
+  using namespace cb;
+  if (dtype != CB_F32 && dtype != CB_BF16) return CB_ERR_INVALID;
+  if (!valid_shape(num_seqs, num_decodes, T, max_q_len, max_decode_ctx, max_ctx, Hq, Hkv, D))
+    return CB_ERR_INVALID;
+  if (block_size < 1 || !(scale > 0.f)) return CB_ERR_INVALID;
+  if (num_seqs == 0) return CB_OK;
+  if (!q || !k_cache || !v_cache || !cu_seqlens_q || !context_lens || !cu_blocks || !block_table || !out)
+    return CB_ERR_INVALID;
+  const void* ptrs[] = {q, k_cache, v_cache, out};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return CB_ERR_INVALID;
+  const Plan p = make_plan(num_seqs, num_decodes, T, max_q_len, max_decode_ctx, max_ctx, Hq, Hkv, D);
+  if (p.total > 0 && (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u))) return CB_ERR_INVALID;
+  if (workspace_bytes < p.total) return CB_ERR_CAPACITY;
+
+  AttnArgs a{};
+  a.q = q; a.k_cache = k_cache; a.v_cache = v_cache;
+  a.cu_q = cu_seqlens_q; a.ctx_lens = context_lens; a.cu_blocks = cu_blocks; a.block_table = block_table;
+  a.out = out;
+  char* ws = static_cast<char*>(workspace);
+  a.dec_o = reinterpret_cast<float*>(ws + p.dec_o);
+  a.dec_ml = reinterpret_cast<float*>(ws + p.dec_ml);
+  a.chk_o = reinterpret_cast<float*>(ws + p.chk_o);
+  a.chk_ml = reinterpret_cast<float*>(ws + p.chk_ml);
+  a.num_seqs = num_seqs; a.nd = num_decodes; a.T = T; a.Hq = Hq; a.Hkv = Hkv; a.G = p.G;
+  a.bs = block_size;
+  a.part = p.part; a.max_parts = std::max(p.max_parts, 1); a.head_blocks = p.head_blocks;
+  a.bmq = p.bmq; a.q_blocks = p.q_blocks; a.n_chunk = p.n_chunk; a.nsplit = p.nsplit;
+  a.scale_log2 = scale * 1.4426950408889634f;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (dtype == CB_BF16) {
+    return D == 128 ? launch_all<bf16_t, 128>(st, a, p, events) : launch_all<bf16_t, 64>(st, a, p, events);
+  }
+  return D == 128 ? launch_all<float, 128>(st, a, p, events) : launch_all<float, 64>(st, a, p, events);
+}
+
+extern "C" int cb_mixed_paged_attention(
+    void* stream, int32_t dtype, int32_t num_seqs, int32_t num_decodes, int32_t T,
+    int32_t max_q_len, int32_t max_decode_ctx, int32_t max_ctx, int32_t Hq, int32_t Hkv,
+    int32_t D, int32_t block_size, float scale, const void* q, const void* k_cache,
+    const void* v_cache, const int32_t* cu_seqlens_q, const int32_t* context_lens,
+    const int32_t* cu_blocks, const int32_t* block_table, void* out, void* workspace,
+    size_t workspace_bytes) {
+  return cb_mixed_paged_attention_timed(stream, dtype, num_seqs, num_decodes, T, max_q_len,
+                                        max_decode_ctx, max_ctx, Hq, Hkv, D, block_size, scale, q,
+                                        k_cache, v_cache, cu_seqlens_q, context_lens, cu_blocks,
+                                        block_table, out, workspace, workspace_bytes, nullptr);
+}

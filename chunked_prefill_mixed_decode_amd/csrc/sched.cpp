@@ -1,0 +1,327 @@
+// Host batch builder for one mixed step: block pool, running and waiting queues, and the
+// decode-first, first-come-first-served token-budget plan.
+//
+// Follows "Chunked Prefill: Ending the Great Stall" §03-§04 (decodes first at one token each,
+// then every waiting prompt in order takes the largest chunk that fits the rest of the budget;
+// finished prompts join the decodes), "Chunked Prefill 的 Token 预算" §04-§08 and §11 (budget
+// inequality, error when decodes alone exceed the budget, per-row positions / slots / block
+// table / context length, atomic commit, whole-prompt reservation) and "Splitting Prefill From
+// Decode Inside a Step" ("The arithmetic of chunk boundaries": reserve before the first chunk).
+//
+// A build runs in two phases.  Phase 1 checks everything that can fail (budget, blocks,
+// capacities) and pre-allocates host memory without touching the logical state; phase 2 commits
+// and writes the plan and cannot fail.  So every error leaves the builder exactly as it was.
+#include <algorithm>
+#include <cstdint>
+#include <new>
+#include <vector>
+
+#include "cb.h"
+
+namespace {
+
+struct RunningReq {
+  int32_t rid;
+  int32_t ctx;                   // tokens in the cache
+  std::vector<int32_t> blocks;
+};
+
+struct WaitingReq {
+  int32_t rid;
+  int32_t len;                   // prompt length
+  int32_t done;                  // tokens already in the cache (cached prefix + chunks run)
+  std::vector<int32_t> blocks;
+  bool reserved;
+};
+
+inline int32_t ceil_div(int64_t a, int64_t b) { return static_cast<int32_t>((a + b - 1) / b); }
+
+}  // namespace
+
+struct cb_sched {
+  int32_t bs = 0;
+  int32_t max_chunk = 0;
+  std::vector<int32_t> free_list;  // free blocks are free_list[free_head..]
+  size_t free_head = 0;
+  std::vector<RunningReq> running;
+  std::vector<WaitingReq> waiting;
+  int32_t next_id = 0;
+
+  size_t free_count() const { return free_list.size() - free_head; }
+  int32_t pop_block() { return free_list[free_head++]; }
+};
+
+extern "C" {
+
+const char* cb_status_string(int status) {
+  switch (status) {
+    case CB_OK: return "ok";
+    case CB_ERR_INVALID: return "invalid argument";
+    case CB_ERR_DECODE_OVER_BUDGET: return "running decodes exceed the token budget";
+    case CB_ERR_OUT_OF_BLOCKS: return "KV block pool exhausted";
+    case CB_ERR_CAPACITY: return "output buffer too small";
+    case CB_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int cb_sched_create(const cb_sched_config* cfg, cb_sched** out) {
+  if (!cfg || !out || cfg->block_size < 1 || cfg->num_blocks < 0 || cfg->max_chunk < 0)
+    return CB_ERR_INVALID;
+  *out = nullptr;
+  try {
+    auto* s = new cb_sched();
+    s->bs = cfg->block_size;
+    s->max_chunk = cfg->max_chunk;
+    s->free_list.resize(cfg->num_blocks);
+    if (cfg->free_list) {
+      std::vector<char> seen(cfg->num_blocks, 0);
+      for (int32_t i = 0; i < cfg->num_blocks; ++i) {
+        int32_t b = cfg->free_list[i];
+        if (b < 0 || b >= cfg->num_blocks || seen[b]) {
+          delete s;
+          return CB_ERR_INVALID;
+        }
+        seen[b] = 1;
+        s->free_list[i] = b;
+      }
+    } else {
+      for (int32_t i = 0; i < cfg->num_blocks; ++i) s->free_list[i] = i;
+    }
+    *out = s;
+    return CB_OK;
+  } catch (const std::bad_alloc&) {
+    return CB_ERR_CAPACITY;
+  }
+}
+
+void cb_sched_destroy(cb_sched* s) { delete s; }
+
+int cb_sched_clone(const cb_sched* s, cb_sched** out) {
+  if (!s || !out) return CB_ERR_INVALID;
+  try {
+    *out = new cb_sched(*s);
+    return CB_OK;
+  } catch (const std::bad_alloc&) {
+    *out = nullptr;
+    return CB_ERR_CAPACITY;
+  }
+}
+
+int cb_sched_add_running(cb_sched* s, int32_t context_len, int32_t* req_id) {
+  if (!s || context_len < 1) return CB_ERR_INVALID;
+  const int32_t need = ceil_div(context_len, s->bs);
+  if (static_cast<size_t>(need) > s->free_count()) return CB_ERR_OUT_OF_BLOCKS;
+  try {
+    RunningReq r{s->next_id, context_len, {}};
+    r.blocks.reserve(need + 1);
+    s->running.reserve(s->running.size() + 1);
+    for (int32_t i = 0; i < need; ++i) r.blocks.push_back(s->pop_block());
+    s->running.push_back(std::move(r));
+  } catch (const std::bad_alloc&) {
+    return CB_ERR_CAPACITY;
+  }
+  if (req_id) *req_id = s->next_id;
+  ++s->next_id;
+  return CB_OK;
+}
+
+int cb_sched_add_prompt(cb_sched* s, int32_t prompt_len, int32_t cached_len, int32_t* req_id) {
+  if (!s || prompt_len < 1 || cached_len < 0 || cached_len > prompt_len - 1) return CB_ERR_INVALID;
+  const int32_t need = ceil_div(cached_len, s->bs);
+  if (static_cast<size_t>(need) > s->free_count()) return CB_ERR_OUT_OF_BLOCKS;
+  try {
+    WaitingReq w{s->next_id, prompt_len, cached_len, {}, false};
+    w.blocks.reserve(ceil_div(prompt_len, s->bs));
+    s->waiting.reserve(s->waiting.size() + 1);
+    for (int32_t i = 0; i < need; ++i) w.blocks.push_back(s->pop_block());
+    s->waiting.push_back(std::move(w));
+  } catch (const std::bad_alloc&) {
+    return CB_ERR_CAPACITY;
+  }
+  if (req_id) *req_id = s->next_id;
+  ++s->next_id;
+  return CB_OK;
+}
+
+int cb_sched_get_blocks(const cb_sched* s, int32_t req_id, int32_t* out, int32_t cap, int32_t* n) {
+  if (!s || !n || cap < 0) return CB_ERR_INVALID;
+  const std::vector<int32_t>* bl = nullptr;
+  for (const auto& r : s->running)
+    if (r.rid == req_id) bl = &r.blocks;
+  for (const auto& w : s->waiting)
+    if (w.rid == req_id) bl = &w.blocks;
+  if (!bl) return CB_ERR_INVALID;
+  *n = static_cast<int32_t>(bl->size());
+  if (static_cast<size_t>(cap) < bl->size()) return CB_ERR_CAPACITY;
+  if (!bl->empty() && !out) return CB_ERR_INVALID;
+  std::copy(bl->begin(), bl->end(), out);
+  return CB_OK;
+}
+
+int cb_sched_pending_prompts(const cb_sched* s, int32_t* n) {
+  if (!s || !n) return CB_ERR_INVALID;
+  int32_t c = 0;
+  for (const auto& w : s->waiting) c += (w.done < w.len);
+  *n = c;
+  return CB_OK;
+}
+
+int cb_sched_free_blocks(const cb_sched* s, int32_t* n) {
+  if (!s || !n) return CB_ERR_INVALID;
+  *n = static_cast<int32_t>(s->free_count());
+  return CB_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+int build_step_impl(cb_sched* s, int32_t token_budget, cb_step* out) {
+  const int32_t bs = s->bs;
+
+  // ---------------- phase 1: plan without touching the logical state ----------------
+  // Decodes are the running requests in order, then prompts that finished last step (FCFS).
+  std::vector<int32_t> graduating;  // indices into waiting
+  for (size_t i = 0; i < s->waiting.size(); ++i)
+    if (s->waiting[i].done == s->waiting[i].len) graduating.push_back(static_cast<int32_t>(i));
+  const int64_t nd = static_cast<int64_t>(s->running.size()) + graduating.size();
+  if (nd > token_budget) return CB_ERR_DECODE_OVER_BUDGET;
+
+  // A decode at position ctx needs a fresh block when its blocks are exactly full.
+  size_t decode_need = 0;
+  int64_t blocks_emitted = 0;
+  int32_t max_ctx = 0, max_dctx = 0;
+  for (const auto& r : s->running) {
+    decode_need += (static_cast<int64_t>(r.ctx) == static_cast<int64_t>(bs) * static_cast<int64_t>(r.blocks.size()));
+    blocks_emitted += ceil_div(r.ctx + 1, bs);
+    max_dctx = std::max(max_dctx, r.ctx + 1);
+  }
+  for (int32_t i : graduating) {
+    const auto& w = s->waiting[i];
+    decode_need += (static_cast<int64_t>(w.len) == static_cast<int64_t>(bs) * static_cast<int64_t>(w.blocks.size()));
+    blocks_emitted += ceil_div(w.len + 1, bs);
+    max_dctx = std::max(max_dctx, w.len + 1);
+  }
+  if (decode_need > s->free_count()) return CB_ERR_OUT_OF_BLOCKS;
+  max_ctx = max_dctx;
+
+  struct Chunk { int32_t widx, take, reserve; };
+  std::vector<Chunk> chunks;
+  int64_t left = token_budget - nd;
+  size_t free_avail = s->free_count() - decode_need;
+  int32_t max_q = nd > 0 ? 1 : 0;
+  for (size_t i = 0; i < s->waiting.size() && left > 0; ++i) {
+    const auto& w = s->waiting[i];
+    if (w.done == w.len) continue;  // graduating this step
+    int32_t reserve = 0;
+    if (!w.reserved) {
+      reserve = ceil_div(w.len, bs) - static_cast<int32_t>(w.blocks.size());
+      if (static_cast<size_t>(reserve) > free_avail) break;  // strict FCFS: the head waits
+      free_avail -= reserve;
+    }
+    int64_t take = std::min<int64_t>(w.len - w.done, left);
+    if (s->max_chunk > 0) take = std::min<int64_t>(take, s->max_chunk);
+    chunks.push_back({static_cast<int32_t>(i), static_cast<int32_t>(take), reserve});
+    left -= take;
+    max_q = std::max<int32_t>(max_q, static_cast<int32_t>(take));
+    const int32_t ctx = w.done + static_cast<int32_t>(take);
+    blocks_emitted += ceil_div(ctx, bs);
+    max_ctx = std::max(max_ctx, ctx);
+  }
+
+  const int64_t num_seqs = nd + static_cast<int64_t>(chunks.size());
+  const int64_t T = token_budget - left;
+  if (num_seqs > out->cap_seqs || T > out->cap_tokens || blocks_emitted > out->cap_blocks) {
+    out->cap_seqs = static_cast<int32_t>(num_seqs);
+    out->cap_tokens = static_cast<int32_t>(T);
+    out->cap_blocks = static_cast<int32_t>(blocks_emitted);
+    return CB_ERR_CAPACITY;
+  }
+  if (!out->seq_ids || !out->cu_seqlens_q || !out->context_lens || !out->cu_blocks ||
+      (!out->block_table && blocks_emitted) || (!out->positions && T) ||
+      (!out->slot_mapping && T))
+    return CB_ERR_INVALID;
+
+  // Reserve host memory up front (capacity only; the logical state is untouched) so that
+  // phase 2 cannot fail.  A bad_alloc here propagates to the caller of this function.
+  s->running.reserve(s->running.size() + graduating.size());
+  for (auto& r : s->running) r.blocks.reserve(r.blocks.size() + 1);
+  for (int32_t i : graduating) s->waiting[i].blocks.reserve(s->waiting[i].blocks.size() + 1);
+  for (const auto& c : chunks) s->waiting[c.widx].blocks.reserve(ceil_div(s->waiting[c.widx].len, bs));
+
+  // ---------------- phase 2: commit and emit (no failure past this point) ----------------
+  for (int32_t i : graduating) {
+    auto& w = s->waiting[i];
+    s->running.push_back(RunningReq{w.rid, w.len, std::move(w.blocks)});
+  }
+
+  int32_t seq = 0, row = 0, nblk = 0;
+  out->cu_seqlens_q[0] = 0;
+  out->cu_blocks[0] = 0;
+  auto emit = [&](int32_t rid, int32_t first, int32_t n, const std::vector<int32_t>& blocks) {
+    const int32_t ctx = first + n;
+    out->seq_ids[seq] = rid;
+    out->context_lens[seq] = ctx;
+    const int32_t nb = ceil_div(ctx, bs);
+    for (int32_t j = 0; j < nb; ++j) out->block_table[nblk + j] = blocks[j];
+    nblk += nb;
+    for (int32_t p = first; p < ctx; ++p, ++row) {
+      out->positions[row] = p;
+      out->slot_mapping[row] = blocks[p / bs] * bs + p % bs;
+    }
+    ++seq;
+    out->cu_seqlens_q[seq] = row;
+    out->cu_blocks[seq] = nblk;
+  };
+
+  for (auto& r : s->running) {
+    if (static_cast<int64_t>(r.ctx) == static_cast<int64_t>(bs) * static_cast<int64_t>(r.blocks.size()))
+      r.blocks.push_back(s->pop_block());
+    emit(r.rid, r.ctx, 1, r.blocks);
+    r.ctx += 1;
+  }
+  for (const auto& c : chunks) {
+    auto& w = s->waiting[c.widx];
+    if (!w.reserved) {
+      for (int32_t j = 0; j < c.reserve; ++j) w.blocks.push_back(s->pop_block());
+      w.reserved = true;
+    }
+    emit(w.rid, w.done, c.take, w.blocks);
+    w.done += c.take;
+  }
+  if (!graduating.empty()) {  // compact the queue in place (no allocation)
+    size_t g = 0, wpos = 0;
+    for (size_t i = 0; i < s->waiting.size(); ++i) {
+      if (g < graduating.size() && static_cast<size_t>(graduating[g]) == i) {
+        ++g;
+        continue;
+      }
+      if (wpos != i) s->waiting[wpos] = std::move(s->waiting[i]);
+      ++wpos;
+    }
+    s->waiting.erase(s->waiting.begin() + wpos, s->waiting.end());
+  }
+
+  out->num_seqs = seq;
+  out->num_decodes = static_cast<int32_t>(nd);
+  out->num_tokens = row;
+  out->num_prefill_tokens = row - static_cast<int32_t>(nd);
+  out->unused_tokens = static_cast<int32_t>(left);
+  out->max_q_len = max_q;
+  out->max_context_len = max_ctx;
+  out->max_decode_context_len = max_dctx;
+  out->num_blocks_emitted = nblk;
+  return CB_OK;
+}
+
+}  // namespace
+
+extern "C" int cb_build_step(cb_sched* s, int32_t token_budget, cb_step* out) {
+  if (!s || !out || token_budget < 1) return CB_ERR_INVALID;
+  try {
+    return build_step_impl(s, token_budget, out);
+  } catch (const std::bad_alloc&) {  // only phase 1 allocates: the state is unchanged
+    return CB_ERR_CAPACITY;
+  }
+}

@@ -1,0 +1,89 @@
+"""One mixed step on one GPU: build (C++), one metadata copy, rope + append, attention.
+
+``MixedStepRunner`` owns the device side of a serving layer for one head geometry: the paged
+K/V caches (``[num_blocks, Hkv, block_size, D]``), the rotary table, a ring of two pinned
+metadata buffers, the device copy of the metadata and the attention workspace.  Each call below
+forwards to one C entry point of libcb.so; the runner only allocates and orders them on the
+current torch stream.
+"""
+from __future__ import annotations
+
+import math
+
+import torch
+
+from . import binding as cb
+
+SENTINEL_BITS = {torch.bfloat16: -1, torch.float32: -1}   # all-ones: a NaN that no write produces
+
+
+class MixedStepRunner:
+    def __init__(self, *, Hq: int, Hkv: int, D: int, block_size: int, num_blocks: int,
+                 dtype: torch.dtype, device, max_pos: int, cap_seqs: int, cap_tokens: int,
+                 cap_blocks: int, sentinel: bool = True, rope_base: float = 10000.0):
+        self.Hq, self.Hkv, self.D, self.bs = Hq, Hkv, D, block_size
+        self.dtype = dtype
+        self.device = torch.device(device)
+        self.scale = 1.0 / math.sqrt(D)
+        shape = (num_blocks, Hkv, block_size, D)
+        self.k_cache = torch.empty(shape, dtype=dtype, device=self.device)
+        self.v_cache = torch.empty(shape, dtype=dtype, device=self.device)
+        if sentinel:
+            ity = torch.int16 if dtype == torch.bfloat16 else torch.int32
+            self.k_cache.view(ity).fill_(SENTINEL_BITS[dtype])
+            self.v_cache.view(ity).fill_(SENTINEL_BITS[dtype])
+        self.cos_sin = cb.cb_rope_cos_sin(max_pos, D, rope_base).to(self.device)
+        self.bufs = [cb.StepBuffers(cap_seqs, cap_tokens, cap_blocks) for _ in range(2)]
+        self.copied = [None, None]                 # event after the last copy out of each buffer
+        self.ring = 0
+        self.dev_flat = torch.empty_like(self.bufs[0].flat, device=self.device)
+        self.workspace = torch.empty(0, dtype=torch.uint8, device=self.device)
+
+    # ---- host builder + metadata copy ----------------------------------------------------------
+    def build(self, sched: cb.Sched, budget: int) -> cb.StepMeta:
+        """cb_build_step into the next pinned buffer (after its previous copy has finished)."""
+        i = self.ring
+        self.ring ^= 1
+        if self.copied[i] is not None:
+            self.copied[i].synchronize()
+        meta = cb.cb_build_step(sched, budget, self.bufs[i])
+        meta.buf_index = i
+        return meta
+
+    def upload(self, meta: cb.StepMeta) -> dict:
+        """One asynchronous host-to-device copy of the step's metadata; device int32 views."""
+        buf = self.bufs[meta.buf_index]
+        self.dev_flat.copy_(buf.flat, non_blocking=True)
+        ev = torch.cuda.Event()
+        ev.record()
+        self.copied[meta.buf_index] = ev
+        return {k: self.dev_flat[buf.offsets[k]:buf.offsets[k] + n] for k, n in meta.lengths().items()}
+
+    # ---- device work ---------------------------------------------------------------------------
+    def append(self, dev: dict, q, k, v, q_out):
+        """cb_rope_kv_append: rotate q into q_out, rotate k and append k, v at the step's slots."""
+        cb.cb_rope_kv_append(q, k, v, dev["positions"], dev["slot_mapping"], self.cos_sin, q_out,
+                             self.k_cache, self.v_cache)
+
+    def append_rows(self, positions, slots, k, v):
+        """Append rows outside a step (cache set-up for contexts that already exist)."""
+        cb.cb_rope_kv_append(None, k, v, positions, slots, self.cos_sin, None, self.k_cache, self.v_cache)
+
+    def ensure_workspace(self, nbytes: int):
+        if self.workspace.numel() < nbytes:
+            self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+
+    def workspace_bytes(self, meta: cb.StepMeta) -> int:
+        return cb.cb_attn_workspace_bytes(meta.num_seqs, meta.num_decodes, meta.num_tokens,
+                                          meta.max_q_len, meta.max_decode_context_len,
+                                          meta.max_context_len, self.Hq, self.Hkv, self.D)
+
+    def attend(self, meta: cb.StepMeta, dev: dict, q_rot, out, events=None):
+        """cb_mixed_paged_attention over the step's varlen batch."""
+        self.ensure_workspace(self.workspace_bytes(meta))
+        cb.cb_mixed_paged_attention(
+            q_rot, self.k_cache, self.v_cache, dev["cu_seqlens_q"], dev["context_lens"],
+            dev["cu_blocks"], dev["block_table"], out, self.workspace,
+            num_seqs=meta.num_seqs, num_decodes=meta.num_decodes, max_q_len=meta.max_q_len,
+            max_decode_ctx=meta.max_decode_context_len, max_ctx=meta.max_context_len,
+            scale=self.scale, events=events)

@@ -8,9 +8,12 @@ The pages fix neither the rotary variant nor its precision.  Reading used here (
 the pages as to the choice; the arithmetic below is pinned by tests):
 
 * rotate-half layout over the full head dimension D: pair (i, i + D/2) for i < D/2;
-* frequency theta_i = base ** (-2 i / D) with base 10000, evaluated in fp64;
-* table[p, i] = fp32(cos(p * theta_i)), table[p, D/2 + i] = fp32(sin(p * theta_i)), the angle
-  and both functions in fp64, rounded once;
+* frequency theta_i = base ** (-2 i / D) with base 10000, correctly rounded to fp64;
+* table[p, i] = fp32(cos(p * theta_i)), table[p, D/2 + i] = fp32(sin(p * theta_i)): the angle is
+  the fp64 product of p and theta_i; its cosine and sine are evaluated in x87 extended precision
+  (numpy longdouble) and rounded once to fp32 -- for practical purposes the correctly rounded
+  fp32 value of the exact cosine of that fp64 angle (vectorised fp64 libraries lose relative
+  accuracy near the zeros of cos and sin, which would change the fp32 rounding there);
 * for x in fp32 (bf16 inputs are widened exactly), c = table[p, i], s = table[p, D/2 + i]:
       out[i]       = fp32( fp32(x[i] * c)       - fp32(x[i + D/2] * s) )
       out[i + D/2] = fp32( fp32(x[i + D/2] * c) + fp32(x[i] * s) )
@@ -21,12 +24,18 @@ NumPy float32 ufuncs round each operation separately, which is exactly this defi
 """
 from __future__ import annotations
 
+import decimal
+
 import numpy as np
 
 
 def frequencies(D: int, base: float = 10000.0) -> np.ndarray:
-    i = np.arange(D // 2, dtype=np.float64)
-    return base ** ((-2.0 * i) / D)
+    """theta_i = base ** (-2 i / D), correctly rounded to fp64 (50-digit decimal arithmetic)."""
+    with decimal.localcontext() as ctx:
+        ctx.prec = 50
+        b = decimal.Decimal(base)
+        return np.array([float(b ** (decimal.Decimal(-2 * i) / decimal.Decimal(D))) for i in range(D // 2)],
+                        dtype=np.float64)
 
 
 def cos_sin_table(max_pos: int, D: int, base: float = 10000.0) -> np.ndarray:
@@ -34,7 +43,7 @@ def cos_sin_table(max_pos: int, D: int, base: float = 10000.0) -> np.ndarray:
     if D % 2:
         raise ValueError("head dimension must be even")
     theta = frequencies(D, base)
-    ang = np.arange(max_pos, dtype=np.float64)[:, None] * theta[None, :]
+    ang = (np.arange(max_pos, dtype=np.float64)[:, None] * theta[None, :]).astype(np.longdouble)
     return np.concatenate([np.cos(ang), np.sin(ang)], axis=1).astype(np.float32)
 
 

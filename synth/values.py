@@ -120,3 +120,35 @@ def range_values(seed: int, tensor: str, req: int, start: int, stop: int, n_head
     """``token_values`` for the contiguous positions ``[start, stop)``."""
     pos = torch.arange(start, stop, dtype=torch.int64, device=device)
     return token_values(seed, tensor, req, pos, n_heads, dim, dtype=dtype, device=device)
+
+
+def rows_values(seed: int, tensor: str, reqs, pos, n_heads: int, dim: int,
+                dtype: torch.dtype = torch.float32, device="cpu",
+                max_elems: int = 1 << 25) -> torch.Tensor:
+    """Values of ``tensor`` for rows given by (request, position) pairs: ``[n, n_heads, dim]``.
+
+    Equal to stacking ``token_values(seed, tensor, reqs[i], [pos[i]], ...)`` over the rows.
+    """
+    reqs = torch.as_tensor(reqs, dtype=torch.int64, device=device).reshape(-1)
+    pos = torch.as_tensor(pos, dtype=torch.int64, device=device).reshape(-1)
+    if reqs.shape != pos.shape:
+        raise ValueError("reqs and pos must have the same length")
+    if pos.numel():
+        if int(pos.min()) < 0 or int(pos.max()) >= (1 << POS_BITS):
+            raise ValueError("position out of range")
+        if int(reqs.min()) < 0 or int(reqs.max()) >= (1 << REQ_BITS):
+            raise ValueError("request index out of range")
+    if n_heads > (1 << HEAD_BITS) or dim > (1 << DIM_BITS):
+        raise ValueError("head or dim out of range")
+    table = quantile_table(dtype, device)
+    out = torch.empty((pos.numel(), n_heads, dim), dtype=dtype, device=device)
+    heads = torch.arange(n_heads, dtype=torch.int64, device=device) << HEAD_SHIFT
+    dims = torch.arange(dim, dtype=torch.int64, device=device)
+    hd = heads[:, None] + dims[None, :]
+    rows = max(1, max_elems // max(1, n_heads * dim))
+    base = TENSOR_ID[tensor] << TENSOR_SHIFT
+    for r0 in range(0, pos.numel(), rows):
+        rb = base + (reqs[r0:r0 + rows] << REQ_SHIFT) + (pos[r0:r0 + rows] << POS_SHIFT)
+        ctr = rb[:, None, None] + hd[None, :, :]
+        out[r0:r0 + rows] = table[_lsr(splitmix64_at(seed, ctr), 64 - TABLE_BITS)]
+    return out

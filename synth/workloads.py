@@ -117,3 +117,38 @@ CONFIGS = {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}
 
 def get(i: int) -> Workload:
     return CONFIGS[i]()
+
+
+def small(i: int) -> Workload:
+    """Scaled-down variants of the five workloads (same structure and draws, fewer heads and
+    tokens) that the oracle checks row by row in seconds while spanning several query tiles,
+    several key tiles and ragged tails."""
+    rng = np.random.Generator(np.random.PCG64(2000 + i))
+    if i == 1:
+        return config1()
+    if i == 2:   # MHA, 6 decodes, one prompt in 294-token chunks (3 query tiles), 5 steps
+        ctx = rng.integers(100, 700, size=6, endpoint=True)
+        return _make("small2_mha_bf16", "bf16", 4, 4, 128, 16, 300, ctx, ((1200, 0),), 5, 2002, rng)
+    if i == 3:   # 5 heads, decodes at 300, C = 128
+        return _make("small3_mha_bf16", "bf16", 5, 5, 128, 16, 132, [300] * 4, ((600, 0),), 6,
+                     2003, rng)
+    if i == 4:   # GQA group of 7, three prompts, several chunks per step
+        ctx = rng.integers(100, 900, size=8, endpoint=True)
+        z = rng.normal(math.log(400.0), 0.5, size=3)
+        lens = np.clip(np.rint(np.exp(z)), 1, 1200).astype(np.int64)
+        return _make("small4_gqa7_bf16", "bf16", 14, 2, 128, 16, 256, ctx,
+                     tuple((int(L), 0) for L in lens), None, 2004, rng, max_steps=32)
+    if i == 5:   # GQA group of 8, block 32, chunk of 500 after a 3000-token cached prefix
+        ctx = rng.integers(100, 3000, size=8, endpoint=True)
+        return _make("small5_gqa8_longctx_bf16", "bf16", 16, 2, 128, 32, 1024, ctx,
+                     ((3500, 3000),), 1, 2005, rng)
+    if i == 6:   # head dim 64 in bf16
+        ctx = rng.integers(20, 400, size=5, endpoint=True)
+        return _make("small6_d64_bf16", "bf16", 4, 2, 64, 16, 200, ctx, ((500, 0),), 3, 2006, rng)
+    if i == 7:   # float32 at head dim 128
+        ctx = rng.integers(20, 300, size=4, endpoint=True)
+        return _make("small7_d128_f32", "f32", 4, 4, 128, 16, 160, ctx, ((400, 0),), 3, 2007, rng)
+    raise KeyError(i)
+
+
+SMALL = (1, 2, 3, 4, 5, 6, 7)

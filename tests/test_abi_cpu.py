@@ -1,0 +1,234 @@
+"""CPU tests of libcb.so: exported symbols, the C++ builder against the oracle builder (bit-exact),
+atomic errors, the rotary table, and host-side argument checks of the device entry points (which
+return before any HIP call, so they run without a GPU)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+from hypothesis import HealthCheck, given, settings
+from hypothesis import strategies as st
+
+from oracle import rope as orope
+from oracle.builder import BuildError, RefBuilder
+from synth import workloads
+from tests.conftest import ROOT
+from tests.harness import step_caps
+
+from chunked_prefill_mixed_decode_amd import binding as cb
+
+HEADER = os.path.join(ROOT, "include", "cb.h")
+
+REASON = {cb.CB_ERR_INVALID: "invalid", cb.CB_ERR_DECODE_OVER_BUDGET: "decode_over_budget",
+          cb.CB_ERR_OUT_OF_BLOCKS: "out_of_blocks"}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def built_library():
+    if not os.path.exists(cb.LIB_PATH):
+        from chunked_prefill_mixed_decode_amd import build
+        build.build()
+    return cb._lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(cb_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert len(names) >= 14
+    lib = ctypes.CDLL(cb.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(cb.EXPORTS), "binding and header disagree"
+
+
+def test_status_strings():
+    for code in (0, -1, -2, -3, -4, -5, 42):
+        assert cb._lib().cb_status_string(code)
+
+
+def _pair(w: workloads.Workload):
+    ref = RefBuilder(w.block_size, w.num_blocks, w.free_list)
+    s = cb.cb_sched_create(w.block_size, w.num_blocks, w.free_list)
+    for c in w.decode_ctx:
+        assert ref.add_running(c) == cb.cb_sched_add_running(s, c)
+    for L, cached in w.prompts:
+        assert ref.add_prompt(L, cached) == cb.cb_sched_add_prompt(s, L, cached)
+    return ref, s
+
+
+def _same_plan(plan: dict, meta):
+    for k in cb.STEP_ARRAYS:
+        assert meta.host[k].tolist() == plan[k], k
+    for k in ("num_seqs", "num_decodes", "num_tokens", "num_prefill_tokens", "unused_tokens",
+              "max_q_len", "max_context_len", "num_blocks_emitted"):
+        assert getattr(meta, k) == plan[k], k
+    nd = plan["num_decodes"]
+    assert meta.max_decode_context_len == max(plan["context_lens"][:nd], default=0)
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_builder_matches_oracle_over_full_runs(cfg):
+    w = workloads.get(cfg)
+    ref, s = _pair(w)
+    buf = cb.StepBuffers(*step_caps(w), pin=False)
+    steps = 0
+    while True:
+        if w.steps is not None and steps == w.steps:
+            break
+        if w.steps is None and ref.pending_prompts() == 0:
+            break
+        plan = ref.build(w.budget)
+        meta = cb.cb_build_step(s, w.budget, buf)
+        _same_plan(plan, meta)
+        steps += 1
+        assert steps <= w.max_steps
+    for rid in range(len(w.decode_ctx) + len(w.prompts)):
+        assert cb.cb_sched_get_blocks(s, rid) == ref.blocks_of(rid)
+    assert cb.cb_sched_free_blocks(s) == len(ref.free)
+    if cfg == 2:
+        assert steps == 10
+    if cfg == 3:
+        assert steps == 9
+
+
+def test_worked_example_metadata_rounds():
+    # Derived from the budget-8 example of the zwjcode page, §03, with the identity free list.
+    w = workloads.get(1)
+    _, s = _pair(w)
+    buf = cb.StepBuffers(8, 8, 16, pin=False)
+    m = cb.cb_build_step(s, 8, buf)
+    assert m.host["positions"].tolist() == [16, 20, 24, 0, 1, 2, 3, 4]
+    assert m.host["slot_mapping"].tolist() == [80, 36, 72, 96, 97, 98, 99, 100]
+    assert m.host["context_lens"].tolist() == [17, 21, 25, 5]
+    assert m.host["block_table"].tolist() == [0, 5, 1, 2, 3, 4, 6]
+
+
+@st.composite
+def scenario(draw):
+    bs = draw(st.sampled_from([1, 2, 4, 16]))
+    nb = draw(st.integers(0, 60))
+    perm = draw(st.permutations(list(range(nb))))
+    ops = draw(st.lists(st.one_of(
+        st.tuples(st.just("run"), st.integers(0, 40)),
+        st.tuples(st.just("prompt"), st.integers(0, 50), st.integers(-1, 50)),
+        st.tuples(st.just("build"), st.integers(0, 24)),
+        st.tuples(st.just("clone"), st.just(0))), max_size=40))
+    cap = draw(st.sampled_from([0, 0, 3]))
+    return bs, nb, perm, ops, cap
+
+
+@settings(max_examples=300, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(scenario())
+def test_builder_matches_oracle_random(sc):
+    bs, nb, perm, ops, cap = sc
+    ref = RefBuilder(bs, nb, perm, max_chunk=cap)
+    s = cb.cb_sched_create(bs, nb, perm, max_chunk=cap)
+    buf = cb.StepBuffers(64, 32, 256, pin=False)
+    rids = []
+    for op in ops:
+        if op[0] == "run":
+            try:
+                want = ref.add_running(op[1])
+            except BuildError as e:
+                with pytest.raises(cb.CbError) as ce:
+                    cb.cb_sched_add_running(s, op[1])
+                assert REASON[ce.value.status] == e.reason
+            else:
+                assert cb.cb_sched_add_running(s, op[1]) == want
+                rids.append(want)
+        elif op[0] == "prompt":
+            try:
+                want = ref.add_prompt(op[1], op[2])
+            except BuildError as e:
+                with pytest.raises(cb.CbError) as ce:
+                    cb.cb_sched_add_prompt(s, op[1], op[2])
+                assert REASON[ce.value.status] == e.reason
+            else:
+                assert cb.cb_sched_add_prompt(s, op[1], op[2]) == want
+                rids.append(want)
+        elif op[0] == "clone":
+            s2 = cb.cb_sched_clone(s)
+            del s
+            s = s2
+        else:
+            try:
+                plan = ref.build(op[1])
+            except BuildError as e:
+                with pytest.raises(cb.CbError) as ce:
+                    cb.cb_build_step(s, op[1], buf)
+                assert REASON[ce.value.status] == e.reason
+            else:
+                _same_plan(plan, cb.cb_build_step(s, op[1], buf))
+        for r in rids:
+            assert cb.cb_sched_get_blocks(s, r) == ref.blocks_of(r)
+        assert cb.cb_sched_pending_prompts(s) == ref.pending_prompts()
+        assert cb.cb_sched_free_blocks(s) == len(ref.free)
+
+
+def test_capacity_error_reports_sizes_and_changes_nothing():
+    w = workloads.get(2)
+    ref, s = _pair(w)
+    small = cb.StepBuffers(4, 8, 8, pin=False)
+    with pytest.raises(cb.CbError) as e:
+        cb.cb_build_step(s, w.budget, small)
+    assert e.value.status == cb.CB_ERR_CAPACITY
+    assert small.step.cap_seqs == 65 and small.step.cap_tokens == 512
+    _same_plan(ref.build(w.budget), cb.cb_build_step(s, w.budget, cb.StepBuffers(*step_caps(w), pin=False)))
+
+
+def test_decode_over_budget_and_out_of_blocks_are_atomic():
+    s = cb.cb_sched_create(4, 3)
+    for _ in range(3):
+        cb.cb_sched_add_running(s, 4)
+    buf = cb.StepBuffers(8, 8, 8, pin=False)
+    with pytest.raises(cb.CbError) as e:
+        cb.cb_build_step(s, 2, buf)
+    assert e.value.status == cb.CB_ERR_DECODE_OVER_BUDGET
+    with pytest.raises(cb.CbError) as e:
+        cb.cb_build_step(s, 8, buf)          # every decode needs a fifth-token block; pool empty
+    assert e.value.status == cb.CB_ERR_OUT_OF_BLOCKS
+    assert [cb.cb_sched_get_blocks(s, r) for r in range(3)] == [[0], [1], [2]]
+
+
+@pytest.mark.parametrize("max_pos,D", [(64, 64), (5000, 128), (300000, 128)])
+def test_rope_table_matches_oracle_bit_exact(max_pos, D):
+    lib = cb.cb_rope_cos_sin(max_pos, D).numpy()
+    ora = orope.cos_sin_table(max_pos, D)
+    assert np.array_equal(lib.view(np.uint32), ora.view(np.uint32))
+
+
+def test_device_entry_points_reject_bad_arguments_on_the_host():
+    lib = cb._lib()
+    # D = 96 is unsupported; dtype 7 unknown; Hq not a multiple of Hkv
+    assert lib.cb_rope_kv_append(None, 1, 4, 4, 4, 96, 16, None, None, None, None, None, None, 8,
+                                 None, None, None, 4) == cb.CB_ERR_INVALID
+    assert lib.cb_rope_kv_append(None, 7, 4, 4, 4, 128, 16, None, None, None, None, None, None, 8,
+                                 None, None, None, 4) == cb.CB_ERR_INVALID
+    assert lib.cb_mixed_paged_attention(None, 1, 2, 1, 5, 4, 10, 10, 6, 4, 128, 16, 0.1, *([None] * 8),
+                                        None, 0) == cb.CB_ERR_INVALID
+    assert lib.cb_attn_workspace_bytes(2, 1, 5, 4, 10, 10, 6, 4, 128) == 0
+    # workspace too small
+    buf = ctypes.create_string_buffer(64)
+    p = ctypes.cast(buf, ctypes.c_void_p)
+    aligned = ctypes.c_void_p((p.value + 255) // 256 * 256)
+    need = lib.cb_attn_workspace_bytes(2, 1, 5, 4, 10, 10, 8, 4, 128)
+    assert need > 0
+    assert lib.cb_mixed_paged_attention(None, 1, 2, 1, 5, 4, 10, 10, 8, 4, 128, 16, 0.1, *([p] * 7),
+                                        p, aligned, need - 1) == cb.CB_ERR_CAPACITY
+
+
+def test_workspace_grows_with_context_and_rows():
+    f = cb.cb_attn_workspace_bytes
+    a = f(65, 64, 512, 448, 4097, 4097, 32, 32, 128)
+    b = f(129, 128, 576, 448, 4097, 4097, 32, 32, 128)
+    assert 0 < a < b
+    # decode partitions grow to at most 4096 keys: ceil(300000 / 4096) = 74 partials per head
+    assert f(2, 1, 2, 1, 300000, 300000, 8, 8, 128) <= 74 * 8 * 130 * 4 + 8 * 8 * 130 * 4 + 4 * 256
+    assert f(0, 0, 0, 0, 0, 0, 32, 32, 128) == 0

@@ -1,0 +1,303 @@
+"""GPU parity of the HIP path (through the C ABI) against the oracle.
+
+Bars: step metadata and every written K/V slot bit-exact; rotated queries bit-exact; attention
+outputs |gpu - oracle| <= atol + rtol |oracle| with (atol, rtol) = (1e-4, 0) for float32 and
+(2e-2, 1e-2) for bfloat16 (float32 accumulation).  Cache elements outside the written slots keep
+their all-ones sentinel.  Scaled-down workloads are checked on every row of every step; the five
+full-size workloads on sampled rows and slots, in the same launch configuration as the benchmark.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention as oattn
+from oracle import rope as orope
+from synth import workloads
+from tests.harness import GpuRun, OracleRun, bits_of, compare, plan_of_meta
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "the gpu tests need a GPU"
+    from chunked_prefill_mixed_decode_amd import binding
+    binding._lib()
+    return torch.device("cuda:0")
+
+
+def check_metadata(meta, plan):
+    got = plan_of_meta(meta)
+    for k in ("seq_ids", "cu_seqlens_q", "context_lens", "cu_blocks", "block_table", "positions",
+              "slot_mapping", "num_seqs", "num_decodes", "num_tokens", "unused_tokens"):
+        assert got[k] == plan[k], k
+
+
+def check_step_kv(gpu: GpuRun, ora: OracleRun, plan, rows):
+    """K/V written by the step's ``rows`` are bit-exact."""
+    cu = plan["cu_seqlens_q"]
+    for s in range(plan["num_seqs"]):
+        srows = [r for r in range(cu[s], cu[s + 1]) if r in rows]
+        if not srows:
+            continue
+        rid = plan["seq_ids"][s]
+        pos = np.array([plan["positions"][r] for r in srows])
+        slots = np.array([plan["slot_mapping"][r] for r in srows])
+        kw, vw = ora.expected_kv(rid, pos)
+        _, _, kb, vb = gpu.cache_rows(slots)
+        for name, got, want in (("K", kb, bits_of(kw, gpu.w.dtype)), ("V", vb, bits_of(vw, gpu.w.dtype))):
+            bad = np.argwhere(got != want)
+            if len(bad):
+                i = tuple(bad[0])
+                say(f"  {name} mismatch request {rid}: {len(bad)} of {got.size} elements; first at "
+                    f"(row {i[0]} pos {pos[i[0]]}, head {i[1]}, dim {i[2]}): got {got[i]} want {want[i]}")
+            assert not len(bad), f"{name} slots of request {rid}"
+
+
+def check_q_rot(gpu: GpuRun, ora: OracleRun, plan, q_rot, rows):
+    cu = plan["cu_seqlens_q"]
+    got = q_rot.float().cpu().numpy()
+    for s in range(plan["num_seqs"]):
+        srows = [r for r in range(cu[s], cu[s + 1]) if r in rows]
+        if not srows:
+            continue
+        pos = np.array([plan["positions"][r] for r in srows])
+        want = orope.rotate_stored(ora.raw("q", plan["seq_ids"][s], pos), pos, ora.table, gpu.w.dtype)
+        assert np.array_equal(bits_of(got[srows], gpu.w.dtype), bits_of(want, gpu.w.dtype))
+
+
+def check_outputs(gpu: GpuRun, ora: OracleRun, plan, out, rows, tag):
+    want = ora.expected_rows(plan, rows)
+    got = out.float().cpu().numpy()
+    rs = sorted(want)
+    ok, mabs, mrel = compare(got[rs], np.stack([want[r] for r in rs]), gpu.w.dtype)
+    say(f"  {tag}: {len(rs)} rows, max|err| {mabs:.3e}, max rel {mrel:.3e}")
+    assert ok, f"{tag}: max abs {mabs}, max rel {mrel}"
+    return mabs
+
+
+def sample_rows(plan, n_dec, n_chunk, seed):
+    rng = np.random.default_rng(seed)
+    nd, T = plan["num_decodes"], plan["num_tokens"]
+    rows = set()
+    if nd:
+        rows |= set(rng.choice(nd, size=min(n_dec, nd), replace=False).tolist())
+        rows |= {0, nd - 1}
+    if T > nd:
+        cu = plan["cu_seqlens_q"]
+        for s in range(nd, plan["num_seqs"]):                 # first and last rows of each chunk
+            rows |= {cu[s], cu[s + 1] - 1}
+        rows |= set((nd + rng.choice(T - nd, size=min(n_chunk, T - nd), replace=False)).tolist())
+    return rows
+
+
+# ---------------------------------------------------------------------------------------------
+# Scaled-down workloads: every row of every step.
+# ---------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("i", workloads.SMALL)
+def test_small_workload_every_row_every_step(dev, i):
+    w = workloads.small(i)
+    say(f"[{w.name}] set-up")
+    gpu = GpuRun(w, dev)
+    ora = OracleRun(w, value_device=dev)
+    step = 0
+    while (w.steps is None and ora.b.pending_prompts() > 0) or (w.steps is not None and step < w.steps):
+        say(f"[{w.name}] step {step}")
+        plan = ora.build()
+        meta, out, q_rot = gpu.step()
+        torch.cuda.synchronize()
+        check_metadata(meta, plan)
+        rows = set(range(plan["num_tokens"]))
+        check_step_kv(gpu, ora, plan, rows)
+        check_q_rot(gpu, ora, plan, q_rot, rows)
+        check_outputs(gpu, ora, plan, out, None, f"step {step}")
+        step += 1
+        assert step <= w.max_steps
+    # set-up slots too, and nothing written outside the slots
+    nd = len(w.decode_ctx)
+    for rid, n in [(r, c) for r, c in enumerate(w.decode_ctx)] + \
+                  [(nd + j, c) for j, (_, c) in enumerate(w.prompts) if c]:
+        blocks = np.array(gpu.cb.cb_sched_get_blocks(gpu.sched, rid))
+        pos = np.arange(n)
+        slots = blocks[pos // w.block_size] * w.block_size + pos % w.block_size
+        kw, vw = ora.expected_kv(rid, pos)
+        _, _, kb, vb = gpu.cache_rows(slots)
+        assert np.array_equal(kb, bits_of(kw, w.dtype)) and np.array_equal(vb, bits_of(vw, w.dtype))
+    total = 2 * gpu.runner.k_cache.numel()
+    assert gpu.sentinel_count() == total - 2 * gpu.written * w.Hkv * w.D
+
+
+# ---------------------------------------------------------------------------------------------
+# Full-size workloads: sampled rows and slots at the benchmark's launch configuration.
+# ---------------------------------------------------------------------------------------------
+FULL_SAMPLE = {1: (8, 8, 1), 2: (8, 24, 1), 3: (8, 24, 1), 4: (4, 12, 4), 5: (16, 12, 1)}
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_full_workload_sampled(dev, cfg):
+    w = workloads.get(cfg)
+    n_dec, n_chunk, every = FULL_SAMPLE[cfg]
+    say(f"[{w.name}] set-up: {len(w.decode_ctx)} decodes, {w.num_blocks} blocks")
+    gpu = GpuRun(w, dev)
+    ora = OracleRun(w, value_device=dev)
+    step = 0
+    while (w.steps is None and ora.b.pending_prompts() > 0) or (w.steps is not None and step < w.steps):
+        plan = ora.build()
+        meta, out, q_rot = gpu.step()
+        torch.cuda.synchronize()
+        check_metadata(meta, plan)
+        if step % every == 0 or step == (w.steps or 0) - 1:
+            say(f"[{w.name}] step {step}: T={plan['num_tokens']} nd={plan['num_decodes']}")
+            rows = sample_rows(plan, n_dec, n_chunk, seed=step)
+            check_step_kv(gpu, ora, plan, rows)
+            check_q_rot(gpu, ora, plan, q_rot, rows)
+            check_outputs(gpu, ora, plan, out, rows, f"step {step}")
+        step += 1
+    total = 2 * gpu.runner.k_cache.numel()
+    assert gpu.sentinel_count() == total - 2 * gpu.written * w.Hkv * w.D
+
+
+# ---------------------------------------------------------------------------------------------
+# Invariants of the method on the GPU path.
+# ---------------------------------------------------------------------------------------------
+def test_chunked_run_equals_monolithic_run(dev):
+    # "Chunked Prefill 的 Token 预算", intro and §02: chunking changes when work happens, not the
+    # final cache; rows match the unchunked computation.
+    w = workloads.small(2)
+    big = w.budget * 8
+    chunked, mono = GpuRun(w, dev), GpuRun(w, dev, max_budget=big)
+    prompt = len(w.decode_ctx)
+    outs_c, outs_m = {}, {}
+    while True:
+        meta, out, _ = chunked.step()
+        h = plan_of_meta(meta)
+        for s in range(meta.num_decodes, meta.num_seqs):
+            for r in range(h["cu_seqlens_q"][s], h["cu_seqlens_q"][s + 1]):
+                outs_c[h["positions"][r]] = out[r].float().cpu().numpy()
+        if gpu_pending(chunked) == 0:
+            break
+    meta, out, _ = mono.step(budget=big)
+    h = plan_of_meta(meta)
+    assert meta.num_seqs == len(w.decode_ctx) + 1
+    s = meta.num_seqs - 1
+    for r in range(h["cu_seqlens_q"][s], h["cu_seqlens_q"][s + 1]):
+        outs_m[h["positions"][r]] = out[r].float().cpu().numpy()
+    assert sorted(outs_c) == sorted(outs_m) == list(range(w.prompts[0][0]))
+    diff = max(float(np.abs(outs_c[p] - outs_m[p]).max()) for p in outs_c)
+    say(f"  chunked vs monolithic max|diff| {diff:.3e}")
+    assert diff <= 2 * 2e-2
+    blocks = np.array(chunked.cb.cb_sched_get_blocks(chunked.sched, prompt))
+    assert blocks.tolist() == mono.cb.cb_sched_get_blocks(mono.sched, prompt)
+    pos = np.arange(w.prompts[0][0])
+    slots = blocks[pos // w.block_size] * w.block_size + pos % w.block_size
+    a, b = chunked.cache_rows(slots), mono.cache_rows(slots)
+    assert np.array_equal(a[2], b[2]) and np.array_equal(a[3], b[3])     # bit-identical K and V
+
+
+def gpu_pending(g: GpuRun) -> int:
+    return g.cb.cb_sched_pending_prompts(g.sched)
+
+
+def test_run_to_run_bitwise_determinism_and_decode_isolation(dev):
+    w = workloads.small(4)
+    g = GpuRun(w, dev)
+    g.step()                                   # advance once so chunks have a cached prefix
+    snap = g.cb.cb_sched_clone(g.sched)
+    meta, out1, _ = g.step()
+    out1 = out1.clone()
+    g.sched = g.cb.cb_sched_clone(snap)        # replay the same step: identical appends
+    meta2, out2, _ = g.step()
+    assert meta.num_tokens == meta2.num_tokens and meta.num_prefill_tokens > 0
+    assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
+    g.sched = g.cb.cb_sched_clone(snap)        # decodes alone: same decode rows, bit for bit
+    meta3, out3, _ = g.step(budget=meta.num_decodes)
+    assert meta3.num_prefill_tokens == 0
+    nd = meta.num_decodes
+    assert torch.equal(out1[:nd].view(torch.int16), out3[:nd].view(torch.int16))
+
+
+def test_planted_mistakes_are_caught(dev):
+    # zwjcode §07: a chunk's positions restarted at 0, or its rows blind to the cached prefix,
+    # give different results; planted in the oracle, they must fail the parity bar.
+    w = workloads.small(3)
+    gpu, ora = GpuRun(w, dev), OracleRun(w, value_device=dev)
+    for _ in range(2):
+        plan = ora.build()
+        meta, out, _ = gpu.step()
+    torch.cuda.synchronize()
+    nd = plan["num_decodes"]
+    s = nd
+    cu = plan["cu_seqlens_q"]
+    rows = list(range(cu[s], cu[s + 1]))
+    pos = np.array([plan["positions"][r] for r in rows])
+    c = int(pos[0])
+    assert c > 0
+    rid = plan["seq_ids"][s]
+    got = out[rows].float().cpu().numpy()
+    good = np.stack([ora.expected_rows(plan, rows)[r] for r in rows])
+    assert compare(got, good, w.dtype)[0]
+    # (a) positions reset to 0 inside the chunk
+    local = pos - c
+    q_bad = orope.rotate_stored(ora.raw("q", rid, pos), local, ora.table, w.dtype)
+    kpos = np.arange(pos[-1] + 1)
+    kpos_bad = np.concatenate([kpos[:c], kpos[c:] - c])
+    k_bad = orope.rotate_stored(ora.raw("k", rid, kpos), kpos_bad, ora.table, w.dtype)
+    v = ora.raw("v", rid, kpos)
+    bad_a = oattn.attend(q_bad, k_bad, v, pos, ora.scale)
+    assert not compare(got, bad_a, w.dtype)[0]
+    # (b) chunk-local visibility {c .. c + i}
+    kh, _ = ora.expected_kv(rid, kpos)
+    qh = orope.rotate_stored(ora.raw("q", rid, pos), pos, ora.table, w.dtype)
+    bad_b = oattn.attend(qh, kh[c:], v[c:], pos - c, ora.scale)
+    assert not compare(got, bad_b, w.dtype)[0]
+
+
+def test_edge_steps(dev):
+    """Decode-only steps, chunk-only steps, one-token prompts and a one-token budget."""
+    from synth.workloads import _make
+    rng = np.random.default_rng(0)
+    cases = [
+        _make("edge_decode_only", "bf16", 4, 2, 128, 16, 3, (17, 1, 64), (), 3, 3001, np.random.default_rng(1)),
+        _make("edge_chunk_only", "bf16", 8, 8, 128, 16, 97, (), ((300, 0), (1, 0), (2, 0)), 5, 3002, np.random.default_rng(2)),
+        _make("edge_budget_one", "bf16", 2, 1, 64, 8, 1, (), ((5, 0),), 6, 3003, np.random.default_rng(3)),
+        _make("edge_cached_all_but_one", "bf16", 4, 4, 128, 32, 64, (40,), ((200, 199),), 2, 3004, np.random.default_rng(4)),
+    ]
+    del rng
+    for w in cases:
+        say(f"[{w.name}]")
+        gpu, ora = GpuRun(w, dev), OracleRun(w, value_device=dev)
+        for step in range(w.steps):
+            plan = ora.build()
+            meta, out, q_rot = gpu.step()
+            torch.cuda.synchronize()
+            check_metadata(meta, plan)
+            if plan["num_tokens"] == 0:
+                continue
+            rows = set(range(plan["num_tokens"]))
+            check_step_kv(gpu, ora, plan, rows)
+            check_outputs(gpu, ora, plan, out, None, f"{w.name} step {step}")
+
+
+def test_rope_append_skips_invalid_rows(dev):
+    from chunked_prefill_mixed_decode_amd.runner import MixedStepRunner
+    r = MixedStepRunner(Hq=4, Hkv=2, D=128, block_size=16, num_blocks=4, dtype=torch.bfloat16,
+                        device=dev, max_pos=100, cap_seqs=4, cap_tokens=8, cap_blocks=8)
+    T = 5
+    q = torch.randn(T, 4, 128, device=dev).to(torch.bfloat16)
+    k = torch.randn(T, 2, 128, device=dev).to(torch.bfloat16)
+    v = torch.randn(T, 2, 128, device=dev).to(torch.bfloat16)
+    pos = torch.tensor([3, 100, 7, -1, 9], dtype=torch.int32, device=dev)      # rows 1, 3 invalid
+    slots = torch.tensor([0, 1, -1, 3, 64], dtype=torch.int32, device=dev)     # row 2 no slot, row 4 out of range
+    q_out = torch.full_like(q, float("nan"))
+    r.append({"positions": pos, "slot_mapping": slots}, q, k, v, q_out)
+    torch.cuda.synchronize()
+    assert torch.isnan(q_out[1].float()).all() and torch.isnan(q_out[3].float()).all()
+    assert not torch.isnan(q_out[[0, 2, 4]].float()).any()
+    kb = r.k_cache.view(torch.int16)
+    written = (kb != -1).any(dim=-1)            # [nb, Hkv, bs]
+    assert written.sum().item() == 2            # only row 0 (slot 0), one entry per KV head
+    assert written[0, :, 0].all()

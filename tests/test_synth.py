@@ -101,3 +101,11 @@ def test_workloads_shapes():
     w5 = workloads.get(5)
     assert w5.prompts == ((264192, 262144),) and w5.block_size == 32 and w5.group == 8
     assert workloads.get(2) == w2                           # seeded: identical on every call
+
+
+def test_rows_values_equal_per_request_values():
+    reqs = [0, 0, 3, 7, 3]
+    pos = [5, 6, 0, 100, 9]
+    got = values.rows_values(17, "k", reqs, pos, 3, 16)
+    for i, (r, p) in enumerate(zip(reqs, pos)):
+        assert torch.equal(got[i], values.token_values(17, "k", r, [p], 3, 16)[0])
