@@ -1,0 +1,241 @@
+"""Mixed-step benchmark on one MI355X: the 7B-like layer at token budget 512.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+Workload: 32 query / 32 KV heads, head dim 128, KV blocks of 16 tokens, bf16; 64 running decodes
+with contexts uniform on [512, 4096] and one 4096-token prompt under a budget of 512 tokens per
+step (64 decode rows + 448 chunk rows; the prompt's life is 10 steps: nine 448-token chunks and a
+64-token one).  A step is one pass of the whole hot path over one batch: the host batch build
+(C++), one host-to-device metadata copy, the rope + paged-KV-append kernel and the mixed
+attention (decode split, chunk tiles, combine).  The benchmark cycles through the prompt's ten
+steps, restoring the builder from a snapshot after each cycle (re-appending identical K/V to
+identical slots leaves the cache unchanged).  Every step's raw q/k/v are generated and resident in
+HBM before the timed region.
+
+Prints one JSON line.  ``roofline`` reports the dominant kernel (the decode split, bound by HBM):
+algorithmic bytes per launch (K and V of every decode context, plus q and out) divided by its
+average duration measured with HIP events on the launch stream over the timed steps.
+``cpu_baseline`` times the CPU oracle (reference builder + fp64 full-prefill attention with
+rotary embedding) on one step of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "mixed-step tokens/s + step latency; % bf16 MFMA peak (chunks), % HBM BW (decode)"
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2516.6
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2, help="workload index (default: the budget-512 layer)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-step", type=int, default=8)
+    ap.add_argument("--json-out", default=None)
+    return ap.parse_args()
+
+
+def decode_bytes(meta, w, elt: int) -> int:
+    """Algorithmic HBM bytes of the decode rows: K and V of every visible key, q and out."""
+    nd = meta.num_decodes
+    ctx = int(meta.host["context_lens"][:nd].sum())
+    return ctx * w.Hkv * w.D * 2 * elt + 2 * nd * w.Hq * w.D * elt
+
+
+def chunk_flops(meta, w) -> int:
+    """Algorithmic FLOPs of the chunk rows: 4 D Hq per visible (row, key) pair (QK^T and PV)."""
+    nd = meta.num_decodes
+    pos = meta.host["positions"][nd:meta.num_tokens].long()
+    return int((pos + 1).sum()) * 4 * w.D * w.Hq
+
+
+def cpu_baseline(w, step_index: int):
+    """The oracle on one step: Python reference builder up to that step, then fp64 attention
+    (rotary embedding included) of all the step's rows.  Raw inputs are generated beforehand."""
+    import numpy as np
+
+    from oracle import attention as oattn
+    from oracle import rope as orope
+    from oracle.builder import RefBuilder
+    from synth import values
+    from tests.gpu_harness import TORCH_DTYPE
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    b = RefBuilder(w.block_size, w.num_blocks, w.free_list)
+    for c in w.decode_ctx:
+        b.add_running(c)
+    for L, cached in w.prompts:
+        b.add_prompt(L, cached)
+    for _ in range(step_index):
+        b.build(w.budget)
+    # inputs of the step (untimed): raw q/k/v of every sequence up to its last row
+    probe = b.clone().build(w.budget)
+    dt = TORCH_DTYPE[w.dtype]
+    raw = {}
+    cu = probe["cu_seqlens_q"]
+    for s in range(probe["num_seqs"]):
+        rid = probe["seq_ids"][s]
+        last = probe["context_lens"][s]
+        pos = list(range(probe["positions"][cu[s]], probe["positions"][cu[s + 1] - 1] + 1))
+        raw[rid] = (values.range_values(w.seed, "k", rid, 0, last, w.Hkv, w.D, dt).float().numpy(),
+                    values.range_values(w.seed, "v", rid, 0, last, w.Hkv, w.D, dt).float().numpy(),
+                    values.token_values(w.seed, "q", rid, pos, w.Hq, w.D, dt).float().numpy())
+    table = orope.cos_sin_table(w.max_position(), w.D)
+    t0 = time.perf_counter()
+    plan = b.build(w.budget)
+    cu = plan["cu_seqlens_q"]
+    rows = 0
+    for s in range(plan["num_seqs"]):
+        rid = plan["seq_ids"][s]
+        k, v, q = raw[rid]
+        pos = np.array(plan["positions"][cu[s]:cu[s + 1]])
+        kh = orope.rotate_stored(k, np.arange(k.shape[0]), table, w.dtype)
+        qh = orope.rotate_stored(q, pos, table, w.dtype)
+        oattn.attend(qh, kh, v, pos, 1.0 / np.sqrt(w.D))
+        rows += len(pos)
+    el = time.perf_counter() - t0
+    return {"value": rows / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "seconds": el,
+            "sample": f"step {step_index} of the cycle: reference builder + rotary + fp64 causal "
+                      f"attention of all {rows} rows x {w.Hq} heads (raw inputs pre-generated)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: every box here has one GPU and this path has no "
+              f"multi-GPU leg (--gpus {args.gpus} is not supported)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from synth import workloads
+    from tests.gpu_harness import GpuRun
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    w = workloads.get(args.config)
+    cb_steps = w.steps
+    print(f"[bench] set-up {w.name}: {len(w.decode_ctx)} decodes, {w.num_blocks} blocks", file=sys.stderr, flush=True)
+    g = GpuRun(w, dev, sentinel=False)
+    cb = g.cb
+    snapshot = cb.cb_sched_clone(g.sched)
+
+    # One dry cycle learns each step's metadata; its inputs are generated and kept in HBM.
+    inputs, metas, ws = [], [], 0
+    probe = cb.cb_sched_clone(snapshot)
+    bufs = cb.StepBuffers(*g.runner.bufs[0].cap)
+    for k in range(cb_steps):
+        meta = cb.cb_build_step(probe, w.budget, bufs)
+        meta.host = {kk: vv.clone() for kk, vv in meta.host.items()}
+        metas.append(meta)
+        inputs.append(g.step_inputs(meta))
+        ws = max(ws, g.runner.workspace_bytes(meta))
+    g.runner.ensure_workspace(ws)
+    outs = [torch.empty_like(inp[0]) for inp in inputs]
+    qrots = [torch.empty_like(inp[0]) for inp in inputs]
+    torch.cuda.synchronize()
+
+    state = {"sched": cb.cb_sched_clone(snapshot), "k": 0}
+
+    def one_step(events=None):
+        k = state["k"]
+        meta = g.runner.build(state["sched"], w.budget)
+        dev_meta = g.runner.upload(meta)
+        q, kk, vv = inputs[k]
+        g.runner.append(dev_meta, q, kk, vv, qrots[k])
+        g.runner.attend(meta, dev_meta, qrots[k], outs[k], events=events)
+        state["k"] = k + 1
+        if state["k"] == cb_steps:
+            state["k"] = 0
+            state["sched"] = cb.cb_sched_clone(snapshot)
+        return meta.num_tokens, k
+
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+
+    # Per-step phase events (created and touched once so the runtime objects exist).
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for e4 in evs:
+        for e in e4:
+            e.record()
+    torch.cuda.synchronize()
+
+    tokens = 0
+    step_ids = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        n, k = one_step(evs[i])
+        tokens += n
+        step_ids.append(k)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+
+    dec_ms, chk_ms, cmb_ms = [], [], []
+    for e4 in evs:
+        dec_ms.append(e4[0].elapsed_time(e4[1]))
+        chk_ms.append(e4[1].elapsed_time(e4[2]))
+        cmb_ms.append(e4[2].elapsed_time(e4[3]))
+    elt = 2
+    dbytes = [decode_bytes(metas[k], w, elt) for k in step_ids]
+    cflops = [chunk_flops(metas[k], w) for k in step_ids]
+    dec_avg_s = sum(dec_ms) / len(dec_ms) / 1e3
+    achieved = sum(dbytes) / len(dbytes) / dec_avg_s / 1e9
+    chunk_tflops = sum(cflops) / (sum(chk_ms) / 1e3) / 1e12
+
+    res = {
+        "metric": METRIC,
+        "value": tokens / el,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": el / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded SplitMix64 normal-quantile activations; seeded workload structure)",
+        "config": {"workload": w.name, "heads_q": w.Hq, "heads_kv": w.Hkv, "head_dim": w.D,
+                   "block_size": w.block_size, "token_budget": w.budget,
+                   "decodes": len(w.decode_ctx), "prompt_len": w.prompts[0][0],
+                   "steps_per_cycle": cb_steps, "parallelism": "1 GPU"},
+        "roofline": {"bound": "hbm", "kernel": "decode_kernel (split-context decode rows)",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "bytes_per_launch": sum(dbytes) / len(dbytes), "avg_launch_us": dec_avg_s * 1e6},
+        "chunk_tiles": {"bound": "mfma", "achieved": chunk_tflops, "peak": MFMA_BF16_PEAK_TFLOPS,
+                        "unit": "TFLOP/s", "frac": chunk_tflops / MFMA_BF16_PEAK_TFLOPS,
+                        "avg_launch_us": sum(chk_ms) / len(chk_ms) * 1e3,
+                        "flops_per_step": sum(cflops) / len(cflops)},
+        "combine_avg_us": sum(cmb_ms) / len(cmb_ms) * 1e3,
+        "device_step_ms": None,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)...", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_step)
+    line = json.dumps(res)
+    print(line, flush=True)
+    if args.json_out:
+        with open(args.json_out, "w") as f:
+            f.write(line + "\n")
+
+
+if __name__ == "__main__":
+    main()
