@@ -29,9 +29,14 @@ namespace cb {
 namespace {
 
 constexpr int kChunkRows = 128;   // rows per chunk tile: 4 waves x 32
-constexpr int kChunkKeys = 64;    // keys per LDS tile
+constexpr int kChunkKeys = 32;    // keys per LDS stage of a chunk tile
 constexpr int kDecodeKeys = 32;   // keys per decode iteration
 constexpr int kMaxSplit = 8;
+constexpr int kMaxPart = 4096;                       // longest decode partition (keys)
+constexpr int kMinBlock = 8;
+constexpr int kMaxPartBlocks = kMaxPart / kMinBlock;
+constexpr int kMaxBlock = 256;
+constexpr int kBlockWindow = 2048;                   // block ids per LDS window (chunk tiles)
 
 struct Plan {
   int32_t G = 1, head_blocks = 1;
@@ -50,7 +55,7 @@ Plan make_plan(int32_t num_seqs, int32_t nd, int32_t T, int32_t max_q_len, int32
   p.head_blocks = (p.G + 15) / 16;
   if (nd > 0) {
     const int32_t want = (std::max(max_dctx, 1) + 15) / 16;   // ~16 partitions per longest row
-    while (p.part < want && p.part < 4096) p.part *= 2;
+    while (p.part < want && p.part < kMaxPart) p.part *= 2;
     p.max_parts = (std::max(max_dctx, 1) + p.part - 1) / p.part;
   }
   p.bmq = kChunkRows / p.G;
@@ -86,11 +91,127 @@ struct AttnArgs {
   float* dec_ml;
   float* chk_o;
   float* chk_ml;
-  int32_t num_seqs, nd, T, Hq, Hkv, G, bs;
+  int32_t num_seqs, nd, T, Hq, Hkv, G, bs, bs_shift;
   int32_t part, max_parts, head_blocks;
   int32_t bmq, q_blocks, n_chunk, nsplit;
   float scale_log2;
 };
+
+// ---------------------------------------------------------------------------------------------
+// LDS staging.  K and V rows are copied from HBM straight into LDS with the gfx950 16-byte LDS
+// DMA (global_load_lds_dwordx4): lane l of one instruction lands at byte 16 l of a 1 KB span.
+// Rows are chunk-swizzled: logical 16-byte chunk c of row r sits at chunk c ^ (r mod m), m the
+// smaller of 16 and the chunks per row, so the lanes that read one chunk of many rows hit
+// different banks.
+// ---------------------------------------------------------------------------------------------
+__device__ __forceinline__ int lds_chunk(int c, int r, int row_bytes) {
+  const int m = (row_bytes / 16 < 16 ? row_bytes / 16 : 16) - 1;
+  return c ^ (r & m);
+}
+__device__ __forceinline__ void lds_copy16(const char* src, char* lds_dst) {
+  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(src),
+                                   (void __attribute__((address_space(3)))*)(lds_dst),
+                                   16, 0, 0);
+}
+// Wait for this wave's LDS reads before a DMA overwrites the buffer they read
+// (s_waitcnt lgkmcnt(0), vmcnt and expcnt untouched).
+__device__ __forceinline__ void lds_reads_done() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// 8 consecutive elements [e0, e0 + 8) of row r.
+template <typename T>
+__device__ __forceinline__ Frag<T> lds_row_frag(const char* base, int r, int e0, int row_bytes) {
+  Frag<T> f;
+  const char* row = base + r * row_bytes;
+  const int b0 = e0 * static_cast<int>(sizeof(T));
+  if constexpr (sizeof(T) == 2) {
+    f.u = *reinterpret_cast<const uint4*>(row + 16 * lds_chunk(b0 >> 4, r, row_bytes));
+  } else {
+    const float4 x = *reinterpret_cast<const float4*>(row + 16 * lds_chunk(b0 >> 4, r, row_bytes));
+    const float4 y = *reinterpret_cast<const float4*>(row + 16 * lds_chunk((b0 >> 4) + 1, r, row_bytes));
+    f.f[0] = x.x; f.f[1] = x.y; f.f[2] = x.z; f.f[3] = x.w;
+    f.f[4] = y.x; f.f[5] = y.y; f.f[6] = y.z; f.f[7] = y.w;
+  }
+  return f;
+}
+
+// The V^T operand of a 16x16x32 step: lane (grp, col) gets dimension 16 dt + col of keys
+// 16 h + 4 grp + j (slot 4 h + j), h in {0, 1}, j in 0..3, from a 32-key stage of V rows.
+// bf16: two ds_read_b64_tr_b16, whose 16-lane groups return, to lane i, element i % 4 of the
+// 8-byte row piece addressed by lane 4 j + i / 4 -- so lane 4 j + q addresses row (key) base + j
+// at dimensions 16 dt + 4 q .. + 3.  float: eight 4-byte reads.
+template <typename T>
+__device__ __forceinline__ Frag<T> lds_vt_frag16(const char* base, int dt, int grp, int col, int row_bytes);
+template <>
+__device__ __forceinline__ Frag<bf16_t> lds_vt_frag16<bf16_t>(const char* base, int dt, int grp, int col, int row_bytes) {
+  typedef __attribute__((ext_vector_type(4))) short s4;
+  Frag<bf16_t> f;
+  const int j = col >> 2, qd = col & 3;
+  const int e = 16 * dt + 4 * qd;                 // first dimension addressed by this lane
+  uint32_t w[4];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int r = 16 * h + 4 * grp + j;
+    const char* addr = base + r * row_bytes + 16 * lds_chunk((2 * e) >> 4, r, row_bytes) + ((2 * e) & 15);
+    const s4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (s4 __attribute__((address_space(3)))*)(const_cast<char*>(addr)));
+    w[2 * h] = static_cast<uint16_t>(v[0]) | (static_cast<uint32_t>(static_cast<uint16_t>(v[1])) << 16);
+    w[2 * h + 1] = static_cast<uint16_t>(v[2]) | (static_cast<uint32_t>(static_cast<uint16_t>(v[3])) << 16);
+  }
+  f.u = make_uint4(w[0], w[1], w[2], w[3]);
+  return f;
+}
+template <>
+__device__ __forceinline__ Frag<float> lds_vt_frag16<float>(const char* base, int dt, int grp, int col, int row_bytes) {
+  Frag<float> f;
+  const int dim = 16 * dt + col;
+#pragma unroll
+  for (int jj = 0; jj < 8; ++jj) {
+    const int r = 16 * (jj >> 2) + 4 * grp + (jj & 3);
+    f.f[jj] = *reinterpret_cast<const float*>(base + r * row_bytes + 16 * lds_chunk((4 * dim) >> 4, r, row_bytes) + ((4 * dim) & 15));
+  }
+  return f;
+}
+
+// The V^T operand of a 32x32x16 step over keys [16 ps, 16 ps + 16) of a stage: lane l gets
+// dimension 32 mt + l % 32 of the keys in slot order 8 (l / 32) + jj <-> key
+// 16 ps + 8 (jj / 4) + 4 (l / 32) + jj % 4 (the key order of the S^T accumulator).
+template <typename T>
+__device__ __forceinline__ Frag<T> lds_vt_frag32(const char* base, int mt, int ps, int lane, int row_bytes);
+template <>
+__device__ __forceinline__ Frag<bf16_t> lds_vt_frag32<bf16_t>(const char* base, int mt, int ps, int lane, int row_bytes) {
+  typedef __attribute__((ext_vector_type(4))) short s4;
+  Frag<bf16_t> f;
+  const int grp = lane >> 4, i = lane & 15;
+  const int j = i >> 2, qd = i & 3;
+  const int e = 32 * mt + 16 * (grp & 1) + 4 * qd;
+  uint32_t w[4];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int r = 16 * ps + 8 * h + 4 * (grp >> 1) + j;
+    const char* addr = base + r * row_bytes + 16 * lds_chunk((2 * e) >> 4, r, row_bytes) + ((2 * e) & 15);
+    const s4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (s4 __attribute__((address_space(3)))*)(const_cast<char*>(addr)));
+    w[2 * h] = static_cast<uint16_t>(v[0]) | (static_cast<uint32_t>(static_cast<uint16_t>(v[1])) << 16);
+    w[2 * h + 1] = static_cast<uint16_t>(v[2]) | (static_cast<uint32_t>(static_cast<uint16_t>(v[3])) << 16);
+  }
+  f.u = make_uint4(w[0], w[1], w[2], w[3]);
+  return f;
+}
+template <>
+__device__ __forceinline__ Frag<float> lds_vt_frag32<float>(const char* base, int mt, int ps, int lane, int row_bytes) {
+  Frag<float> f;
+  const int dim = 32 * mt + (lane & 31);
+#pragma unroll
+  for (int jj = 0; jj < 8; ++jj) {
+    const int r = 16 * ps + 8 * (jj >> 2) + 4 * (lane >> 5) + (jj & 3);
+    f.f[jj] = *reinterpret_cast<const float*>(base + r * row_bytes + 16 * lds_chunk((4 * dim) >> 4, r, row_bytes) + ((4 * dim) & 15));
+  }
+  return f;
+}
+
+// Wait until this wave's LDS copies have landed (s_waitcnt vmcnt(0); lgkmcnt, expcnt untouched).
+// Other waves' copies are visible after the workgroup barrier that follows.
+__device__ __forceinline__ void lds_copies_done() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // ---------------------------------------------------------------------------------------------
 // Decode rows.
@@ -99,10 +220,12 @@ template <typename T, int D>
 __global__ __launch_bounds__(64) void decode_kernel(AttnArgs a) {
   constexpr int KS = D / 32;          // 32-slot contraction steps over the head dimension
   constexpr int DT = D / 16;          // 16-dim output tiles
-  constexpr int DC = D / 8;           // 8-element chunks per row
-  constexpr int QUADS = (kDecodeKeys / 4) * DC / 64;   // 4-key quads per lane per iteration
-  constexpr int VPAD = 16 / sizeof(T);
-  __shared__ __attribute__((aligned(16))) T sVt[D][kDecodeKeys + VPAD];
+  constexpr int ROW = D * sizeof(T);  // bytes per key row in LDS
+  constexpr int RPI = 1024 / ROW;     // key rows per 1 KB copy instruction
+  constexpr int NCP = kDecodeKeys / RPI;
+  __shared__ __attribute__((aligned(1024))) char sK[kDecodeKeys * ROW];
+  __shared__ __attribute__((aligned(1024))) char sV[kDecodeKeys * ROW];
+  __shared__ int32_t sBlk[kMaxPartBlocks];
 
   const int lane = threadIdx.x;
   int64_t item = blockIdx.x;
@@ -114,17 +237,25 @@ __global__ __launch_bounds__(64) void decode_kernel(AttnArgs a) {
   const int32_t k_lo = p * a.part;
   if (k_lo >= ctx) return;
   const int32_t k_hi = min(ctx, k_lo + a.part);
+  const int32_t k_last = k_hi - 1;
   const int32_t gh = min(16, a.G - 16 * hb);
   const int32_t h0 = g * a.G + 16 * hb;
   const int32_t col = lane & 15;      // head owned by this lane in S^T / P^T / O^T
   const int32_t grp = lane >> 4;      // slot group
+  const int bsh = a.bs_shift;
+  const int32_t bmask = (1 << bsh) - 1;
 
   const T* q = static_cast<const T*>(a.q);
-  const T* kc = static_cast<const T*>(a.k_cache);
-  const T* vc = static_cast<const T*>(a.v_cache);
-  const int32_t* btab = a.block_table + a.cu_blocks[s];
-  const int32_t bs = a.bs;
+  const char* kc = static_cast<const char*>(a.k_cache);
+  const char* vc = static_cast<const char*>(a.v_cache);
 
+  // The partition's physical block ids, read once into LDS.
+  const int32_t b_lo = k_lo >> bsh;
+  {
+    const int32_t* btab = a.block_table + a.cu_blocks[s] + b_lo;
+    const int32_t nblk = ((k_hi - 1) >> bsh) - b_lo + 1;
+    for (int32_t i = lane; i < nblk; i += 64) sBlk[i] = btab[i];
+  }
   Frag<T> qf[KS];
   {
     const T* qrow = q + (static_cast<int64_t>(s) * a.Hq + h0 + col) * D;
@@ -134,46 +265,48 @@ __global__ __launch_bounds__(64) void decode_kernel(AttnArgs a) {
       else qf[ks].zero();
     }
   }
+  __syncthreads();
+
+  // Copy the 32 keys' K and V rows straight into LDS (no registers), chunk-swizzled.  Keys past
+  // the partition repeat its last key; they are masked out of the softmax.
+  const int64_t head_bytes = static_cast<int64_t>(g) * ((int64_t)ROW << bsh);
+  const int64_t blk_bytes = static_cast<int64_t>(a.Hkv) * ((int64_t)ROW << bsh);
+  const int cp_row = lane / (ROW / 16), cp_pos = lane % (ROW / 16);
+  auto issue = [&](int32_t key0) {
+#pragma unroll
+    for (int i = 0; i < NCP; ++i) {
+      const int r = i * RPI + cp_row;                        // row within the stage
+      const int32_t key = min(key0 + r, k_last);
+      const int64_t off = static_cast<int64_t>(sBlk[(key >> bsh) - b_lo]) * blk_bytes + head_bytes +
+                          static_cast<int64_t>(key & bmask) * ROW + 16 * lds_chunk(cp_pos, r, ROW);
+      lds_copy16(kc + off, sK + i * 1024);
+      lds_copy16(vc + off, sV + i * 1024);
+    }
+  };
 
   float m_run = kNegInf, l_run = 0.f;
   f32x4 o[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int vchunk = lane % DC;
-  const int vquad0 = lane / DC;
-
+  issue(k_lo);
   for (int32_t key0 = k_lo; key0 < k_hi; key0 += kDecodeKeys) {
+    // Operands of this stage into registers (the copy above has landed: the compiler waits for it
+    // before the first LDS read), then the next stage's copy, which overlaps the compute below.
     Frag<T> kf[2][KS];
 #pragma unroll
-    for (int kg = 0; kg < 2; ++kg) {
-      const int32_t key = key0 + 16 * kg + col;
-      if (key < k_hi) {
-        const T* kp = kc + ((static_cast<int64_t>(btab[key / bs]) * a.Hkv + g) * bs + key % bs) * D;
+    for (int kg = 0; kg < 2; ++kg)
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) kf[kg][ks].load(kp + 32 * ks + 8 * grp);
-      } else {
+      for (int ks = 0; ks < KS; ++ks) kf[kg][ks] = lds_row_frag<T>(sK, 16 * kg + col, 32 * ks + 8 * grp, ROW);
+    Frag<T> vt[DT];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) kf[kg][ks].zero();
-      }
-    }
-    Frag<T> vf[QUADS][4];
-#pragma unroll
-    for (int i = 0; i < QUADS; ++i) {
-      const int quad = vquad0 + (64 / DC) * i;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int32_t key = key0 + 4 * quad + e;
-        if (key < k_hi) {
-          const T* vp = vc + ((static_cast<int64_t>(btab[key / bs]) * a.Hkv + g) * bs + key % bs) * D;
-          vf[i][e].load(vp + 8 * vchunk);
-        } else {
-          vf[i][e].zero();
-        }
-      }
+    for (int dt = 0; dt < DT; ++dt) vt[dt] = lds_vt_frag16<T>(sV, dt, grp, col, ROW);
+    if (key0 + kDecodeKeys < k_hi) {
+      lds_reads_done();
+      issue(key0 + kDecodeKeys);
     }
 
-    // S^T[key, head] for the 32 keys: lane holds keys 16 kg + 4 grp + r of head col.
+    // S^T[key, head]: lane holds keys 16 kg + 4 grp + r of head col.
     f32x4 st[2];
 #pragma unroll
     for (int kg = 0; kg < 2; ++kg) {
@@ -203,41 +336,12 @@ __global__ __launch_bounds__(64) void decode_kernel(AttnArgs a) {
     }
     l_run = l_run * alpha + psum;
     m_run = m_new;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
     Frag<T> pf;   // P^T slot 8 grp + j <-> key 16 (j / 4) + 4 grp + j % 4 (same order as sv)
     pf.set_all(pv);
-
-    // V^T into LDS: key 16 b + 4 a + c goes to slot 8 a + 4 b + c of its dimension row.
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < QUADS; ++i) {
-      const int quad = vquad0 + (64 / DC) * i;
-      const int slot0 = 8 * (quad & 3) + 4 * (quad >> 2);
-#pragma unroll
-      for (int d = 0; d < 8; ++d) {
-        T* dst = &sVt[8 * vchunk + d][slot0];
-        if constexpr (sizeof(T) == 2) {
-          const uint32_t* w0 = &vf[i][0].u.x;
-          const uint32_t* w1 = &vf[i][1].u.x;
-          const uint32_t* w2 = &vf[i][2].u.x;
-          const uint32_t* w3 = &vf[i][3].u.x;
-          const int sh = 16 * (d & 1);
-          const uint32_t lo = ((w0[d >> 1] >> sh) & 0xffffu) | (((w1[d >> 1] >> sh) & 0xffffu) << 16);
-          const uint32_t hi = ((w2[d >> 1] >> sh) & 0xffffu) | (((w3[d >> 1] >> sh) & 0xffffu) << 16);
-          *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
-        } else {
-          *reinterpret_cast<float4*>(dst) =
-              make_float4(vf[i][0].get(d), vf[i][1].get(d), vf[i][2].get(d), vf[i][3].get(d));
-        }
-      }
-    }
-    __syncthreads();
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      Frag<T> vt;
-      vt.load(&sVt[16 * dt + col][8 * grp]);
-      mma16_k32(o[dt], vt, pf);
+      o[dt] *= alpha;
+      mma16_k32(o[dt], vt[dt], pf);
     }
   }
 
@@ -270,17 +374,15 @@ __device__ __forceinline__ void store4<float>(float* dst, float x0, float x1, fl
 }
 
 template <typename T, int D>
-__global__ __launch_bounds__(256) void chunk_kernel(AttnArgs a, int32_t n_tiles, int32_t per_xcd) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void chunk_kernel(AttnArgs a, int32_t n_tiles, int32_t per_xcd) {
   constexpr int KS = D / 16;          // 16-slot contraction steps over the head dimension
   constexpr int MT = D / 32;          // 32-dim output tiles
-  constexpr int DC = D / 8;           // 8-element chunks per key row
-  constexpr int KPAD = 16 / sizeof(T);
-  constexpr int VPAD = 16 / sizeof(T);
-  constexpr int KLOADS = kChunkKeys * DC / 256;            // K chunks per thread per tile
-  constexpr int VPAIRS = (kChunkKeys / 4) * DC;            // (quad, chunk) pairs per tile
-  constexpr int VLOADS = (VPAIRS + 255) / 256;
-  __shared__ __attribute__((aligned(16))) T sK[kChunkKeys][D + KPAD];
-  __shared__ __attribute__((aligned(16))) T sVt[D][kChunkKeys + VPAD];
+  constexpr int ROW = D * sizeof(T);  // bytes per key row in LDS
+  constexpr int RPI = 1024 / ROW;     // key rows per 1 KB copy instruction
+  constexpr int NCPW = kChunkKeys / RPI / 4;    // copy instructions per wave per tensor
+  __shared__ __attribute__((aligned(1024))) char sK[kChunkKeys * ROW];
+  __shared__ __attribute__((aligned(1024))) char sV[kChunkKeys * ROW];
+  __shared__ int32_t sBlk[kBlockWindow];       // a window of the sequence's block table
 
   // XCD-aware order: workgroup b runs on XCD b % 8; give each XCD a contiguous run of logical
   // tiles so that the tiles sharing one (chunk, KV head) K/V stream share that XCD's L2.
@@ -316,10 +418,11 @@ __global__ __launch_bounds__(256) void chunk_kernel(AttnArgs a, int32_t n_tiles,
   const int32_t qpos = valid ? c + pos_local : 0x7fffffff;      // padding rows see everything
 
   const T* q = static_cast<const T*>(a.q);
-  const T* kc = static_cast<const T*>(a.k_cache);
-  const T* vc = static_cast<const T*>(a.v_cache);
+  const char* kc = static_cast<const char*>(a.k_cache);
+  const char* vc = static_cast<const char*>(a.v_cache);
   const int32_t* btab = a.block_table + a.cu_blocks[s];
-  const int32_t bs = a.bs;
+  const int bsh = a.bs_shift;
+  const int32_t bmask = (1 << bsh) - 1;
 
   Frag<T> qf[KS];
   {
@@ -336,104 +439,78 @@ __global__ __launch_bounds__(256) void chunk_kernel(AttnArgs a, int32_t n_tiles,
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) o[mt] = f32x16{};
 
-  Frag<T> kreg[KLOADS];
-  Frag<T> vreg[VLOADS][4];
-  auto gload = [&](int32_t kt) {
+  // Block ids come from an LDS window [win_lo, win_lo + kBlockWindow) of the block table.  K and V
+  // rows go HBM -> LDS by DMA (chunk-swizzled rows); keys at or past kv_end repeat kv_end - 1 and
+  // are masked (probability 0).  Each stage is read whole into registers before the next copy is
+  // issued into the same buffer, so the copy overlaps the stage's matrix work.
+  int32_t win_lo = 0;
+  const int32_t n_blk = ((kv_end - 1) >> bsh) + 1;
+  auto fill_window = [&](int32_t first_block) {
+    win_lo = first_block;
+    const int32_t n = min(kBlockWindow, n_blk - first_block);
+    for (int32_t i = tid; i < n; i += 256) sBlk[i] = btab[first_block + i];
+  };
+  auto window_covers = [&](int32_t kt) {
+    const int32_t b0 = (kt * kChunkKeys) >> bsh;
+    const int32_t b1 = (min(kt * kChunkKeys + kChunkKeys, kv_end) - 1) >> bsh;
+    return b0 >= win_lo && b1 < win_lo + kBlockWindow;
+  };
+  const int32_t k_last = kv_end - 1;
+  const int64_t head_bytes = static_cast<int64_t>(g) * ((int64_t)ROW << bsh);
+  const int64_t blk_bytes = static_cast<int64_t>(a.Hkv) * ((int64_t)ROW << bsh);
+  const int cp_row = lane / (ROW / 16), cp_pos = lane % (ROW / 16);
+  auto issue = [&](int32_t kt) {
     const int32_t k0 = kt * kChunkKeys;
 #pragma unroll
-    for (int i = 0; i < KLOADS; ++i) {
-      const int cid = tid + 256 * i;
-      const int32_t key = k0 + cid / DC;
-      if (key < kv_end) {
-        const T* kp = kc + ((static_cast<int64_t>(btab[key / bs]) * a.Hkv + g) * bs + key % bs) * D;
-        kreg[i].load(kp + 8 * (cid % DC));
-      } else {
-        kreg[i].zero();
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < VLOADS; ++i) {
-      const int pid = tid + 256 * i;
-      const int quad = pid / DC, ch = pid % DC;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int32_t key = k0 + 4 * quad + e;
-        if (pid < VPAIRS && key < kv_end) {
-          const T* vp = vc + ((static_cast<int64_t>(btab[key / bs]) * a.Hkv + g) * bs + key % bs) * D;
-          vreg[i][e].load(vp + 8 * ch);
-        } else {
-          vreg[i][e].zero();
-        }
-      }
-    }
-  };
-  auto lstore = [&]() {
-#pragma unroll
-    for (int i = 0; i < KLOADS; ++i) {
-      const int cid = tid + 256 * i;
-      kreg[i].store(&sK[cid / DC][8 * (cid % DC)]);
-    }
-#pragma unroll
-    for (int i = 0; i < VLOADS; ++i) {
-      const int pid = tid + 256 * i;
-      if (pid >= VPAIRS) continue;
-      const int quad = pid / DC, ch = pid % DC;
-      // key 16 u + k goes to column 16 u + sigma(k), sigma swapping the middle two 4-key quads
-      const int qq = quad & 3;
-      const int slot0 = 16 * (quad >> 2) + 4 * (qq == 1 ? 2 : (qq == 2 ? 1 : qq));
-#pragma unroll
-      for (int dd = 0; dd < 8; ++dd) {
-        T* dst = &sVt[8 * ch + dd][slot0];
-        if constexpr (sizeof(T) == 2) {
-          const uint32_t* w0 = &vreg[i][0].u.x;
-          const uint32_t* w1 = &vreg[i][1].u.x;
-          const uint32_t* w2 = &vreg[i][2].u.x;
-          const uint32_t* w3 = &vreg[i][3].u.x;
-          const int sh = 16 * (dd & 1);
-          const uint32_t lo = ((w0[dd >> 1] >> sh) & 0xffffu) | (((w1[dd >> 1] >> sh) & 0xffffu) << 16);
-          const uint32_t hi = ((w2[dd >> 1] >> sh) & 0xffffu) | (((w3[dd >> 1] >> sh) & 0xffffu) << 16);
-          *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
-        } else {
-          *reinterpret_cast<float4*>(dst) =
-              make_float4(vreg[i][0].get(dd), vreg[i][1].get(dd), vreg[i][2].get(dd), vreg[i][3].get(dd));
-        }
-      }
+    for (int j = 0; j < NCPW; ++j) {
+      const int i = wave * NCPW + j;
+      const int r = i * RPI + cp_row;
+      const int32_t key = min(k0 + r, k_last);
+      const int64_t off = static_cast<int64_t>(sBlk[(key >> bsh) - win_lo]) * blk_bytes + head_bytes +
+                          static_cast<int64_t>(key & bmask) * ROW + 16 * lds_chunk(cp_pos, r, ROW);
+      lds_copy16(kc + off, sK + i * 1024);
+      lds_copy16(vc + off, sV + i * 1024);
     }
   };
 
-  if (kt_lo < kt_hi) gload(kt_lo);
+  if (kt_lo < kt_hi) {
+    fill_window((kt_lo * kChunkKeys) >> bsh);
+    __syncthreads();
+    issue(kt_lo);
+  }
   for (int32_t kt = kt_lo; kt < kt_hi; ++kt) {
-    __syncthreads();
-    lstore();
-    __syncthreads();
-    if (kt + 1 < kt_hi) gload(kt + 1);
+    lds_copies_done();
+    __syncthreads();                          // every wave's copy of this stage has landed
+    Frag<T> kf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) kf[ks] = lds_row_frag<T>(sK, col, 16 * ks + 8 * half, ROW);
+    Frag<T> vt[2][MT];
+#pragma unroll
+    for (int ps = 0; ps < 2; ++ps)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) vt[ps][mt] = lds_vt_frag32<T>(sV, mt, ps, lane, ROW);
+    lds_reads_done();
+    __syncthreads();                          // every wave has read the stage
+    if (kt + 1 < kt_hi) {
+      if (!window_covers(kt + 1)) {
+        fill_window(((kt + 1) * kChunkKeys) >> bsh);
+        __syncthreads();
+      }
+      issue(kt + 1);
+    }
+
     const int32_t k0 = kt * kChunkKeys;
     const bool need_mask = k0 + kChunkKeys - 1 > c + qb * a.bmq;   // some key may pass a row
-
-    f32x16 st[2];
+    f32x16 st = f32x16{};
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      st[h] = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        Frag<T> kf;
-        kf.load(&sK[32 * h + col][16 * ks + 8 * half]);
-        mma32_k16(st[h], kf, qf[ks]);
-      }
-    }
+    for (int ks = 0; ks < KS; ++ks) mma32_k16(st, kf[ks], qf[ks]);
     float mx = kNegInf;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = st[h][r] * a.scale_log2;
-        if (need_mask) {
-          const int32_t key = k0 + 32 * h + acc32_row(lane, r);
-          if (key > qpos) x = kNegInf;
-        }
-        st[h][r] = x;
-        mx = fmaxf(mx, x);
-      }
+    for (int r = 0; r < 16; ++r) {
+      float x = st[r] * a.scale_log2;
+      if (need_mask && k0 + acc32_row(lane, r) > qpos) x = kNegInf;
+      st[r] = x;
+      mx = fmaxf(mx, x);
     }
     mx = wave_xor_max(mx, 32);
     const float m_new = fmaxf(m_run, mx);
@@ -441,31 +518,24 @@ __global__ __launch_bounds__(256) void chunk_kernel(AttnArgs a, int32_t n_tiles,
     const float alpha = exp2f(m_run - m_use);
     float psum = 0.f;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float e = exp2f(st[h][r] - m_use);
-        st[h][r] = e;
-        psum += e;
-      }
+    for (int r = 0; r < 16; ++r) {
+      const float e = exp2f(st[r] - m_use);
+      st[r] = e;
+      psum += e;
     }
     l_run = l_run * alpha + psum;
     m_run = m_new;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) o[mt] *= alpha;
 #pragma unroll
-    for (int ps = 0; ps < 4; ++ps) {          // 16-key contraction steps
+    for (int ps = 0; ps < 2; ++ps) {          // 16-key contraction steps
       float pv[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) pv[j] = st[ps >> 1][8 * (ps & 1) + j];
+      for (int j = 0; j < 8; ++j) pv[j] = st[8 * ps + j];
       Frag<T> pf;
       pf.set_all(pv);
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        Frag<T> vt;
-        vt.load(&sVt[32 * mt + col][16 * ps + 8 * half]);
-        mma32_k16(o[mt], vt, pf);
-      }
+      for (int mt = 0; mt < MT; ++mt) mma32_k16(o[mt], vt[ps][mt], pf);
     }
   }
 
@@ -617,7 +687,9 @@ extern "C" int cb_mixed_paged_attention_timed(
   if (dtype != CB_F32 && dtype != CB_BF16) return CB_ERR_INVALID;
   if (!valid_shape(num_seqs, num_decodes, T, max_q_len, max_decode_ctx, max_ctx, Hq, Hkv, D))
     return CB_ERR_INVALID;
-  if (block_size < 1 || !(scale > 0.f)) return CB_ERR_INVALID;
+  if (block_size < kMinBlock || block_size > kMaxBlock || (block_size & (block_size - 1)) ||
+      !(scale > 0.f))
+    return CB_ERR_INVALID;
   if (num_seqs == 0) return CB_OK;
   if (!q || !k_cache || !v_cache || !cu_seqlens_q || !context_lens || !cu_blocks || !block_table || !out)
     return CB_ERR_INVALID;
@@ -639,6 +711,7 @@ extern "C" int cb_mixed_paged_attention_timed(
   a.chk_ml = reinterpret_cast<float*>(ws + p.chk_ml);
   a.num_seqs = num_seqs; a.nd = num_decodes; a.T = T; a.Hq = Hq; a.Hkv = Hkv; a.G = p.G;
   a.bs = block_size;
+  a.bs_shift = __builtin_ctz(static_cast<unsigned>(block_size));
   a.part = p.part; a.max_parts = std::max(p.max_parts, 1); a.head_blocks = p.head_blocks;
   a.bmq = p.bmq; a.q_blocks = p.q_blocks; a.n_chunk = p.n_chunk; a.nsplit = p.nsplit;
   a.scale_log2 = scale * 1.4426950408889634f;
