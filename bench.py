@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-step", type=int, default=8)
     ap.add_argument("--json-out", default=None)
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="run one device copy of this many MiB before timing (a known-size kernel "
+                         "for scaling profiler byte counters)")
     return ap.parse_args()
 
 
@@ -165,14 +168,21 @@ def main():
             state["sched"] = cb.cb_sched_clone(snapshot)
         return meta.num_tokens, k
 
+    if args.calib_copy_mib:
+        src = torch.ones(args.calib_copy_mib << 19, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         one_step()
     torch.cuda.synchronize()
 
     # Per-step phase events (created and touched once so the runtime objects exist).
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    for e4 in evs:
-        for e in e4:
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    for e6 in evs:
+        for e in e6:
             e.record()
     torch.cuda.synchronize()
 
@@ -188,10 +198,10 @@ def main():
     el = time.perf_counter() - t0
 
     dec_ms, chk_ms, cmb_ms = [], [], []
-    for e4 in evs:
-        dec_ms.append(e4[0].elapsed_time(e4[1]))
-        chk_ms.append(e4[1].elapsed_time(e4[2]))
-        cmb_ms.append(e4[2].elapsed_time(e4[3]))
+    for e6 in evs:
+        dec_ms.append(e6[0].elapsed_time(e6[1]))
+        chk_ms.append(e6[2].elapsed_time(e6[3]))
+        cmb_ms.append(e6[4].elapsed_time(e6[5]))
     elt = 2
     dbytes = [decode_bytes(metas[k], w, elt) for k in step_ids]
     cflops = [chunk_flops(metas[k], w) for k in step_ids]

@@ -15,7 +15,8 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libcb.so")
+# The in-tree build; CB_LIBCB_PATH names another build of the same library (e.g. a tuning variant).
+LIB_PATH = os.environ.get("CB_LIBCB_PATH") or os.path.join(_PKG, "libcb.so")
 
 CB_OK, CB_ERR_INVALID, CB_ERR_DECODE_OVER_BUDGET, CB_ERR_OUT_OF_BLOCKS, CB_ERR_CAPACITY, CB_ERR_HIP = (
     0, -1, -2, -3, -4, -5)
@@ -284,5 +285,7 @@ def cb_mixed_paged_attention(q, k_cache, v_cache, cu_seqlens_q, context_lens, cu
     if events is None:
         _check(_lib().cb_mixed_paged_attention(*args), "cb_mixed_paged_attention")
     else:
-        ev = (_vp * 4)(*[ctypes.c_void_p(e.cuda_event) if e is not None else None for e in events])
+        if len(events) != 6:
+            raise ValueError("events: six torch.cuda.Event (or None) entries")
+        ev = (_vp * 6)(*[ctypes.c_void_p(e.cuda_event) if e is not None else None for e in events])
         _check(_lib().cb_mixed_paged_attention_timed(*args, ev), "cb_mixed_paged_attention_timed")

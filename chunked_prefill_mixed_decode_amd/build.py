@@ -28,20 +28,20 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the HIP toolchain (ROCm) is required to build libcb.so")
 
 
-def command(out: str = LIB) -> list[str]:
+def command(out: str = LIB, defines=()) -> list[str]:
     return [
         hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-Wall", "-Wno-unused-result",
-        f"-I{INCLUDE}", f"-I{CSRC}",
+        f"-I{INCLUDE}", f"-I{CSRC}", *[f"-D{d}" for d in defines],
         *[os.path.join(CSRC, s) for s in SOURCES],
         "-o", out,
     ]
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = command(tmp)
+def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
+    tmp = out + ".tmp"
+    cmd = command(tmp, defines)
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -50,8 +50,8 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed with status {res.returncode}")
     if verbose and res.stderr.strip():
         sys.stderr.write(res.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -21,12 +21,24 @@
 //   combine_kernel log-sum-exp merge of the partials of each (row, head) into out.
 // Softmax runs in base 2 with scale * log2(e) folded into the scores.
 #include <algorithm>
+#include <mutex>
 
 #include "cb.h"
 #include "common.h"
 
 namespace cb {
 namespace {
+
+// Tuning constants (compile-time; the defaults are the measured choices on MI355X).
+#ifndef CB_DECODE_TARGET_PARTS
+#define CB_DECODE_TARGET_PARTS 16     // aim for about this many key partitions per longest decode
+#endif
+#ifndef CB_DECODE_MIN_PART
+#define CB_DECODE_MIN_PART 256        // smallest decode key partition
+#endif
+#ifndef CB_CHUNK_MIN_TILES
+#define CB_CHUNK_MIN_TILES 512        // split chunk keys until at least this many tiles
+#endif
 
 constexpr int kChunkRows = 128;   // rows per chunk tile: 4 waves x 32
 constexpr int kChunkKeys = 32;    // keys per LDS stage of a chunk tile
@@ -53,8 +65,9 @@ Plan make_plan(int32_t num_seqs, int32_t nd, int32_t T, int32_t max_q_len, int32
   Plan p;
   p.G = Hq / Hkv;
   p.head_blocks = (p.G + 15) / 16;
+  p.part = CB_DECODE_MIN_PART;
   if (nd > 0) {
-    const int32_t want = (std::max(max_dctx, 1) + 15) / 16;   // ~16 partitions per longest row
+    const int32_t want = (std::max(max_dctx, 1) + CB_DECODE_TARGET_PARTS - 1) / CB_DECODE_TARGET_PARTS;
     while (p.part < want && p.part < kMaxPart) p.part *= 2;
     p.max_parts = (std::max(max_dctx, 1) + p.part - 1) / p.part;
   }
@@ -63,7 +76,7 @@ Plan make_plan(int32_t num_seqs, int32_t nd, int32_t T, int32_t max_q_len, int32
   if (p.n_chunk > 0) {
     p.q_blocks = (std::max(max_q_len, 1) + p.bmq - 1) / p.bmq;
     const int64_t tiles = static_cast<int64_t>(p.n_chunk) * p.q_blocks * Hkv;
-    while (p.nsplit < kMaxSplit && tiles * p.nsplit < 512 &&
+    while (p.nsplit < kMaxSplit && tiles * p.nsplit < CB_CHUNK_MIN_TILES &&
            max_ctx / (2 * p.nsplit) >= 2 * kChunkKeys)
       p.nsplit *= 2;
   }
@@ -591,64 +604,121 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a, int32_t n_dec_
     po = a.chk_o + base * D;
     pml = a.chk_ml + base * 2;
   }
+  // Lanes read the partials' (m, l) pairs side by side; butterfly reductions give every lane the
+  // same maximum and total in the same order on every run.
   float m = kNegInf;
-  for (int32_t i = 0; i < P; ++i) m = fmaxf(m, pml[2 * i]);
+  for (int32_t i = lane; i < P; i += 64) m = fmaxf(m, pml[2 * i]);
+#pragma unroll
+  for (int x = 32; x >= 1; x >>= 1) m = wave_xor_max(m, x);
   const float m_use = m == kNegInf ? 0.f : m;
   float L = 0.f;
+  for (int32_t i = lane; i < P; i += 64) L += exp2f(pml[2 * i] - m_use) * pml[2 * i + 1];
+#pragma unroll
+  for (int x = 32; x >= 1; x >>= 1) L = wave_xor_sum(L, x);
+  const float inv = L > 0.f ? 1.f / L : 0.f;
   float acc[PER];
 #pragma unroll
   for (int j = 0; j < PER; ++j) acc[j] = 0.f;
-  for (int32_t i = 0; i < P; ++i) {
-    const float wgt = exp2f(pml[2 * i] - m_use);
-    L += wgt * pml[2 * i + 1];
+  for (int32_t base = 0; base < P; base += 64) {
+    const int32_t i = base + lane;
+    const float wl = i < P ? exp2f(pml[2 * i] - m_use) * inv : 0.f;
+    const int32_t n = min(64, P - base);
+    for (int32_t k = 0; k < n; ++k) {
+      const float wk = __shfl(wl, k, 64);
+      const float* pk = po + static_cast<int64_t>(base + k) * D + lane;
 #pragma unroll
-    for (int j = 0; j < PER; ++j) acc[j] += wgt * po[static_cast<int64_t>(i) * D + lane + 64 * j];
+      for (int j = 0; j < PER; ++j) acc[j] += wk * pk[64 * j];
+    }
   }
-  const float inv = L > 0.f ? 1.f / L : 0.f;
   T* orow = static_cast<T*>(a.out) + (static_cast<int64_t>(row) * a.Hq + h) * D;
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
-    const float x = acc[j] * inv;
     if constexpr (sizeof(T) == 2) {
-      reinterpret_cast<uint16_t*>(orow)[lane + 64 * j] = f32_to_bf16_bits(x);
+      reinterpret_cast<uint16_t*>(orow)[lane + 64 * j] = f32_to_bf16_bits(acc[j]);
     } else {
-      orow[lane + 64 * j] = x;
+      orow[lane + 64 * j] = acc[j];
     }
   }
 }
 
+// Per-device side stream and fork/join events: the chunk tiles (matrix-core bound) run on the
+// side stream while the decode split (HBM bound) runs on the caller's stream; the combine waits
+// for both.  Created on first use, default priority, kept until the process ends.  The mutex
+// makes the record/wait/launch sequence of one call atomic with respect to other host threads.
+struct SideStream {
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+constexpr int kMaxDevices = 64;
+SideStream g_side[kMaxDevices];
+std::mutex g_side_mutex;
+
+int side_stream(SideStream** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return CB_ERR_HIP;
+  SideStream& ss = g_side[dev];
+  if (!ss.stream) {
+    if (hipStreamCreateWithFlags(&ss.stream, hipStreamNonBlocking) != hipSuccess) return CB_ERR_HIP;
+    if (hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess) return CB_ERR_HIP;
+    if (hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess) return CB_ERR_HIP;
+  }
+  *out = &ss;
+  return CB_OK;
+}
+
 template <typename T, int D>
 int launch_all(hipStream_t st, const AttnArgs& a, const Plan& p, void* const* events) {
-  auto rec = [&](int i) {
-    if (events && events[i]) (void)hipEventRecord(static_cast<hipEvent_t>(events[i]), st);
+  auto rec = [&](int i, hipStream_t on) {
+    if (events && events[i]) (void)hipEventRecord(static_cast<hipEvent_t>(events[i]), on);
   };
-  rec(0);
+  const bool both = a.nd > 0 && a.n_chunk > 0;
+  std::unique_lock<std::mutex> lock(g_side_mutex, std::defer_lock);
+  SideStream* ss = nullptr;
+  hipStream_t cst = st;                       // stream of the chunk kernel
+  if (both) {
+    lock.lock();
+    const int rc = side_stream(&ss);
+    if (rc != CB_OK) return rc;
+    cst = ss->stream;
+    if (hipEventRecord(ss->fork, st) != hipSuccess) return CB_ERR_HIP;
+    if (hipStreamWaitEvent(cst, ss->fork, 0) != hipSuccess) return CB_ERR_HIP;
+  }
+  // Decode first: it takes every CU; chunk tiles fill the slots its waves leave, mostly in its
+  // tail, instead of taking LDS away from it at the start.
   if (a.nd > 0) {
     const int64_t grid = static_cast<int64_t>(a.nd) * a.Hkv * a.head_blocks * a.max_parts;
     if (grid > 0x7fffffff) return CB_ERR_INVALID;
+    rec(0, st);
     decode_kernel<T, D><<<dim3(static_cast<uint32_t>(grid)), dim3(64), 0, st>>>(a);
     if (hipGetLastError() != hipSuccess) return CB_ERR_HIP;
+    rec(1, st);
   }
-  rec(1);
   if (a.n_chunk > 0) {
     const int64_t n_tiles = static_cast<int64_t>(a.n_chunk) * a.q_blocks * a.Hkv * a.nsplit;
     const int64_t per_xcd = (n_tiles + 7) / 8;
     if (per_xcd * 8 > 0x7fffffff) return CB_ERR_INVALID;
-    chunk_kernel<T, D><<<dim3(static_cast<uint32_t>(per_xcd * 8)), dim3(256), 0, st>>>(
+    rec(2, cst);
+    chunk_kernel<T, D><<<dim3(static_cast<uint32_t>(per_xcd * 8)), dim3(256), 0, cst>>>(
         a, static_cast<int32_t>(n_tiles), static_cast<int32_t>(per_xcd));
     if (hipGetLastError() != hipSuccess) return CB_ERR_HIP;
+    rec(3, cst);
   }
-  rec(2);
+  if (both) {
+    if (hipEventRecord(ss->join, cst) != hipSuccess) return CB_ERR_HIP;
+    if (hipStreamWaitEvent(st, ss->join, 0) != hipSuccess) return CB_ERR_HIP;
+    lock.unlock();
+  }
   const int32_t n_chunk_rows = a.nsplit > 1 ? a.T - a.nd : 0;
   const int64_t items = static_cast<int64_t>(a.nd + n_chunk_rows) * a.Hq;
   if (items > 0) {
     const int64_t grid = (items + 3) / 4;
     if (grid > 0x7fffffff) return CB_ERR_INVALID;
+    rec(4, st);
     combine_kernel<T, D><<<dim3(static_cast<uint32_t>(grid)), dim3(256), 0, st>>>(
         a, a.nd, static_cast<int32_t>(items));
     if (hipGetLastError() != hipSuccess) return CB_ERR_HIP;
+    rec(5, st);
   }
-  rec(3);
   return CB_OK;
 }
 
