@@ -63,6 +63,59 @@ def chunk_flops(meta, w) -> int:
     return int((pos + 1).sum()) * 4 * w.D * w.Hq
 
 
+def committed_traffic(kernel: str):
+    """HBM bytes per launch of ``kernel`` from the committed counter summary, or None when the
+    attention source has changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "hbm_traffic_b512_7b_layer.json")
+    src = os.path.join(ROOT, "chunked_prefill_mixed_decode_amd", "csrc", "attention.hip")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+        with open(src, "rb") as f:
+            h = hashlib.sha256(f.read()).hexdigest()[:16]
+    except OSError:
+        return None
+    if rec.get("source_sha256_16") != h:
+        return None
+    return rec["kernels"][kernel]["traffic_bytes"]
+
+
+def isolation_pass(g, metas, qrots, outs, w, reps: int):
+    """Decode-only and chunk-only launches of each step's metadata, timed with HIP events on the
+    launch stream: per-kernel durations without the other kernel running beside it."""
+    import torch
+    cb = g.cb
+    dec, chk = [], []
+    for k, meta in enumerate(metas):
+        nd, T = meta.num_decodes, meta.num_tokens
+        h = meta.host
+        dev = {kk: vv.to(g.device) for kk, vv in h.items()}
+        cu_chunk = (dev["cu_seqlens_q"][nd:] - nd).contiguous()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+        for e in ev:
+            e.record()
+        for _ in range(reps):
+            cb.cb_mixed_paged_attention(
+                qrots[k][:nd], g.runner.k_cache, g.runner.v_cache, dev["cu_seqlens_q"],
+                dev["context_lens"], dev["cu_blocks"], dev["block_table"], outs[k][:nd],
+                g.runner.workspace, num_seqs=nd, num_decodes=nd, max_q_len=1,
+                max_decode_ctx=meta.max_decode_context_len, max_ctx=meta.max_decode_context_len,
+                scale=g.runner.scale, events=[ev[0], ev[1], None, None, None, None])
+            torch.cuda.synchronize()
+            dec.append((k, ev[0].elapsed_time(ev[1])))
+            if T > nd:
+                cb.cb_mixed_paged_attention(
+                    qrots[k][nd:], g.runner.k_cache, g.runner.v_cache, cu_chunk,
+                    dev["context_lens"][nd:], dev["cu_blocks"][nd:], dev["block_table"], outs[k][nd:],
+                    g.runner.workspace, num_seqs=meta.num_seqs - nd, num_decodes=0,
+                    max_q_len=meta.max_q_len, max_decode_ctx=0, max_ctx=meta.max_context_len,
+                    scale=g.runner.scale, events=[None, None, ev[2], ev[3], None, None])
+                torch.cuda.synchronize()
+                chk.append((k, ev[2].elapsed_time(ev[3])))
+    return dec, chk
+
+
 def cpu_baseline(w, step_index: int):
     """The oracle on one step: Python reference builder up to that step, then fp64 attention
     (rotary embedding included) of all the step's rows.  Raw inputs are generated beforehand."""
@@ -207,7 +260,13 @@ def main():
     cflops = [chunk_flops(metas[k], w) for k in step_ids]
     dec_avg_s = sum(dec_ms) / len(dec_ms) / 1e3
     achieved = sum(dbytes) / len(dbytes) / dec_avg_s / 1e9
-    chunk_tflops = sum(cflops) / (sum(chk_ms) / 1e3) / 1e12
+
+    iso_dec, iso_chk = isolation_pass(g, metas, qrots, outs, w, reps=3)
+    iso_dec_s = sum(t for _, t in iso_dec) / 1e3
+    iso_chk_s = sum(t for _, t in iso_chk) / 1e3
+    iso_bytes = sum(decode_bytes(metas[k], w, elt) for k, _ in iso_dec)
+    iso_flops = sum(chunk_flops(metas[k], w) for k, _ in iso_chk)
+    traffic = committed_traffic("decode_kernel")
 
     res = {
         "metric": METRIC,
@@ -228,14 +287,18 @@ def main():
                    "steps_per_cycle": cb_steps, "parallelism": "1 GPU"},
         "roofline": {"bound": "hbm", "kernel": "decode_kernel (split-context decode rows)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "bytes_per_launch": sum(dbytes) / len(dbytes), "avg_launch_us": dec_avg_s * 1e6},
-        "chunk_tiles": {"bound": "mfma", "achieved": chunk_tflops, "peak": MFMA_BF16_PEAK_TFLOPS,
-                        "unit": "TFLOP/s", "frac": chunk_tflops / MFMA_BF16_PEAK_TFLOPS,
-                        "avg_launch_us": sum(chk_ms) / len(chk_ms) * 1e3,
+        "chunk_tiles": {"bound": "mfma", "overlapped_avg_launch_us": sum(chk_ms) / len(chk_ms) * 1e3,
                         "flops_per_step": sum(cflops) / len(cflops)},
+        "isolated": {"decode_avg_us": iso_dec_s / len(iso_dec) * 1e6,
+                     "decode_GBps": iso_bytes / iso_dec_s / 1e9,
+                     "decode_frac_hbm": iso_bytes / iso_dec_s / 1e9 / HBM_PEAK_GBS,
+                     "chunk_avg_us": iso_chk_s / max(1, len(iso_chk)) * 1e6,
+                     "chunk_TFLOPs": iso_flops / max(iso_chk_s, 1e-12) / 1e12,
+                     "chunk_frac_mfma": iso_flops / max(iso_chk_s, 1e-12) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                     "note": "decode-only and chunk-only launches of the same step metadata, 3 reps per step"},
         "combine_avg_us": sum(cmb_ms) / len(cmb_ms) * 1e3,
-        "device_step_ms": None,
     }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)...", file=sys.stderr, flush=True)
