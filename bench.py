@@ -208,13 +208,17 @@ def main():
 
     state = {"sched": cb.cb_sched_clone(snapshot), "k": 0}
 
-    def one_step(events=None):
+    def one_step(events=None, bracket=None):
         k = state["k"]
         meta = g.runner.build(state["sched"], w.budget)
+        if bracket is not None:
+            bracket[0].record()
         dev_meta = g.runner.upload(meta)
         q, kk, vv = inputs[k]
         g.runner.append(dev_meta, q, kk, vv, qrots[k])
         g.runner.attend(meta, dev_meta, qrots[k], outs[k], events=events)
+        if bracket is not None:
+            bracket[1].record()
         state["k"] = k + 1
         if state["k"] == cb_steps:
             state["k"] = 0
@@ -233,7 +237,7 @@ def main():
     torch.cuda.synchronize()
 
     # Per-step phase events (created and touched once so the runtime objects exist).
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(args.steps)]
     for e6 in evs:
         for e in e6:
             e.record()
@@ -244,12 +248,13 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        n, k = one_step(evs[i])
+        n, k = one_step(evs[i][:6], evs[i][6:])
         tokens += n
         step_ids.append(k)
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
 
+    dev_step_ms = [e8[6].elapsed_time(e8[7]) for e8 in evs]
     dec_ms, chk_ms, cmb_ms = [], [], []
     for e6 in evs:
         dec_ms.append(e6[0].elapsed_time(e6[1]))
@@ -299,6 +304,7 @@ def main():
                      "chunk_frac_mfma": iso_flops / max(iso_chk_s, 1e-12) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
                      "note": "decode-only and chunk-only launches of the same step metadata, 3 reps per step"},
         "combine_avg_us": sum(cmb_ms) / len(cmb_ms) * 1e3,
+        "device_step_us": sum(dev_step_ms) / len(dev_step_ms) * 1e3,
     }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)...", file=sys.stderr, flush=True)

@@ -21,7 +21,6 @@
 //   combine_kernel log-sum-exp merge of the partials of each (row, head) into out.
 // Softmax runs in base 2 with scale * log2(e) folded into the scores.
 #include <algorithm>
-#include <mutex>
 
 #include "cb.h"
 #include "common.h"
@@ -623,7 +622,21 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a, int32_t n_dec_
     const int32_t i = base + lane;
     const float wl = i < P ? exp2f(pml[2 * i] - m_use) * inv : 0.f;
     const int32_t n = min(64, P - base);
-    for (int32_t k = 0; k < n; ++k) {
+    int32_t k = 0;
+    for (; k + 8 <= n; k += 8) {              // eight partials' loads in flight together
+      float x[8][PER];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int j = 0; j < PER; ++j) x[u][j] = po[static_cast<int64_t>(base + k + u) * D + lane + 64 * j];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float wk = __shfl(wl, k + u, 64);
+#pragma unroll
+        for (int j = 0; j < PER; ++j) acc[j] += wk * x[u][j];
+      }
+    }
+    for (; k < n; ++k) {
       const float wk = __shfl(wl, k, 64);
       const float* pk = po + static_cast<int64_t>(base + k) * D + lane;
 #pragma unroll
@@ -641,83 +654,42 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a, int32_t n_dec_
   }
 }
 
-// Per-device side stream and fork/join events: the chunk tiles (matrix-core bound) run on the
-// side stream while the decode split (HBM bound) runs on the caller's stream; the combine waits
-// for both.  Created on first use, default priority, kept until the process ends.  The mutex
-// makes the record/wait/launch sequence of one call atomic with respect to other host threads.
-struct SideStream {
-  hipStream_t stream = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
-};
-constexpr int kMaxDevices = 64;
-SideStream g_side[kMaxDevices];
-std::mutex g_side_mutex;
-
-int side_stream(SideStream** out) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return CB_ERR_HIP;
-  SideStream& ss = g_side[dev];
-  if (!ss.stream) {
-    if (hipStreamCreateWithFlags(&ss.stream, hipStreamNonBlocking) != hipSuccess) return CB_ERR_HIP;
-    if (hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess) return CB_ERR_HIP;
-    if (hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess) return CB_ERR_HIP;
-  }
-  *out = &ss;
-  return CB_OK;
-}
-
+// Decode split, chunk tiles and combine in order on the caller's stream.  (Running the chunk
+// kernel on a second stream beside the decode split was measured slower: the cross-queue join
+// before the combine cost more than the overlap saved.)
 template <typename T, int D>
 int launch_all(hipStream_t st, const AttnArgs& a, const Plan& p, void* const* events) {
-  auto rec = [&](int i, hipStream_t on) {
-    if (events && events[i]) (void)hipEventRecord(static_cast<hipEvent_t>(events[i]), on);
+  auto rec = [&](int i) {
+    if (events && events[i]) (void)hipEventRecord(static_cast<hipEvent_t>(events[i]), st);
   };
-  const bool both = a.nd > 0 && a.n_chunk > 0;
-  std::unique_lock<std::mutex> lock(g_side_mutex, std::defer_lock);
-  SideStream* ss = nullptr;
-  hipStream_t cst = st;                       // stream of the chunk kernel
-  if (both) {
-    lock.lock();
-    const int rc = side_stream(&ss);
-    if (rc != CB_OK) return rc;
-    cst = ss->stream;
-    if (hipEventRecord(ss->fork, st) != hipSuccess) return CB_ERR_HIP;
-    if (hipStreamWaitEvent(cst, ss->fork, 0) != hipSuccess) return CB_ERR_HIP;
-  }
-  // Decode first: it takes every CU; chunk tiles fill the slots its waves leave, mostly in its
-  // tail, instead of taking LDS away from it at the start.
   if (a.nd > 0) {
     const int64_t grid = static_cast<int64_t>(a.nd) * a.Hkv * a.head_blocks * a.max_parts;
     if (grid > 0x7fffffff) return CB_ERR_INVALID;
-    rec(0, st);
+    rec(0);
     decode_kernel<T, D><<<dim3(static_cast<uint32_t>(grid)), dim3(64), 0, st>>>(a);
     if (hipGetLastError() != hipSuccess) return CB_ERR_HIP;
-    rec(1, st);
+    rec(1);
   }
   if (a.n_chunk > 0) {
     const int64_t n_tiles = static_cast<int64_t>(a.n_chunk) * a.q_blocks * a.Hkv * a.nsplit;
     const int64_t per_xcd = (n_tiles + 7) / 8;
     if (per_xcd * 8 > 0x7fffffff) return CB_ERR_INVALID;
-    rec(2, cst);
-    chunk_kernel<T, D><<<dim3(static_cast<uint32_t>(per_xcd * 8)), dim3(256), 0, cst>>>(
+    rec(2);
+    chunk_kernel<T, D><<<dim3(static_cast<uint32_t>(per_xcd * 8)), dim3(256), 0, st>>>(
         a, static_cast<int32_t>(n_tiles), static_cast<int32_t>(per_xcd));
     if (hipGetLastError() != hipSuccess) return CB_ERR_HIP;
-    rec(3, cst);
-  }
-  if (both) {
-    if (hipEventRecord(ss->join, cst) != hipSuccess) return CB_ERR_HIP;
-    if (hipStreamWaitEvent(st, ss->join, 0) != hipSuccess) return CB_ERR_HIP;
-    lock.unlock();
+    rec(3);
   }
   const int32_t n_chunk_rows = a.nsplit > 1 ? a.T - a.nd : 0;
   const int64_t items = static_cast<int64_t>(a.nd + n_chunk_rows) * a.Hq;
   if (items > 0) {
     const int64_t grid = (items + 3) / 4;
     if (grid > 0x7fffffff) return CB_ERR_INVALID;
-    rec(4, st);
+    rec(4);
     combine_kernel<T, D><<<dim3(static_cast<uint32_t>(grid)), dim3(256), 0, st>>>(
         a, a.nd, static_cast<int32_t>(items));
     if (hipGetLastError() != hipSuccess) return CB_ERR_HIP;
-    rec(5, st);
+    rec(5);
   }
   return CB_OK;
 }

@@ -182,8 +182,7 @@ int cb_rope_kv_append(void* stream, int32_t dtype, int32_t T, int32_t Hq, int32_
  * workspace: device memory of at least cb_attn_workspace_bytes(...) bytes for the same
  * arguments (float32 partial results of split-context work), 256-byte aligned; CB_ERR_CAPACITY
  * if workspace_bytes is smaller.  Calls that share a workspace must not overlap in time.
- * Execution: decode split and chunk tiles run concurrently (the chunk kernel on a library-owned
- * side stream of the device, joined back before the combine); see the _timed variant.
+ * Execution: three kernels in order on the stream (decode split, chunk tiles, combine).
  * Layouts (device): q, out [T, Hq, D]; caches as above; cu_seqlens_q, cu_blocks [num_seqs + 1];
  * context_lens [num_seqs]; block_table [cu_blocks[num_seqs]].  out must not overlap q.
  * ------------------------------------------------------------------------------------------- */
@@ -200,14 +199,10 @@ int cb_mixed_paged_attention(void* stream, int32_t dtype, int32_t num_seqs, int3
                              const int32_t* cu_blocks, const int32_t* block_table, void* out,
                              void* workspace, size_t workspace_bytes);
 
-/* The same operation, recording caller-created HIP events (hipEvent_t, passed as void*) around
- * its kernels for timing, each on the stream that kernel runs on: events[0] / events[1] before /
- * after the decode kernel (caller's stream), events[2] / events[3] before / after the chunk
- * kernel, events[4] / events[5] before / after the combine kernel (caller's stream).  When a
- * step has both decode rows and chunks, the chunk kernel runs on a library-owned stream of the
- * current device (default priority, created on first use), forked from and joined back into the
- * caller's stream with events, so that it overlaps the decode kernel; otherwise everything runs
- * on the caller's stream.  events may be NULL and any entry may be NULL. */
+/* The same operation, recording caller-created HIP events (hipEvent_t, passed as void*) on the
+ * stream around its kernels for timing: events[0] / events[1] before / after the decode kernel,
+ * events[2] / events[3] before / after the chunk kernel, events[4] / events[5] before / after
+ * the combine kernel.  events may be NULL and any entry may be NULL. */
 int cb_mixed_paged_attention_timed(void* stream, int32_t dtype, int32_t num_seqs,
                                    int32_t num_decodes, int32_t T, int32_t max_q_len,
                                    int32_t max_decode_ctx, int32_t max_ctx, int32_t Hq,
