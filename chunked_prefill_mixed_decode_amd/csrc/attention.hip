@@ -7,19 +7,22 @@
 // ("Two kernels with different limiting resources"): decode rows stream the whole cache and are
 // bandwidth-bound, chunk rows are dense matrix work and compute-bound.
 //
-// Three kernels on the caller's stream:
-//   decode_kernel  rows [0, nd): one wave per (decode, KV head, 16-head block, key partition).
-//                  S^T = K Q^T on 16x16x32 MFMA with K loaded from HBM straight into operand
-//                  registers; online softmax in the lane that owns the head; O^T += V^T P^T with
-//                  V transposed through LDS.  Writes float32 partials (m, l, unnormalised o).
+// Four kernels on the caller's stream:
+//   decode_prep_kernel  one workgroup: the decode work list (row, key partition).
+//   decode_kernel  rows [0, nd): persistent one-wave workgroups, each taking every n-th work
+//                  item (decode, KV head, 16-head block, key partition).  K and V rows of 32
+//                  keys go HBM -> LDS by DMA; S^T = K Q^T on 16x16x32 MFMA, online softmax in the
+//                  lane that owns the head, O^T += V^T P^T with V^T read by transposing LDS
+//                  loads.  Writes float32 partials (m, l, unnormalised o).
 //   chunk_kernel   rows [nd, T): one 256-thread workgroup per (chunk, query block, KV head,
 //                  key split).  Rows of a tile are (position, head-in-group) pairs, so all query
-//                  heads of a GQA group share one K/V tile.  K and V^T tiles of 64 keys staged
-//                  in LDS; S^T = K Q^T and O^T += V^T P^T on 32x32x16 MFMA; causal mask only
+//                  heads of a GQA group share one K/V tile.  K and V tiles of 32 keys staged in
+//                  LDS by DMA; S^T = K Q^T and O^T += V^T P^T on 32x32x16 MFMA; causal mask only
 //                  where a key can exceed the row's position.  One split: normalised output
 //                  written directly; several: float32 partials.
 //   combine_kernel log-sum-exp merge of the partials of each (row, head) into out.
-// Softmax runs in base 2 with scale * log2(e) folded into the scores.
+// Softmax runs in base 2: weights are 2^(s c - m) with c = scale * log2(e) and m the running
+// maximum of s c.
 #include <algorithm>
 
 #include "cb.h"
@@ -38,6 +41,9 @@ namespace {
 #ifndef CB_CHUNK_MIN_TILES
 #define CB_CHUNK_MIN_TILES 512        // split chunk keys until at least this many tiles
 #endif
+#ifndef CB_DECODE_WAVES_PER_CU
+#define CB_DECODE_WAVES_PER_CU 8      // resident decode waves per compute unit (LDS-limited)
+#endif
 
 constexpr int kChunkRows = 128;   // rows per chunk tile: 4 waves x 32
 constexpr int kChunkKeys = 32;    // keys per LDS stage of a chunk tile
@@ -53,7 +59,7 @@ struct Plan {
   int32_t G = 1, head_blocks = 1;
   int32_t part = 256, max_parts = 0;
   int32_t bmq = 128, q_blocks = 0, n_chunk = 0, nsplit = 1;
-  size_t dec_o = 0, dec_ml = 0, chk_o = 0, chk_ml = 0, total = 0;
+  size_t dec_o = 0, dec_ml = 0, chk_o = 0, chk_ml = 0, dec_items = 0, dec_count = 0, total = 0;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
@@ -86,6 +92,8 @@ Plan make_plan(int32_t num_seqs, int32_t nd, int32_t T, int32_t max_q_len, int32
   const size_t chk_rows = p.nsplit > 1 ? static_cast<size_t>(T - nd) * Hq * p.nsplit : 0;
   p.chk_o = off;  off = align256(off + chk_rows * D * sizeof(float));
   p.chk_ml = off; off = align256(off + chk_rows * 2 * sizeof(float));
+  p.dec_items = off; off = align256(off + static_cast<size_t>(nd) * p.max_parts * 4 * sizeof(int32_t));
+  p.dec_count = off; off = align256(off + (nd > 0 ? sizeof(int32_t) : 0));
   p.total = off;
   return p;
 }
@@ -103,6 +111,8 @@ struct AttnArgs {
   float* dec_ml;
   float* chk_o;
   float* chk_ml;
+  int4* dec_items;      // decode partitions (s, p, context length, block-table offset)
+  int32_t* dec_count;   // number of decode work items
   int32_t num_seqs, nd, T, Hq, Hkv, G, bs, bs_shift;
   int32_t part, max_parts, head_blocks;
   int32_t bmq, q_blocks, n_chunk, nsplit;
@@ -228,144 +238,230 @@ __device__ __forceinline__ void lds_copies_done() { __builtin_amdgcn_s_waitcnt(0
 // ---------------------------------------------------------------------------------------------
 // Decode rows.
 // ---------------------------------------------------------------------------------------------
+// Work list: one entry per (decode row, key partition).  A single workgroup scans the partition
+// counts and writes the full partitions (part keys) of all rows first, then each row's shorter
+// last partition, so that the final round of work holds the short items.  It also writes the
+// number of work items (entries x KV heads x 16-head blocks).
+__device__ __forceinline__ int32_t block_scan_1024(int32_t v, int32_t* scan) {
+  const int tid = threadIdx.x;
+  scan[tid] = v;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {       // inclusive prefix sum
+    const int32_t u = tid >= off ? scan[tid - off] : 0;
+    __syncthreads();
+    scan[tid] += u;
+    __syncthreads();
+  }
+  return scan[tid];
+}
+
+__global__ __launch_bounds__(1024) void decode_prep_kernel(AttnArgs a) {
+  __shared__ int32_t scan[1024];
+  __shared__ int32_t carry;
+  const int tid = threadIdx.x;
+  for (int pass = 0; pass < 2; ++pass) {
+    if (tid == 0 && pass == 0) carry = 0;
+    __syncthreads();
+    for (int32_t base = 0; base < a.nd; base += 1024) {
+      const int32_t s = base + tid;
+      int32_t ctx = 0, cub = 0, full = 0, tail = 0;
+      if (s < a.nd) {
+        ctx = max(a.ctx_lens[s], 0);
+        cub = a.cu_blocks[s];
+        full = min(ctx / a.part, a.max_parts);
+        tail = full < a.max_parts && ctx - full * a.part > 0 ? 1 : 0;
+      }
+      const int32_t n = pass == 0 ? full : tail;
+      const int32_t first = carry + block_scan_1024(n, scan) - n;
+      for (int32_t j = 0; j < n; ++j)
+        a.dec_items[first + j] = make_int4(s, pass == 0 ? j : full, ctx, cub);
+      __syncthreads();                                // every thread has read carry
+      if (tid == 1023) carry += scan[1023];
+      __syncthreads();
+    }
+  }
+  if (tid == 0) a.dec_count[0] = carry * a.Hkv * a.head_blocks;
+}
+
+// Persistent waves: wave b takes work items b, b + n_waves, b + 2 n_waves, ...  Item w is list
+// entry w / (Hkv head_blocks) for KV head g and 16-head block hb.  The next item's query and
+// block ids are loaded right after a copy is issued (so waiting for that copy also covers them),
+// and its first K/V stage is copied during the current item's last stage, so a wave keeps one
+// stage in flight from its first item to its last.
 template <typename T, int D>
-__global__ __launch_bounds__(64) void decode_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 2 : 1))) void decode_kernel(AttnArgs a, const int4* __restrict__ items, const int32_t* __restrict__ count,
+                                                         int32_t n_waves) {
   constexpr int KS = D / 32;          // 32-slot contraction steps over the head dimension
   constexpr int DT = D / 16;          // 16-dim output tiles
   constexpr int ROW = D * sizeof(T);  // bytes per key row in LDS
   constexpr int RPI = 1024 / ROW;     // key rows per 1 KB copy instruction
   constexpr int NCP = kDecodeKeys / RPI;
+  constexpr int NBR = kMaxPartBlocks / 64;   // block ids per lane of one partition
   __shared__ __attribute__((aligned(1024))) char sK[kDecodeKeys * ROW];
   __shared__ __attribute__((aligned(1024))) char sV[kDecodeKeys * ROW];
   __shared__ int32_t sBlk[kMaxPartBlocks];
 
   const int lane = threadIdx.x;
-  int64_t item = blockIdx.x;
-  const int32_t p = static_cast<int32_t>(item % a.max_parts); item /= a.max_parts;
-  const int32_t hb = static_cast<int32_t>(item % a.head_blocks); item /= a.head_blocks;
-  const int32_t g = static_cast<int32_t>(item % a.Hkv);
-  const int32_t s = static_cast<int32_t>(item / a.Hkv);
-  const int32_t ctx = a.ctx_lens[s];
-  const int32_t k_lo = p * a.part;
-  if (k_lo >= ctx) return;
-  const int32_t k_hi = min(ctx, k_lo + a.part);
-  const int32_t k_last = k_hi - 1;
-  const int32_t gh = min(16, a.G - 16 * hb);
-  const int32_t h0 = g * a.G + 16 * hb;
   const int32_t col = lane & 15;      // head owned by this lane in S^T / P^T / O^T
   const int32_t grp = lane >> 4;      // slot group
   const int bsh = a.bs_shift;
   const int32_t bmask = (1 << bsh) - 1;
-
+  const int32_t per_entry = a.Hkv * a.head_blocks;
   const T* q = static_cast<const T*>(a.q);
   const char* kc = static_cast<const char*>(a.k_cache);
   const char* vc = static_cast<const char*>(a.v_cache);
-
-  // The partition's physical block ids, read once into LDS.
-  const int32_t b_lo = k_lo >> bsh;
-  {
-    const int32_t* btab = a.block_table + a.cu_blocks[s] + b_lo;
-    const int32_t nblk = ((k_hi - 1) >> bsh) - b_lo + 1;
-    for (int32_t i = lane; i < nblk; i += 64) sBlk[i] = btab[i];
-  }
-  Frag<T> qf[KS];
-  {
-    const T* qrow = q + (static_cast<int64_t>(s) * a.Hq + h0 + col) * D;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      if (col < gh) qf[ks].load(qrow + 32 * ks + 8 * grp);
-      else qf[ks].zero();
-    }
-  }
-  __syncthreads();
-
-  // Copy the 32 keys' K and V rows straight into LDS (no registers), chunk-swizzled.  Keys past
-  // the partition repeat its last key; they are masked out of the softmax.
-  const int64_t head_bytes = static_cast<int64_t>(g) * ((int64_t)ROW << bsh);
   const int64_t blk_bytes = static_cast<int64_t>(a.Hkv) * ((int64_t)ROW << bsh);
   const int cp_row = lane / (ROW / 16), cp_pos = lane % (ROW / 16);
-  auto issue = [&](int32_t key0) {
+
+  struct Item {
+    int32_t s, p, k_lo, k_hi, h0, gh;
+    int64_t head_bytes;
+  };
+  // Item fields from the work list; block ids of the partition and the query into registers
+  // (consumed later: nothing here waits for them).
+  auto resolve = [&](int32_t wi, int32_t (&blk)[NBR], Frag<T> (&qd)[KS]) {
+    Item it;
+    const int32_t e = wi / per_entry;
+    const int32_t r = wi - e * per_entry;
+    const int32_t g = r / a.head_blocks;
+    const int32_t hb = r - g * a.head_blocks;
+    const int4 ent = items[e];     // uniform, read-only here: a scalar load
+    it.s = ent.x;
+    it.p = ent.y;
+    it.k_lo = ent.y * a.part;
+    it.k_hi = min(ent.z, it.k_lo + a.part);
+    it.h0 = g * a.G + 16 * hb;
+    it.gh = min(16, a.G - 16 * hb);
+    it.head_bytes = static_cast<int64_t>(g) * ((int64_t)ROW << bsh);
+    const int32_t* btab = a.block_table + ent.w + (it.k_lo >> bsh);
+    const int32_t nblk = ((it.k_hi - 1) >> bsh) - (it.k_lo >> bsh) + 1;
+#pragma unroll
+    for (int i = 0; i < NBR; ++i)
+      if (64 * i + lane < nblk) blk[i] = btab[64 * i + lane];
+    const T* qrow = q + (static_cast<int64_t>(it.s) * a.Hq + it.h0 + col) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (col < it.gh) qd[ks].load(qrow + 32 * ks + 8 * grp);
+      else qd[ks].zero();
+    }
+    return it;
+  };
+  auto publish_blocks = [&](const Item& it, const int32_t (&blk)[NBR]) {
+    const int32_t nblk = ((it.k_hi - 1) >> bsh) - (it.k_lo >> bsh) + 1;
+#pragma unroll
+    for (int i = 0; i < NBR; ++i)
+      if (64 * i + lane < nblk) sBlk[64 * i + lane] = blk[i];
+  };
+  // Copy 32 keys' K and V rows straight into LDS (no registers), chunk-swizzled.  Keys past the
+  // partition repeat its last key; they are masked out of the softmax.
+  auto issue = [&](const Item& it, int32_t key0) {
+    const int32_t b_lo = it.k_lo >> bsh;
 #pragma unroll
     for (int i = 0; i < NCP; ++i) {
       const int r = i * RPI + cp_row;                        // row within the stage
-      const int32_t key = min(key0 + r, k_last);
-      const int64_t off = static_cast<int64_t>(sBlk[(key >> bsh) - b_lo]) * blk_bytes + head_bytes +
+      const int32_t key = min(key0 + r, it.k_hi - 1);
+      const int64_t off = static_cast<int64_t>(sBlk[(key >> bsh) - b_lo]) * blk_bytes + it.head_bytes +
                           static_cast<int64_t>(key & bmask) * ROW + 16 * lds_chunk(cp_pos, r, ROW);
       lds_copy16(kc + off, sK + i * 1024);
       lds_copy16(vc + off, sV + i * 1024);
     }
   };
+  const int32_t total = count[0];
+  int32_t w = blockIdx.x;
+  if (w >= total) return;
 
-  float m_run = kNegInf, l_run = 0.f;
-  f32x4 o[DT];
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  int32_t blk[NBR];
+  Frag<T> qf[KS], qn[KS];
+  Item cur = resolve(w, blk, qf);
+  publish_blocks(cur, blk);
+  __syncthreads();
+  issue(cur, cur.k_lo);
 
-  issue(k_lo);
-  for (int32_t key0 = k_lo; key0 < k_hi; key0 += kDecodeKeys) {
-    // Operands of this stage into registers (the copy above has landed: the compiler waits for it
-    // before the first LDS read), then the next stage's copy, which overlaps the compute below.
-    Frag<T> kf[2][KS];
+  while (true) {
+    w += n_waves;
+    const bool has_next = w < total;
+    const bool one_stage = cur.k_hi - cur.k_lo <= kDecodeKeys;
+    Item nxt{};
+    if (has_next && one_stage) nxt = resolve(w, blk, qn);
+
+    float m_run = kNegInf, l_run = 0.f;
+    f32x4 o[DT];
 #pragma unroll
-    for (int kg = 0; kg < 2; ++kg)
+    for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    for (int32_t key0 = cur.k_lo; key0 < cur.k_hi; key0 += kDecodeKeys) {
+      // Operands of this stage into registers (the copy has landed: the compiler waits for it
+      // before the first LDS read), then the next copy, which overlaps the compute below.
+      Frag<T> kf[2][KS];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) kf[kg][ks] = lds_row_frag<T>(sK, 16 * kg + col, 32 * ks + 8 * grp, ROW);
-    Frag<T> vt[DT];
+      for (int kg = 0; kg < 2; ++kg)
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) vt[dt] = lds_vt_frag16<T>(sV, dt, grp, col, ROW);
-    if (key0 + kDecodeKeys < k_hi) {
+        for (int ks = 0; ks < KS; ++ks) kf[kg][ks] = lds_row_frag<T>(sK, 16 * kg + col, 32 * ks + 8 * grp, ROW);
+      Frag<T> vt[DT];
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) vt[dt] = lds_vt_frag16<T>(sV, dt, grp, col, ROW);
       lds_reads_done();
-      issue(key0 + kDecodeKeys);
+      if (key0 + kDecodeKeys < cur.k_hi) {
+        issue(cur, key0 + kDecodeKeys);
+        if (key0 == cur.k_lo && has_next) nxt = resolve(w, blk, qn);
+      } else if (has_next) {
+        publish_blocks(nxt, blk);
+        issue(nxt, nxt.k_lo);
+      }
+
+      // S^T[key, head]: lane holds keys 16 kg + 4 grp + r of head col.
+      f32x4 st[2];
+#pragma unroll
+      for (int kg = 0; kg < 2; ++kg) {
+        st[kg] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) mma16_k32(st[kg], kf[kg][ks], qf[ks]);
+      }
+      float sv[8];
+      float mx = kNegInf;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int32_t key = key0 + 16 * (j >> 2) + 4 * grp + (j & 3);
+        const float x = key < cur.k_hi ? st[j >> 2][j & 3] : kNegInf;
+        sv[j] = x;
+        mx = fmaxf(mx, x);
+      }
+      mx = wave_xor_max(mx, 16);
+      mx = wave_xor_max(mx, 32);
+      const float m_new = fmaxf(m_run, mx * a.scale_log2);
+      const float m_use = m_new == kNegInf ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run - m_use);
+      float pv[8], psum = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        pv[j] = fast_exp2(fmaf(sv[j], a.scale_log2, -m_use));
+        psum += pv[j];
+      }
+      l_run = l_run * alpha + psum;
+      m_run = m_new;
+      Frag<T> pf;   // P^T slot 8 grp + j <-> key 16 (j / 4) + 4 grp + j % 4 (same order as sv)
+      pf.set_all(pv);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        o[dt] *= alpha;
+        mma16_k32(o[dt], vt[dt], pf);
+      }
     }
 
-    // S^T[key, head]: lane holds keys 16 kg + 4 grp + r of head col.
-    f32x4 st[2];
+    float l_tot = wave_xor_sum(l_run, 16);
+    l_tot = wave_xor_sum(l_tot, 32);
+    if (col < cur.gh) {
+      const int64_t prow = (static_cast<int64_t>(cur.s) * a.Hq + cur.h0 + col) * a.max_parts + cur.p;
+      float* po = a.dec_o + prow * D;
 #pragma unroll
-    for (int kg = 0; kg < 2; ++kg) {
-      st[kg] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) mma16_k32(st[kg], kf[kg][ks], qf[ks]);
+      for (int dt = 0; dt < DT; ++dt)
+        *reinterpret_cast<float4*>(po + 16 * dt + 4 * grp) = make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
+      if (grp == 0) *reinterpret_cast<float2*>(a.dec_ml + 2 * prow) = make_float2(m_run, l_tot);
     }
-    float sv[8];
-    float mx = kNegInf;
+    if (!has_next) break;
+    cur = nxt;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int32_t key = key0 + 16 * (j >> 2) + 4 * grp + (j & 3);
-      const float x = key < k_hi ? st[j >> 2][j & 3] * a.scale_log2 : kNegInf;
-      sv[j] = x;
-      mx = fmaxf(mx, x);
-    }
-    mx = wave_xor_max(mx, 16);
-    mx = wave_xor_max(mx, 32);
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = m_new == kNegInf ? 0.f : m_new;
-    const float alpha = exp2f(m_run - m_use);
-    float pv[8], psum = 0.f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      pv[j] = exp2f(sv[j] - m_use);
-      psum += pv[j];
-    }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-    Frag<T> pf;   // P^T slot 8 grp + j <-> key 16 (j / 4) + 4 grp + j % 4 (same order as sv)
-    pf.set_all(pv);
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      o[dt] *= alpha;
-      mma16_k32(o[dt], vt[dt], pf);
-    }
-  }
-
-  float l_tot = wave_xor_sum(l_run, 16);
-  l_tot = wave_xor_sum(l_tot, 32);
-  if (col < gh) {
-    const int64_t prow = (static_cast<int64_t>(s) * a.Hq + h0 + col) * a.max_parts + p;
-    float* po = a.dec_o + prow * D;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-      *reinterpret_cast<float4*>(po + 16 * dt + 4 * grp) = make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
-    if (grp == 0) *reinterpret_cast<float2*>(a.dec_ml + 2 * prow) = make_float2(m_run, l_tot);
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = qn[ks];
   }
 }
 
@@ -376,9 +472,7 @@ template <typename T>
 __device__ __forceinline__ void store4(T* dst, float x0, float x1, float x2, float x3);
 template <>
 __device__ __forceinline__ void store4<bf16_t>(bf16_t* dst, float x0, float x1, float x2, float x3) {
-  const uint32_t lo = f32_to_bf16_bits(x0) | (static_cast<uint32_t>(f32_to_bf16_bits(x1)) << 16);
-  const uint32_t hi = f32_to_bf16_bits(x2) | (static_cast<uint32_t>(f32_to_bf16_bits(x3)) << 16);
-  *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
+  *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(x0, x1), pack_bf16x2(x2, x3));
 }
 template <>
 __device__ __forceinline__ void store4<float>(float* dst, float x0, float x1, float x2, float x3) {
@@ -512,33 +606,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
     }
 
     const int32_t k0 = kt * kChunkKeys;
-    const bool need_mask = k0 + kChunkKeys - 1 > c + qb * a.bmq;   // some key may pass a row
     f32x16 st = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) mma32_k16(st, kf[ks], qf[ks]);
-    float mx = kNegInf;
+    if (k0 + kChunkKeys - 1 > c + qb * a.bmq) {   // some key of the stage may pass a row
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float x = st[r] * a.scale_log2;
-      if (need_mask && k0 + acc32_row(lane, r) > qpos) x = kNegInf;
-      st[r] = x;
-      mx = fmaxf(mx, x);
+      for (int r = 0; r < 16; ++r)
+        if (k0 + acc32_row(lane, r) > qpos) st[r] = kNegInf;
     }
+    // Raw scores: the maximum is taken before scaling (scale > 0 keeps the order) and the scale
+    // is folded into the exponent, 2^(s c - m).
+    float mx = st[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, st[r]);
     mx = wave_xor_max(mx, 32);
-    const float m_new = fmaxf(m_run, mx);
+    const float m_new = fmaxf(m_run, mx * a.scale_log2);
     const float m_use = m_new == kNegInf ? 0.f : m_new;
-    const float alpha = exp2f(m_run - m_use);
+    const float alpha = fast_exp2(m_run - m_use);
     float psum = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float e = exp2f(st[r] - m_use);
+      const float e = fast_exp2(fmaf(st[r], a.scale_log2, -m_use));
       st[r] = e;
       psum += e;
     }
     l_run = l_run * alpha + psum;
     m_run = m_new;
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {   // some row's maximum moved
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) o[mt] *= alpha;
+      for (int mt = 0; mt < MT; ++mt) o[mt] *= alpha;
+    }
 #pragma unroll
     for (int ps = 0; ps < 2; ++ps) {          // 16-key contraction steps
       float pv[8];
@@ -654,19 +751,37 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a, int32_t n_dec_
   }
 }
 
-// Decode split, chunk tiles and combine in order on the caller's stream.  (Running the chunk
-// kernel on a second stream beside the decode split was measured slower: the cross-queue join
-// before the combine cost more than the overlap saved.)
+// Compute units of the device that owns the stream (cached per device).
+int compute_units(hipStream_t st) {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipStreamGetDevice(st, &dev) != hipSuccess && hipGetDevice(&dev) != hipSuccess) return 256;
+  if (dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+// Decode work list, decode split, chunk tiles and combine in order on the caller's stream.
+// (Running the chunk kernel on a second stream beside the decode split was measured slower: the
+// cross-queue join before the combine cost more than the overlap saved.)
 template <typename T, int D>
 int launch_all(hipStream_t st, const AttnArgs& a, const Plan& p, void* const* events) {
   auto rec = [&](int i) {
     if (events && events[i]) (void)hipEventRecord(static_cast<hipEvent_t>(events[i]), st);
   };
   if (a.nd > 0) {
-    const int64_t grid = static_cast<int64_t>(a.nd) * a.Hkv * a.head_blocks * a.max_parts;
-    if (grid > 0x7fffffff) return CB_ERR_INVALID;
+    const int64_t upper = static_cast<int64_t>(a.nd) * a.max_parts * a.Hkv * a.head_blocks;
+    if (upper > 0x7fff0000) return CB_ERR_INVALID;    // item indices + one stride stay in int32
+    decode_prep_kernel<<<dim3(1), dim3(1024), 0, st>>>(a);
+    if (hipGetLastError() != hipSuccess) return CB_ERR_HIP;
+    const int64_t n_waves = std::min<int64_t>(upper, static_cast<int64_t>(CB_DECODE_WAVES_PER_CU) * compute_units(st));
     rec(0);
-    decode_kernel<T, D><<<dim3(static_cast<uint32_t>(grid)), dim3(64), 0, st>>>(a);
+    decode_kernel<T, D><<<dim3(static_cast<uint32_t>(n_waves)), dim3(64), 0, st>>>(
+        a, a.dec_items, a.dec_count, static_cast<int32_t>(n_waves));
     if (hipGetLastError() != hipSuccess) return CB_ERR_HIP;
     rec(1);
   }
@@ -751,6 +866,8 @@ extern "C" int cb_mixed_paged_attention_timed(
   a.dec_ml = reinterpret_cast<float*>(ws + p.dec_ml);
   a.chk_o = reinterpret_cast<float*>(ws + p.chk_o);
   a.chk_ml = reinterpret_cast<float*>(ws + p.chk_ml);
+  a.dec_items = reinterpret_cast<int4*>(ws + p.dec_items);
+  a.dec_count = reinterpret_cast<int32_t*>(ws + p.dec_count);
   a.num_seqs = num_seqs; a.nd = num_decodes; a.T = T; a.Hq = Hq; a.Hkv = Hkv; a.G = p.G;
   a.bs = block_size;
   a.bs_shift = __builtin_ctz(static_cast<unsigned>(block_size));

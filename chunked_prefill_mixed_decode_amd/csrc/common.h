@@ -21,6 +21,19 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
 }
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
+// Two floats -> two bfloat16 (round to nearest, ties to even) in one v_cvt_pk_bf16_f32; a in the
+// low half.
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), bf16x2));
+}
+
+// 2^x on the hardware exponential (v_exp_f32): exact at 0, 0 for -inf, results below the
+// smallest normal flushed to 0.  Used for softmax weights, which are then rounded to bf16 or
+// summed in float32.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // Eight consecutive elements of T held by one lane.  For bf16 that is 16 bytes (one dwordx4),
 // for float 32 bytes (two).
 template <typename T> struct Frag;
@@ -36,11 +49,8 @@ template <> struct Frag<bf16_t> {
   }
   // Pack 8 floats (rounded to nearest-even).
   __device__ __forceinline__ void set_all(const float* f) {
-    uint32_t* w = &u.x;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      w[i] = static_cast<uint32_t>(f32_to_bf16_bits(f[2 * i])) |
-             (static_cast<uint32_t>(f32_to_bf16_bits(f[2 * i + 1])) << 16);
+    u = make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
+                   pack_bf16x2(f[6], f[7]));
   }
   __device__ __forceinline__ bf16x8 vec() const { return __builtin_bit_cast(bf16x8, u); }
 };

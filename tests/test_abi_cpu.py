@@ -229,6 +229,8 @@ def test_workspace_grows_with_context_and_rows():
     a = f(65, 64, 512, 448, 4097, 4097, 32, 32, 128)
     b = f(129, 128, 576, 448, 4097, 4097, 32, 32, 128)
     assert 0 < a < b
-    # decode partitions grow to at most 4096 keys: ceil(300000 / 4096) = 74 partials per head
-    assert f(2, 1, 2, 1, 300000, 300000, 8, 8, 128) <= 74 * 8 * 130 * 4 + 8 * 8 * 130 * 4 + 4 * 256
+    # decode partitions grow to at most 4096 keys: ceil(300000 / 4096) = 74 partials per head,
+    # plus a 16-byte work-list entry per partition and the queue counter
+    assert f(2, 1, 2, 1, 300000, 300000, 8, 8, 128) <= (74 * 8 * 130 * 4 + 8 * 8 * 130 * 4 + 74 * 16
+                                                        + 6 * 256)
     assert f(0, 0, 0, 0, 0, 0, 32, 32, 128) == 0
