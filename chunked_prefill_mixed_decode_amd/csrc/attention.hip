@@ -47,6 +47,11 @@ namespace {
 
 constexpr int kChunkRows = 128;   // rows per chunk tile: 4 waves x 32
 constexpr int kChunkKeys = 32;    // keys per LDS stage of a chunk tile
+#ifndef CB_CHUNK_STAGES
+#define CB_CHUNK_STAGES 4             // chunk K/V stages in the LDS ring (copies run NS - 1 ahead)
+#endif
+constexpr int kChunkStages = CB_CHUNK_STAGES;
+static_assert(kChunkStages >= 2 && kChunkStages <= 4, "chunk ring depth");
 constexpr int kDecodeKeys = 32;   // keys per decode iteration
 constexpr int kMaxSplit = 8;
 constexpr int kMaxPart = 4096;                       // longest decode partition (keys)
@@ -122,18 +127,46 @@ struct AttnArgs {
 // ---------------------------------------------------------------------------------------------
 // LDS staging.  K and V rows are copied from HBM straight into LDS with the gfx950 16-byte LDS
 // DMA (global_load_lds_dwordx4): lane l of one instruction lands at byte 16 l of a 1 KB span.
-// Rows are chunk-swizzled: logical 16-byte chunk c of row r sits at chunk c ^ (r mod m), m the
-// smaller of 16 and the chunks per row, so the lanes that read one chunk of many rows hit
-// different banks.
+// Rows are chunk-swizzled: logical 16-byte chunk c of row r sits at chunk c ^ s(r).  Every
+// 256-byte row starts at bank 0, so s decides the banks:
+//   256+ byte rows: s(r) = 4 (r mod 4) + (r / 4) mod 4.  Sixteen consecutive rows read at one
+//     chunk (the K operand reads) get 16 different s; four consecutive rows read at four aligned
+//     consecutive chunks (the transposing V reads) differ in bits 2-3 of s, so all 16 (row,
+//     chunk) pairs land on different 16-byte bank groups.
+//   128-byte rows (two rows per bank line): with q = (r / 2) mod 8, s(r) = 4 (q mod 2) + q / 2,
+//     which gives the same two properties.
 // ---------------------------------------------------------------------------------------------
 __device__ __forceinline__ int lds_chunk(int c, int r, int row_bytes) {
-  const int m = (row_bytes / 16 < 16 ? row_bytes / 16 : 16) - 1;
-  return c ^ (r & m);
+  if (row_bytes >= 256) return c ^ (((r & 3) << 2) | ((r >> 2) & 3));
+  const int q = (r >> 1) & 7;
+  return c ^ (((q & 1) << 2) | (q >> 1));
+}
+// LDS byte address of a pointer into shared memory (the address operand of ds_read).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)(p)));
 }
 __device__ __forceinline__ void lds_copy16(const char* src, char* lds_dst) {
   __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(src),
                                    (void __attribute__((address_space(3)))*)(lds_dst),
                                    16, 0, 0);
+}
+// The same copy issued from inline asm.  The compiler does not see it, so it adds no vmcnt waits
+// for it anywhere: the code that issues these waits for them itself (wait_vm_barrier).  Copies
+// complete in issue order with every other vector-memory operation, so the compiler's own waits
+// stay correct (they only become stricter).  M0 carries the wave-uniform LDS destination; it is
+// saved and restored around the copy (M0 is reserved, so a clobber would not be honoured), with
+// one wait state between the M0 write and the copy that reads it.
+__device__ __forceinline__ void lds_copy16_asm(const char* src, const char* lds_dst) {
+  const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(lds_dst));
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(dst));
 }
 // Wait for this wave's LDS reads before a DMA overwrites the buffer they read
 // (s_waitcnt lgkmcnt(0), vmcnt and expcnt untouched).
@@ -234,6 +267,83 @@ __device__ __forceinline__ Frag<float> lds_vt_frag32<float>(const char* base, in
 // Wait until this wave's LDS copies have landed (s_waitcnt vmcnt(0); lgkmcnt, expcnt untouched).
 // Other waves' copies are visible after the workgroup barrier that follows.
 __device__ __forceinline__ void lds_copies_done() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+
+// Wait until at most N of this wave's vector-memory operations are outstanding (memory returns
+// in issue order, so every older LDS copy has landed), then the workgroup barrier.
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// The operands of one 32-key chunk stage (bf16): K rows (KS ds_read_b128) and V^T (two
+// ds_read_b64_tr_b16 per 32x16 piece, the second 16 keys further down), issued back to back
+// and waited for together inside one asm block.  ka[ks] / va[2 mt + h] are the LDS addresses
+// lds_row_frag / lds_vt_frag32 would read (piece ps = 0); ps = 1 is 16 rows further.
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+template <int D> struct StageRegs;
+template <> struct StageRegs<128> {
+  u32x4 k[8];
+  u32x2 v[2][8];   // [ps][2 mt + h]
+  __device__ __forceinline__ void read(const uint32_t (&ka)[8], const uint32_t (&va)[8]) {
+    asm volatile(
+        "ds_read_b128 %0, %24\n\t"
+        "ds_read_b128 %1, %25\n\t"
+        "ds_read_b128 %2, %26\n\t"
+        "ds_read_b128 %3, %27\n\t"
+        "ds_read_b128 %4, %28\n\t"
+        "ds_read_b128 %5, %29\n\t"
+        "ds_read_b128 %6, %30\n\t"
+        "ds_read_b128 %7, %31\n\t"
+        "ds_read_b64_tr_b16 %8, %32\n\t"
+        "ds_read_b64_tr_b16 %9, %33\n\t"
+        "ds_read_b64_tr_b16 %10, %34\n\t"
+        "ds_read_b64_tr_b16 %11, %35\n\t"
+        "ds_read_b64_tr_b16 %12, %36\n\t"
+        "ds_read_b64_tr_b16 %13, %37\n\t"
+        "ds_read_b64_tr_b16 %14, %38\n\t"
+        "ds_read_b64_tr_b16 %15, %39\n\t"
+        "ds_read_b64_tr_b16 %16, %32 offset:4096\n\t"
+        "ds_read_b64_tr_b16 %17, %33 offset:4096\n\t"
+        "ds_read_b64_tr_b16 %18, %34 offset:4096\n\t"
+        "ds_read_b64_tr_b16 %19, %35 offset:4096\n\t"
+        "ds_read_b64_tr_b16 %20, %36 offset:4096\n\t"
+        "ds_read_b64_tr_b16 %21, %37 offset:4096\n\t"
+        "ds_read_b64_tr_b16 %22, %38 offset:4096\n\t"
+        "ds_read_b64_tr_b16 %23, %39 offset:4096\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(k[4]), "=&v"(k[5]), "=&v"(k[6]),
+          "=&v"(k[7]), "=&v"(v[0][0]), "=&v"(v[0][1]), "=&v"(v[0][2]), "=&v"(v[0][3]), "=&v"(v[0][4]),
+          "=&v"(v[0][5]), "=&v"(v[0][6]), "=&v"(v[0][7]), "=&v"(v[1][0]), "=&v"(v[1][1]), "=&v"(v[1][2]),
+          "=&v"(v[1][3]), "=&v"(v[1][4]), "=&v"(v[1][5]), "=&v"(v[1][6]), "=&v"(v[1][7])
+        : "v"(ka[0]), "v"(ka[1]), "v"(ka[2]), "v"(ka[3]), "v"(ka[4]), "v"(ka[5]), "v"(ka[6]), "v"(ka[7]),
+          "v"(va[0]), "v"(va[1]), "v"(va[2]), "v"(va[3]), "v"(va[4]), "v"(va[5]), "v"(va[6]), "v"(va[7]));
+  }
+};
+template <> struct StageRegs<64> {
+  u32x4 k[4];
+  u32x2 v[2][4];
+  __device__ __forceinline__ void read(const uint32_t (&ka)[4], const uint32_t (&va)[4]) {
+    asm volatile(
+        "ds_read_b128 %0, %12\n\t"
+        "ds_read_b128 %1, %13\n\t"
+        "ds_read_b128 %2, %14\n\t"
+        "ds_read_b128 %3, %15\n\t"
+        "ds_read_b64_tr_b16 %4, %16\n\t"
+        "ds_read_b64_tr_b16 %5, %17\n\t"
+        "ds_read_b64_tr_b16 %6, %18\n\t"
+        "ds_read_b64_tr_b16 %7, %19\n\t"
+        "ds_read_b64_tr_b16 %8, %16 offset:2048\n\t"
+        "ds_read_b64_tr_b16 %9, %17 offset:2048\n\t"
+        "ds_read_b64_tr_b16 %10, %18 offset:2048\n\t"
+        "ds_read_b64_tr_b16 %11, %19 offset:2048\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(v[0][0]), "=&v"(v[0][1]),
+          "=&v"(v[0][2]), "=&v"(v[0][3]), "=&v"(v[1][0]), "=&v"(v[1][1]), "=&v"(v[1][2]), "=&v"(v[1][3])
+        : "v"(ka[0]), "v"(ka[1]), "v"(ka[2]), "v"(ka[3]), "v"(va[0]), "v"(va[1]), "v"(va[2]), "v"(va[3]));
+  }
+};
 
 // ---------------------------------------------------------------------------------------------
 // Decode rows.
@@ -480,14 +590,17 @@ __device__ __forceinline__ void store4<float>(float* dst, float x0, float x1, fl
 }
 
 template <typename T, int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void chunk_kernel(AttnArgs a, int32_t n_tiles, int32_t per_xcd) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 2 : 1))) void chunk_kernel(AttnArgs a, int32_t n_tiles, int32_t per_xcd) {
   constexpr int KS = D / 16;          // 16-slot contraction steps over the head dimension
   constexpr int MT = D / 32;          // 32-dim output tiles
   constexpr int ROW = D * sizeof(T);  // bytes per key row in LDS
   constexpr int RPI = 1024 / ROW;     // key rows per 1 KB copy instruction
   constexpr int NCPW = kChunkKeys / RPI / 4;    // copy instructions per wave per tensor
-  __shared__ __attribute__((aligned(1024))) char sK[kChunkKeys * ROW];
-  __shared__ __attribute__((aligned(1024))) char sV[kChunkKeys * ROW];
+  constexpr int CPW = 2 * NCPW;                 // copy instructions per wave per stage
+  constexpr int NS = sizeof(T) == 2 ? kChunkStages : 2;   // float stages are twice as large
+  constexpr int STAGE = kChunkKeys * ROW;       // bytes of K (and of V) per stage
+  __shared__ __attribute__((aligned(1024))) char sK[NS * STAGE];
+  __shared__ __attribute__((aligned(1024))) char sV[NS * STAGE];
   __shared__ int32_t sBlk[kBlockWindow];       // a window of the sequence's block table
 
   // XCD-aware order: workgroup b runs on XCD b % 8; give each XCD a contiguous run of logical
@@ -546,26 +659,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
   for (int mt = 0; mt < MT; ++mt) o[mt] = f32x16{};
 
   // Block ids come from an LDS window [win_lo, win_lo + kBlockWindow) of the block table.  K and V
-  // rows go HBM -> LDS by DMA (chunk-swizzled rows); keys at or past kv_end repeat kv_end - 1 and
-  // are masked (probability 0).  Each stage is read whole into registers before the next copy is
-  // issued into the same buffer, so the copy overlaps the stage's matrix work.
+  // rows go HBM -> LDS by DMA (chunk-swizzled rows) into a ring of NS stage buffers; keys at or
+  // past kv_end repeat kv_end - 1 and are masked (probability 0).  Stage j's copy is issued
+  // during stage j - NS + 1, after the barrier that proves every wave has read the buffer it
+  // overwrites, so NS - 1 stages of matrix work cover each copy's latency.
   int32_t win_lo = 0;
   const int32_t n_blk = ((kv_end - 1) >> bsh) + 1;
-  auto fill_window = [&](int32_t first_block) {
+  auto fill_window = [&](int32_t first_block) {   // all loads first, then all LDS writes
     win_lo = first_block;
     const int32_t n = min(kBlockWindow, n_blk - first_block);
-    for (int32_t i = tid; i < n; i += 256) sBlk[i] = btab[first_block + i];
-  };
-  auto window_covers = [&](int32_t kt) {
-    const int32_t b0 = (kt * kChunkKeys) >> bsh;
-    const int32_t b1 = (min(kt * kChunkKeys + kChunkKeys, kv_end) - 1) >> bsh;
-    return b0 >= win_lo && b1 < win_lo + kBlockWindow;
+    int32_t ids[kBlockWindow / 256];
+#pragma unroll
+    for (int u = 0; u < kBlockWindow / 256; ++u)
+      if (tid + 256 * u < n) ids[u] = btab[first_block + tid + 256 * u];
+#pragma unroll
+    for (int u = 0; u < kBlockWindow / 256; ++u)
+      if (tid + 256 * u < n) sBlk[tid + 256 * u] = ids[u];
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // no load left pending on any path (see below)
   };
   const int32_t k_last = kv_end - 1;
   const int64_t head_bytes = static_cast<int64_t>(g) * ((int64_t)ROW << bsh);
   const int64_t blk_bytes = static_cast<int64_t>(a.Hkv) * ((int64_t)ROW << bsh);
   const int cp_row = lane / (ROW / 16), cp_pos = lane % (ROW / 16);
-  auto issue = [&](int32_t kt) {
+  auto issue = [&](int32_t kt, int buf) {
     const int32_t k0 = kt * kChunkKeys;
 #pragma unroll
     for (int j = 0; j < NCPW; ++j) {
@@ -574,77 +690,127 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
       const int32_t key = min(k0 + r, k_last);
       const int64_t off = static_cast<int64_t>(sBlk[(key >> bsh) - win_lo]) * blk_bytes + head_bytes +
                           static_cast<int64_t>(key & bmask) * ROW + 16 * lds_chunk(cp_pos, r, ROW);
-      lds_copy16(kc + off, sK + i * 1024);
-      lds_copy16(vc + off, sV + i * 1024);
+      lds_copy16_asm(kc + off, sK + buf * STAGE + i * 1024);
+      lds_copy16_asm(vc + off, sV + buf * STAGE + i * 1024);
     }
   };
+  // Wait for this wave's copies of the current stage (all but the `later` stages issued after
+  // it), then the barrier.
+  auto wait_stage = [&](int32_t later) {
+    if (later >= 2) wait_vm_barrier<2 * CPW>();
+    else if (later == 1) wait_vm_barrier<CPW>();
+    else wait_vm_barrier<0>();
+  };
 
-  if (kt_lo < kt_hi) {
-    fill_window((kt_lo * kChunkKeys) >> bsh);
-    __syncthreads();
-    issue(kt_lo);
-  }
-  for (int32_t kt = kt_lo; kt < kt_hi; ++kt) {
-    lds_copies_done();
-    __syncthreads();                          // every wave's copy of this stage has landed
-    Frag<T> kf[KS];
+  // Loop-invariant LDS read offsets of this lane within a stage buffer (bf16 operand reads).
+  uint32_t ka[KS], va[KS];
+  if constexpr (sizeof(T) == 2) {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) kf[ks] = lds_row_frag<T>(sK, col, 16 * ks + 8 * half, ROW);
-    Frag<T> vt[2][MT];
+    for (int ks = 0; ks < KS; ++ks) {
+      const int b0 = 2 * (16 * ks + 8 * half);
+      ka[ks] = col * ROW + 16 * lds_chunk(b0 >> 4, col, ROW);
+    }
+    const int grp = lane >> 4, ii = lane & 15, jj = ii >> 2, qd = ii & 3;
 #pragma unroll
-    for (int ps = 0; ps < 2; ++ps)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) vt[ps][mt] = lds_vt_frag32<T>(sV, mt, ps, lane, ROW);
-    lds_reads_done();
-    __syncthreads();                          // every wave has read the stage
-    if (kt + 1 < kt_hi) {
-      if (!window_covers(kt + 1)) {
-        fill_window(((kt + 1) * kChunkKeys) >> bsh);
-        __syncthreads();
+      for (int h = 0; h < 2; ++h) {
+        const int e = 32 * mt + 16 * (grp & 1) + 4 * qd;
+        const int r = 8 * h + 4 * (grp >> 1) + jj;
+        va[2 * mt + h] = r * ROW + 16 * lds_chunk((2 * e) >> 4, r, ROW) + ((2 * e) & 15);
       }
-      issue(kt + 1);
-    }
+  }
 
-    const int32_t k0 = kt * kChunkKeys;
-    f32x16 st = f32x16{};
+  // Outer loop: one block-id window at a time (a window covers thousands of stages; the copy ring
+  // drains at its end).  Inner loop: the ring, with no other vector-memory operation inside, so
+  // the compiler adds no waits there.
+  const int32_t n_st = kt_hi - kt_lo;
+  int32_t j = 0;
+  while (j < n_st) {
+    fill_window(((kt_lo + j) * kChunkKeys) >> bsh);   // ends with vmcnt(0): nothing left pending
+    __syncthreads();                                   // also: every wave is done with the ring
+    // Stages whose keys all lie in blocks [win_lo, win_lo + kBlockWindow) (a multiple of 32 keys).
+    const int64_t key_end = static_cast<int64_t>(win_lo + kBlockWindow) << bsh;
+    const int32_t j_end = kv_end <= key_end ? n_st : static_cast<int32_t>(min<int64_t>(n_st, key_end / kChunkKeys - kt_lo));
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) mma32_k16(st, kf[ks], qf[ks]);
-    if (k0 + kChunkKeys - 1 > c + qb * a.bmq) {   // some key of the stage may pass a row
+    for (int p = 0; p < NS - 1; ++p)
+      if (j + p < j_end) issue(kt_lo + j + p, (j + p) % NS);
+    for (; j < j_end; ++j) {
+      const int32_t kt = kt_lo + j;
+      const int buf = j % NS;
+      wait_stage(min(NS - 2, j_end - 1 - j));    // every wave's copy of stage j has landed
+      if (j + NS - 1 < j_end) issue(kt + NS - 1, (j + NS - 1) % NS);
+
+      Frag<T> kf[KS];
+      Frag<T> vt[2][MT];
+      if constexpr (sizeof(T) == 2) {
+        StageRegs<D> sr;
+        uint32_t kaa[KS], vaa[KS];
+        const uint32_t base_k = lds_addr(sK + buf * STAGE), base_v = lds_addr(sV + buf * STAGE);
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (k0 + acc32_row(lane, r) > qpos) st[r] = kNegInf;
-    }
-    // Raw scores: the maximum is taken before scaling (scale > 0 keeps the order) and the scale
-    // is folded into the exponent, 2^(s c - m).
-    float mx = st[0];
+        for (int i = 0; i < KS; ++i) {
+          kaa[i] = base_k + ka[i];
+          vaa[i] = base_v + va[i];
+        }
+        sr.read(kaa, vaa);
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, st[r]);
-    mx = wave_xor_max(mx, 32);
-    const float m_new = fmaxf(m_run, mx * a.scale_log2);
-    const float m_use = m_new == kNegInf ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
-    float psum = 0.f;
+        for (int ks = 0; ks < KS; ++ks) kf[ks].u = make_uint4(sr.k[ks].x, sr.k[ks].y, sr.k[ks].z, sr.k[ks].w);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float e = fast_exp2(fmaf(st[r], a.scale_log2, -m_use));
-      st[r] = e;
-      psum += e;
-    }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {   // some row's maximum moved
+        for (int ps = 0; ps < 2; ++ps)
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) o[mt] *= alpha;
-    }
+          for (int mt = 0; mt < MT; ++mt)
+            vt[ps][mt].u = make_uint4(sr.v[ps][2 * mt].x, sr.v[ps][2 * mt].y, sr.v[ps][2 * mt + 1].x,
+                                      sr.v[ps][2 * mt + 1].y);
+      } else {
 #pragma unroll
-    for (int ps = 0; ps < 2; ++ps) {          // 16-key contraction steps
-      float pv[8];
+        for (int ks = 0; ks < KS; ++ks) kf[ks] = lds_row_frag<T>(sK + buf * STAGE, col, 16 * ks + 8 * half, ROW);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) pv[j] = st[8 * ps + j];
-      Frag<T> pf;
-      pf.set_all(pv);
+        for (int ps = 0; ps < 2; ++ps)
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) mma32_k16(o[mt], vt[ps][mt], pf);
+          for (int mt = 0; mt < MT; ++mt) vt[ps][mt] = lds_vt_frag32<T>(sV + buf * STAGE, mt, ps, lane, ROW);
+      }
+
+      const int32_t k0 = kt * kChunkKeys;
+      f32x16 st = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) mma32_k16(st, kf[ks], qf[ks]);
+      if (k0 + kChunkKeys - 1 > c + qb * a.bmq) {   // some key of the stage may pass a row
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (k0 + acc32_row(lane, r) > qpos) st[r] = kNegInf;
+      }
+      // Raw scores: the maximum is taken before scaling (scale > 0 keeps the order) and the scale
+      // is folded into the exponent, 2^(s c - m).
+      float mx = st[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, st[r]);
+      mx = wave_xor_max(mx, 32);
+      const float m_new = fmaxf(m_run, mx * a.scale_log2);
+      const float m_use = m_new == kNegInf ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run - m_use);
+      float psum = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float e = fast_exp2(fmaf(st[r], a.scale_log2, -m_use));
+        st[r] = e;
+        psum += e;
+      }
+      l_run = l_run * alpha + psum;
+      m_run = m_new;
+      if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {   // some row's maximum moved
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) o[mt] *= alpha;
+      }
+#pragma unroll
+      for (int ps = 0; ps < 2; ++ps) {          // 16-key contraction steps
+        float pv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pv[e] = st[8 * ps + e];
+        Frag<T> pf;
+        pf.set_all(pv);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) mma32_k16(o[mt], vt[ps][mt], pf);
+      }
     }
   }
 
