@@ -32,11 +32,8 @@ namespace cb {
 namespace {
 
 // Tuning constants (compile-time; the defaults are the measured choices on MI355X).
-#ifndef CB_DECODE_TARGET_PARTS
-#define CB_DECODE_TARGET_PARTS 16     // aim for about this many key partitions per longest decode
-#endif
-#ifndef CB_DECODE_MIN_PART
-#define CB_DECODE_MIN_PART 256        // smallest decode key partition
+#ifndef CB_DECODE_MIN_STAGES
+#define CB_DECODE_MIN_STAGES 8        // shortest decode stage range per wave (32-key stages)
 #endif
 #ifndef CB_CHUNK_MIN_TILES
 #define CB_CHUNK_MIN_TILES 512        // split chunk keys until at least this many tiles
@@ -52,35 +49,34 @@ constexpr int kChunkKeys = 32;    // keys per LDS stage of a chunk tile
 #endif
 constexpr int kChunkStages = CB_CHUNK_STAGES;
 static_assert(kChunkStages >= 2 && kChunkStages <= 4, "chunk ring depth");
-constexpr int kDecodeKeys = 32;   // keys per decode iteration
+constexpr int kDecodeKeys = 32;   // keys per decode stage
 constexpr int kMaxSplit = 8;
-constexpr int kMaxPart = 4096;                       // longest decode partition (keys)
 constexpr int kMinBlock = 8;
-constexpr int kMaxPartBlocks = kMaxPart / kMinBlock;
 constexpr int kMaxBlock = 256;
+constexpr int kSubKeys = 3840;                       // longest decode sub-range with one block-id load
+constexpr int kSubBlocks = 512;                      // >= kSubKeys / kMinBlock + 1
+static_assert(kSubKeys % kDecodeKeys == 0 && kSubKeys / kMinBlock + 1 <= kSubBlocks, "sub-range");
+constexpr int kMaxDecodeWaves = 8192;                // workspace bound on the decode grid
 constexpr int kBlockWindow = 2048;                   // block ids per LDS window (chunk tiles)
 
 struct Plan {
-  int32_t G = 1, head_blocks = 1;
-  int32_t part = 256, max_parts = 0;
+  int32_t G = 1, head_blocks = 1, hw = 1, ups = 1;
   int32_t bmq = 128, q_blocks = 0, n_chunk = 0, nsplit = 1;
-  size_t dec_o = 0, dec_ml = 0, chk_o = 0, chk_ml = 0, dec_items = 0, dec_count = 0, total = 0;
+  size_t dec_o = 0, dec_ml = 0, chk_o = 0, chk_ml = 0, dec_seq = 0, dec_wave = 0, dec_par = 0, total = 0;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 // Partitioning decisions, shared by the workspace query and the launch so they always agree.
-Plan make_plan(int32_t num_seqs, int32_t nd, int32_t T, int32_t max_q_len, int32_t max_dctx,
-               int32_t max_ctx, int32_t Hq, int32_t Hkv, int32_t D) {
+// Decode partials: one slot per (unit, wave) pair that shares stages, at most units + waves
+// slots of hw heads each (a unit is a decode row's KV head and 16-head block).
+Plan make_plan(int32_t num_seqs, int32_t nd, int32_t T, int32_t max_q_len, int32_t max_ctx,
+               int32_t Hq, int32_t Hkv, int32_t D) {
   Plan p;
   p.G = Hq / Hkv;
   p.head_blocks = (p.G + 15) / 16;
-  p.part = CB_DECODE_MIN_PART;
-  if (nd > 0) {
-    const int32_t want = (std::max(max_dctx, 1) + CB_DECODE_TARGET_PARTS - 1) / CB_DECODE_TARGET_PARTS;
-    while (p.part < want && p.part < kMaxPart) p.part *= 2;
-    p.max_parts = (std::max(max_dctx, 1) + p.part - 1) / p.part;
-  }
+  p.hw = std::min(16, p.G);
+  p.ups = Hkv * p.head_blocks;
   p.bmq = kChunkRows / p.G;
   p.n_chunk = num_seqs - nd;
   if (p.n_chunk > 0) {
@@ -91,14 +87,15 @@ Plan make_plan(int32_t num_seqs, int32_t nd, int32_t T, int32_t max_q_len, int32
       p.nsplit *= 2;
   }
   size_t off = 0;
-  const size_t dec_rows = static_cast<size_t>(nd) * Hq * p.max_parts;
-  p.dec_o = off;  off = align256(off + dec_rows * D * sizeof(float));
-  p.dec_ml = off; off = align256(off + dec_rows * 2 * sizeof(float));
+  const size_t dec_slots = nd > 0 ? static_cast<size_t>(nd) * p.ups + kMaxDecodeWaves : 0;
+  p.dec_o = off;  off = align256(off + dec_slots * p.hw * D * sizeof(float));
+  p.dec_ml = off; off = align256(off + dec_slots * p.hw * 2 * sizeof(float));
   const size_t chk_rows = p.nsplit > 1 ? static_cast<size_t>(T - nd) * Hq * p.nsplit : 0;
   p.chk_o = off;  off = align256(off + chk_rows * D * sizeof(float));
   p.chk_ml = off; off = align256(off + chk_rows * 2 * sizeof(float));
-  p.dec_items = off; off = align256(off + static_cast<size_t>(nd) * p.max_parts * 4 * sizeof(int32_t));
-  p.dec_count = off; off = align256(off + (nd > 0 ? sizeof(int32_t) : 0));
+  p.dec_seq = off;  off = align256(off + (nd > 0 ? static_cast<size_t>(nd + 1) * sizeof(int32_t) : 0));
+  p.dec_wave = off; off = align256(off + (nd > 0 ? kMaxDecodeWaves * sizeof(int32_t) : 0));
+  p.dec_par = off;  off = align256(off + (nd > 0 ? 4 * sizeof(int32_t) : 0));
   p.total = off;
   return p;
 }
@@ -112,17 +109,21 @@ struct AttnArgs {
   const int32_t* cu_blocks;
   const int32_t* block_table;
   void* out;
-  float* dec_o;
+  float* dec_o;          // decode partials, slot-major: [slot][hw][D] and [slot][hw][2]
   float* dec_ml;
   float* chk_o;
   float* chk_ml;
-  int4* dec_items;      // decode partitions (s, p, context length, block-table offset)
-  int32_t* dec_count;   // number of decode work items
+  int32_t* dec_seq;      // [nd + 1] first stage of each decode row on the stage line; [nd] = total
+  int32_t* dec_wave;     // [waves] unit holding each wave's first stage
+  int32_t* dec_par;      // [0] total stages S, [1] stages per wave L, [2] waves with work W
   int32_t num_seqs, nd, T, Hq, Hkv, G, bs, bs_shift;
-  int32_t part, max_parts, head_blocks;
+  int32_t head_blocks, hw, ups;
   int32_t bmq, q_blocks, n_chunk, nsplit;
   float scale_log2;
 };
+
+// Decode stages (32 keys) of a row with this many cached-plus-current keys.
+__device__ __forceinline__ int32_t decode_stages(int32_t ctx) { return ctx > 0 ? (ctx + kDecodeKeys - 1) / kDecodeKeys : 0; }
 
 // ---------------------------------------------------------------------------------------------
 // LDS staging.  K and V rows are copied from HBM straight into LDS with the gfx950 16-byte LDS
@@ -348,10 +349,16 @@ template <> struct StageRegs<64> {
 // ---------------------------------------------------------------------------------------------
 // Decode rows.
 // ---------------------------------------------------------------------------------------------
-// Work list: one entry per (decode row, key partition).  A single workgroup scans the partition
-// counts and writes the full partitions (part keys) of all rows first, then each row's shorter
-// last partition, so that the final round of work holds the short items.  It also writes the
-// number of work items (entries x KV heads x 16-head blocks).
+// Work layout: a decode row s with context c has units (KV head g, 16-head block hb), each of
+// decode_stages(c) 32-key stages.  All units of all rows, in order, form one line of S stages;
+// wave w takes stages [w L, (w + 1) L), so every wave has the same work (up to one stage) and
+// a unit is shared by the few consecutive waves whose ranges meet it.  Each (unit, wave) pair
+// yields one partial (m, l, o) in slot unit + wave: both indices grow along the line, so the
+// slot is unique and a unit's partials sit in consecutive slots.
+//
+// The prep workgroup scans the rows' stage counts into dec_seq (first stage of each row), picks
+// L = max(CB_DECODE_MIN_STAGES, ceil(S / waves)) and records the unit holding each wave's first
+// stage.
 __device__ __forceinline__ int32_t block_scan_1024(int32_t v, int32_t* scan) {
   const int tid = threadIdx.x;
   scan[tid] = v;
@@ -365,85 +372,143 @@ __device__ __forceinline__ int32_t block_scan_1024(int32_t v, int32_t* scan) {
   return scan[tid];
 }
 
-__global__ __launch_bounds__(1024) void decode_prep_kernel(AttnArgs a) {
+__global__ __launch_bounds__(1024) void decode_prep_kernel(AttnArgs a, int32_t n_waves) {
   __shared__ int32_t scan[1024];
   __shared__ int32_t carry;
   const int tid = threadIdx.x;
-  for (int pass = 0; pass < 2; ++pass) {
-    if (tid == 0 && pass == 0) carry = 0;
+  if (tid == 0) carry = 0;
+  __syncthreads();
+  for (int32_t base = 0; base < a.nd; base += 1024) {
+    const int32_t s = base + tid;
+    const int32_t n = s < a.nd ? decode_stages(a.ctx_lens[s]) * a.ups : 0;
+    const int32_t incl = block_scan_1024(n, scan);
+    if (s < a.nd) a.dec_seq[s] = carry + incl - n;
+    __syncthreads();                                  // every thread has read carry
+    if (tid == 1023) carry += scan[1023];
     __syncthreads();
-    for (int32_t base = 0; base < a.nd; base += 1024) {
-      const int32_t s = base + tid;
-      int32_t ctx = 0, cub = 0, full = 0, tail = 0;
-      if (s < a.nd) {
-        ctx = max(a.ctx_lens[s], 0);
-        cub = a.cu_blocks[s];
-        full = min(ctx / a.part, a.max_parts);
-        tail = full < a.max_parts && ctx - full * a.part > 0 ? 1 : 0;
-      }
-      const int32_t n = pass == 0 ? full : tail;
-      const int32_t first = carry + block_scan_1024(n, scan) - n;
-      for (int32_t j = 0; j < n; ++j)
-        a.dec_items[first + j] = make_int4(s, pass == 0 ? j : full, ctx, cub);
-      __syncthreads();                                // every thread has read carry
-      if (tid == 1023) carry += scan[1023];
-      __syncthreads();
-    }
   }
-  if (tid == 0) a.dec_count[0] = carry * a.Hkv * a.head_blocks;
+  const int32_t S = carry;
+  const int32_t L = max(CB_DECODE_MIN_STAGES, (S + n_waves - 1) / n_waves);
+  const int32_t W = (S + L - 1) / L;
+  if (tid == 0) {
+    a.dec_seq[a.nd] = S;
+    a.dec_par[0] = S;
+    a.dec_par[1] = L;
+    a.dec_par[2] = W;
+  }
+  __syncthreads();                                    // dec_seq is complete for the workgroup
+  for (int32_t w = tid; w < W; w += 1024) {
+    const int32_t pos = w * L;
+    int32_t lo = 0, hi = a.nd;                        // dec_seq[lo] <= pos < dec_seq[hi]
+    while (hi - lo > 1) {
+      const int32_t mid = (lo + hi) >> 1;
+      if (a.dec_seq[mid] <= pos) lo = mid;
+      else hi = mid;
+    }
+    a.dec_wave[w] = lo * a.ups + (pos - a.dec_seq[lo]) / decode_stages(a.ctx_lens[lo]);
+  }
 }
 
-// Persistent waves: wave b takes work items b, b + n_waves, b + 2 n_waves, ...  Item w is list
-// entry w / (Hkv head_blocks) for KV head g and 16-head block hb.  The next item's query and
-// block ids are loaded right after a copy is issued (so waiting for that copy also covers them),
-// and its first K/V stage is copied during the current item's last stage, so a wave keeps one
-// stage in flight from its first item to its last.
+// Persistent waves, one per stage range.  A wave walks its range as sub-ranges of at most
+// kSubKeys keys inside one unit (block ids of a sub-range are loaded once into LDS); the softmax
+// state carries across sub-ranges of the same unit and is written as a partial at the unit's
+// last one.  The next sub-range's query and block ids are loaded right after a copy is issued
+// (waiting for that copy also covers them) and its first K/V stage is copied during the current
+// sub-range's last stage, so the wave keeps one stage in flight from start to end.
 template <typename T, int D>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 2 : 1))) void decode_kernel(AttnArgs a, const int4* __restrict__ items, const int32_t* __restrict__ count,
-                                                         int32_t n_waves) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 2 : 1))) void decode_kernel(
+    AttnArgs a, const int32_t* __restrict__ seq_start, const int32_t* __restrict__ wave_unit,
+    const int32_t* __restrict__ par, const int32_t* __restrict__ ctx_lens, const int32_t* __restrict__ cu_blocks) {
   constexpr int KS = D / 32;          // 32-slot contraction steps over the head dimension
   constexpr int DT = D / 16;          // 16-dim output tiles
   constexpr int ROW = D * sizeof(T);  // bytes per key row in LDS
   constexpr int RPI = 1024 / ROW;     // key rows per 1 KB copy instruction
   constexpr int NCP = kDecodeKeys / RPI;
-  constexpr int NBR = kMaxPartBlocks / 64;   // block ids per lane of one partition
+  constexpr int NBR = kSubBlocks / 64;   // block ids per lane of one sub-range
   __shared__ __attribute__((aligned(1024))) char sK[kDecodeKeys * ROW];
   __shared__ __attribute__((aligned(1024))) char sV[kDecodeKeys * ROW];
-  __shared__ int32_t sBlk[kMaxPartBlocks];
+  __shared__ int32_t sBlk[kSubBlocks];
+
+  const int32_t S = par[0], L = par[1], W = par[2];   // uniform, read-only here: scalar loads
+  const int32_t w = blockIdx.x;
+  if (w >= W) return;
+  const int32_t pos_end = min(S, (w + 1) * L);
 
   const int lane = threadIdx.x;
   const int32_t col = lane & 15;      // head owned by this lane in S^T / P^T / O^T
   const int32_t grp = lane >> 4;      // slot group
   const int bsh = a.bs_shift;
   const int32_t bmask = (1 << bsh) - 1;
-  const int32_t per_entry = a.Hkv * a.head_blocks;
   const T* q = static_cast<const T*>(a.q);
   const char* kc = static_cast<const char*>(a.k_cache);
   const char* vc = static_cast<const char*>(a.v_cache);
   const int64_t blk_bytes = static_cast<int64_t>(a.Hkv) * ((int64_t)ROW << bsh);
   const int cp_row = lane / (ROW / 16), cp_pos = lane % (ROW / 16);
 
-  struct Item {
-    int32_t s, p, k_lo, k_hi, h0, gh;
-    int64_t head_bytes;
+  // Cursor on the stage line: position pos inside unit u = (row s, unit r of the row), whose
+  // first stage is a_u; n_s stages per unit of row s.
+  struct Cursor {
+    int32_t pos, u, s, r, a_u, n_s, ctx, cub;
   };
-  // Item fields from the work list; block ids of the partition and the query into registers
-  // (consumed later: nothing here waits for them).
-  auto resolve = [&](int32_t wi, int32_t (&blk)[NBR], Frag<T> (&qd)[KS]) {
+  struct Item {
+    int32_t s, cub, k_lo, k_hi, h0, gh, slot;
+    int64_t head_bytes;
+    bool last;                        // last sub-range of its (unit, wave) partial
+  };
+  auto load_row = [&](Cursor& c, int32_t s) {        // first unit of row s
+    c.s = s;
+    c.r = 0;
+    c.ctx = ctx_lens[s];
+    c.n_s = decode_stages(c.ctx);
+    c.cub = cu_blocks[s];
+    c.a_u = seq_start[s];
+    c.u = s * a.ups;
+  };
+  Cursor cur_c;
+  cur_c.pos = w * L;
+  {
+    const int32_t u0 = wave_unit[w];
+    load_row(cur_c, u0 / a.ups);
+    cur_c.r = u0 - cur_c.s * a.ups;
+    cur_c.u = u0;
+    cur_c.a_u += cur_c.r * cur_c.n_s;
+  }
+  // The sub-range at the cursor; moves the cursor past it (to the next non-empty unit when the
+  // unit is finished and the wave's range goes on).
+  auto take = [&](Cursor& c) {
     Item it;
-    const int32_t e = wi / per_entry;
-    const int32_t r = wi - e * per_entry;
-    const int32_t g = r / a.head_blocks;
-    const int32_t hb = r - g * a.head_blocks;
-    const int4 ent = items[e];     // uniform, read-only here: a scalar load
-    it.s = ent.x;
-    it.p = ent.y;
-    it.k_lo = ent.y * a.part;
-    it.k_hi = min(ent.z, it.k_lo + a.part);
+    const int32_t unit_end = c.a_u + c.n_s;
+    const int32_t seg_end = min(pos_end, unit_end);
+    const int32_t sub_end = min(seg_end, c.pos + kSubKeys / kDecodeKeys);
+    const int32_t g = c.r / a.head_blocks;
+    const int32_t hb = c.r - g * a.head_blocks;
+    it.s = c.s;
+    it.cub = c.cub;
+    it.k_lo = (c.pos - c.a_u) * kDecodeKeys;
+    it.k_hi = min((sub_end - c.a_u) * kDecodeKeys, c.ctx);
     it.h0 = g * a.G + 16 * hb;
     it.gh = min(16, a.G - 16 * hb);
+    it.slot = c.u + w;
     it.head_bytes = static_cast<int64_t>(g) * ((int64_t)ROW << bsh);
-    const int32_t* btab = a.block_table + ent.w + (it.k_lo >> bsh);
+    it.last = sub_end == seg_end;
+    c.pos = sub_end;
+    if (c.pos == unit_end && c.pos < pos_end) {
+      if (c.r + 1 < a.ups) {
+        ++c.r;
+        ++c.u;
+        c.a_u = unit_end;
+      } else {
+        int32_t s = c.s + 1;
+        while (decode_stages(ctx_lens[s]) == 0) ++s;   // rows with no keys own no stages
+        load_row(c, s);
+      }
+    }
+    return it;
+  };
+
+  // Block ids of a sub-range and the query into registers (consumed later: no wait here).
+  auto fetch = [&](const Item& it, int32_t (&blk)[NBR], Frag<T> (&qd)[KS]) {
+    const int32_t* btab = a.block_table + it.cub + (it.k_lo >> bsh);
     const int32_t nblk = ((it.k_hi - 1) >> bsh) - (it.k_lo >> bsh) + 1;
 #pragma unroll
     for (int i = 0; i < NBR; ++i)
@@ -454,7 +519,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(sizeof(T) ==
       if (col < it.gh) qd[ks].load(qrow + 32 * ks + 8 * grp);
       else qd[ks].zero();
     }
-    return it;
   };
   auto publish_blocks = [&](const Item& it, const int32_t (&blk)[NBR]) {
     const int32_t nblk = ((it.k_hi - 1) >> bsh) - (it.k_lo >> bsh) + 1;
@@ -463,7 +527,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(sizeof(T) ==
       if (64 * i + lane < nblk) sBlk[64 * i + lane] = blk[i];
   };
   // Copy 32 keys' K and V rows straight into LDS (no registers), chunk-swizzled.  Keys past the
-  // partition repeat its last key; they are masked out of the softmax.
+  // sub-range repeat its last key; they are masked out of the softmax.
   auto issue = [&](const Item& it, int32_t key0) {
     const int32_t b_lo = it.k_lo >> bsh;
 #pragma unroll
@@ -476,28 +540,28 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(sizeof(T) ==
       lds_copy16(vc + off, sV + i * 1024);
     }
   };
-  const int32_t total = count[0];
-  int32_t w = blockIdx.x;
-  if (w >= total) return;
 
   int32_t blk[NBR];
   Frag<T> qf[KS], qn[KS];
-  Item cur = resolve(w, blk, qf);
+  Item cur = take(cur_c);
+  fetch(cur, blk, qf);
   publish_blocks(cur, blk);
   __syncthreads();
   issue(cur, cur.k_lo);
 
+  float m_run = kNegInf, l_run = 0.f;
+  f32x4 o[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
   while (true) {
-    w += n_waves;
-    const bool has_next = w < total;
+    const bool has_next = cur_c.pos < pos_end;
     const bool one_stage = cur.k_hi - cur.k_lo <= kDecodeKeys;
     Item nxt{};
-    if (has_next && one_stage) nxt = resolve(w, blk, qn);
-
-    float m_run = kNegInf, l_run = 0.f;
-    f32x4 o[DT];
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (has_next && one_stage) {
+      nxt = take(cur_c);
+      fetch(nxt, blk, qn);
+    }
 
     for (int32_t key0 = cur.k_lo; key0 < cur.k_hi; key0 += kDecodeKeys) {
       // Operands of this stage into registers (the copy has landed: the compiler waits for it
@@ -513,7 +577,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(sizeof(T) ==
       lds_reads_done();
       if (key0 + kDecodeKeys < cur.k_hi) {
         issue(cur, key0 + kDecodeKeys);
-        if (key0 == cur.k_lo && has_next) nxt = resolve(w, blk, qn);
+        if (key0 == cur.k_lo && has_next) {
+          nxt = take(cur_c);
+          fetch(nxt, blk, qn);
+        }
       } else if (has_next) {
         publish_blocks(nxt, blk);
         issue(nxt, nxt.k_lo);
@@ -558,15 +625,21 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(sizeof(T) ==
       }
     }
 
-    float l_tot = wave_xor_sum(l_run, 16);
-    l_tot = wave_xor_sum(l_tot, 32);
-    if (col < cur.gh) {
-      const int64_t prow = (static_cast<int64_t>(cur.s) * a.Hq + cur.h0 + col) * a.max_parts + cur.p;
-      float* po = a.dec_o + prow * D;
+    if (cur.last) {
+      float l_tot = wave_xor_sum(l_run, 16);
+      l_tot = wave_xor_sum(l_tot, 32);
+      if (col < cur.gh) {
+        const int64_t prow = static_cast<int64_t>(cur.slot) * a.hw + col;
+        float* po = a.dec_o + prow * D;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-        *reinterpret_cast<float4*>(po + 16 * dt + 4 * grp) = make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
-      if (grp == 0) *reinterpret_cast<float2*>(a.dec_ml + 2 * prow) = make_float2(m_run, l_tot);
+        for (int dt = 0; dt < DT; ++dt)
+          *reinterpret_cast<float4*>(po + 16 * dt + 4 * grp) = make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
+        if (grp == 0) *reinterpret_cast<float2*>(a.dec_ml + 2 * prow) = make_float2(m_run, l_tot);
+      }
+      m_run = kNegInf;
+      l_run = 0.f;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     if (!has_next) break;
     cur = nxt;
@@ -851,39 +924,53 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a, int32_t n_dec_
   const int32_t ri = static_cast<int32_t>(w / a.Hq);
   const int32_t h = static_cast<int32_t>(w % a.Hq);
   int32_t row, P;
-  const float* po;
+  const float* po;                      // partial i: o at po + i * so, (m, l) at pml + i * sml
   const float* pml;
+  int64_t so, sml;
   if (ri < n_dec_rows) {
+    // Decode row: the partials of unit u sit in slots u + w for the waves w whose stage ranges
+    // meet the unit's stages [a_u, a_u + n).
     row = ri;
-    P = min((a.ctx_lens[row] + a.part - 1) / a.part, a.max_parts);   // never past the workspace
-    const int64_t base = (static_cast<int64_t>(row) * a.Hq + h) * a.max_parts;
+    const int32_t n = decode_stages(a.ctx_lens[row]);
+    const int32_t g = h / a.G, hh = h - g * a.G;
+    const int32_t r = g * a.head_blocks + (hh >> 4);
+    const int32_t u = row * a.ups + r;
+    const int32_t L = a.dec_par[1];
+    const int32_t a_u = a.dec_seq[row] + r * n;
+    const int32_t w0 = a_u / L;
+    P = n > 0 ? (a_u + n - 1) / L - w0 + 1 : 0;
+    const int64_t base = static_cast<int64_t>(u + w0) * a.hw + (hh & 15);
     po = a.dec_o + base * D;
     pml = a.dec_ml + base * 2;
+    so = static_cast<int64_t>(a.hw) * D;
+    sml = 2 * a.hw;
   } else {
     row = a.nd + (ri - n_dec_rows);
     P = a.nsplit;
     const int64_t base = (static_cast<int64_t>(row - a.nd) * a.Hq + h) * a.nsplit;
     po = a.chk_o + base * D;
     pml = a.chk_ml + base * 2;
+    so = D;
+    sml = 2;
   }
   // Lanes read the partials' (m, l) pairs side by side; butterfly reductions give every lane the
   // same maximum and total in the same order on every run.
   float m = kNegInf;
-  for (int32_t i = lane; i < P; i += 64) m = fmaxf(m, pml[2 * i]);
+  for (int32_t i = lane; i < P; i += 64) m = fmaxf(m, pml[i * sml]);
 #pragma unroll
   for (int x = 32; x >= 1; x >>= 1) m = wave_xor_max(m, x);
   const float m_use = m == kNegInf ? 0.f : m;
-  float L = 0.f;
-  for (int32_t i = lane; i < P; i += 64) L += exp2f(pml[2 * i] - m_use) * pml[2 * i + 1];
+  float Lsum = 0.f;
+  for (int32_t i = lane; i < P; i += 64) Lsum += exp2f(pml[i * sml] - m_use) * pml[i * sml + 1];
 #pragma unroll
-  for (int x = 32; x >= 1; x >>= 1) L = wave_xor_sum(L, x);
-  const float inv = L > 0.f ? 1.f / L : 0.f;
+  for (int x = 32; x >= 1; x >>= 1) Lsum = wave_xor_sum(Lsum, x);
+  const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
   float acc[PER];
 #pragma unroll
   for (int j = 0; j < PER; ++j) acc[j] = 0.f;
   for (int32_t base = 0; base < P; base += 64) {
     const int32_t i = base + lane;
-    const float wl = i < P ? exp2f(pml[2 * i] - m_use) * inv : 0.f;
+    const float wl = i < P ? exp2f(pml[i * sml] - m_use) * inv : 0.f;
     const int32_t n = min(64, P - base);
     int32_t k = 0;
     for (; k + 8 <= n; k += 8) {              // eight partials' loads in flight together
@@ -891,7 +978,7 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a, int32_t n_dec_
 #pragma unroll
       for (int u = 0; u < 8; ++u)
 #pragma unroll
-        for (int j = 0; j < PER; ++j) x[u][j] = po[static_cast<int64_t>(base + k + u) * D + lane + 64 * j];
+        for (int j = 0; j < PER; ++j) x[u][j] = po[(base + k + u) * so + lane + 64 * j];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const float wk = __shfl(wl, k + u, 64);
@@ -901,7 +988,7 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a, int32_t n_dec_
     }
     for (; k < n; ++k) {
       const float wk = __shfl(wl, k, 64);
-      const float* pk = po + static_cast<int64_t>(base + k) * D + lane;
+      const float* pk = po + (base + k) * so + lane;
 #pragma unroll
       for (int j = 0; j < PER; ++j) acc[j] += wk * pk[64 * j];
     }
@@ -940,14 +1027,12 @@ int launch_all(hipStream_t st, const AttnArgs& a, const Plan& p, void* const* ev
     if (events && events[i]) (void)hipEventRecord(static_cast<hipEvent_t>(events[i]), st);
   };
   if (a.nd > 0) {
-    const int64_t upper = static_cast<int64_t>(a.nd) * a.max_parts * a.Hkv * a.head_blocks;
-    if (upper > 0x7fff0000) return CB_ERR_INVALID;    // item indices + one stride stay in int32
-    decode_prep_kernel<<<dim3(1), dim3(1024), 0, st>>>(a);
+    const int32_t n_waves = std::min(kMaxDecodeWaves, CB_DECODE_WAVES_PER_CU * compute_units(st));
+    decode_prep_kernel<<<dim3(1), dim3(1024), 0, st>>>(a, n_waves);
     if (hipGetLastError() != hipSuccess) return CB_ERR_HIP;
-    const int64_t n_waves = std::min<int64_t>(upper, static_cast<int64_t>(CB_DECODE_WAVES_PER_CU) * compute_units(st));
     rec(0);
     decode_kernel<T, D><<<dim3(static_cast<uint32_t>(n_waves)), dim3(64), 0, st>>>(
-        a, a.dec_items, a.dec_count, static_cast<int32_t>(n_waves));
+        a, a.dec_seq, a.dec_wave, a.dec_par, a.ctx_lens, a.cu_blocks);
     if (hipGetLastError() != hipSuccess) return CB_ERR_HIP;
     rec(1);
   }
@@ -985,6 +1070,10 @@ bool valid_shape(int32_t num_seqs, int32_t nd, int32_t T, int32_t max_q_len, int
   if (max_q_len < 0 || max_dctx < 0 || max_ctx < 0) return false;
   if (num_seqs > nd && (max_q_len < 1 || max_ctx < 1)) return false;
   if (nd > 0 && max_dctx < 1) return false;
+  // Decode stage positions (and one wave's range past them) must stay in int32.
+  const int64_t units = static_cast<int64_t>(nd) * Hkv * ((Hq / Hkv + 15) / 16);
+  if (units * ((static_cast<int64_t>(max_dctx) + kDecodeKeys - 1) / kDecodeKeys) > 0x7fff0000 - (int64_t)kMaxDecodeWaves * 2)
+    return false;
   return true;
 }
 
@@ -996,7 +1085,7 @@ extern "C" size_t cb_attn_workspace_bytes(int32_t num_seqs, int32_t num_decodes,
                                           int32_t max_ctx, int32_t Hq, int32_t Hkv, int32_t D) {
   if (!cb::valid_shape(num_seqs, num_decodes, T, max_q_len, max_decode_ctx, max_ctx, Hq, Hkv, D))
     return 0;
-  return cb::make_plan(num_seqs, num_decodes, T, max_q_len, max_decode_ctx, max_ctx, Hq, Hkv, D).total;
+  return cb::make_plan(num_seqs, num_decodes, T, max_q_len, max_ctx, Hq, Hkv, D).total;
 }
 
 extern "C" int cb_mixed_paged_attention_timed(
@@ -1019,7 +1108,7 @@ extern "C" int cb_mixed_paged_attention_timed(
   const void* ptrs[] = {q, k_cache, v_cache, out};
   for (const void* p : ptrs)
     if (!aligned16(p)) return CB_ERR_INVALID;
-  const Plan p = make_plan(num_seqs, num_decodes, T, max_q_len, max_decode_ctx, max_ctx, Hq, Hkv, D);
+  const Plan p = make_plan(num_seqs, num_decodes, T, max_q_len, max_ctx, Hq, Hkv, D);
   if (p.total > 0 && (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u))) return CB_ERR_INVALID;
   if (workspace_bytes < p.total) return CB_ERR_CAPACITY;
 
@@ -1032,12 +1121,13 @@ extern "C" int cb_mixed_paged_attention_timed(
   a.dec_ml = reinterpret_cast<float*>(ws + p.dec_ml);
   a.chk_o = reinterpret_cast<float*>(ws + p.chk_o);
   a.chk_ml = reinterpret_cast<float*>(ws + p.chk_ml);
-  a.dec_items = reinterpret_cast<int4*>(ws + p.dec_items);
-  a.dec_count = reinterpret_cast<int32_t*>(ws + p.dec_count);
+  a.dec_seq = reinterpret_cast<int32_t*>(ws + p.dec_seq);
+  a.dec_wave = reinterpret_cast<int32_t*>(ws + p.dec_wave);
+  a.dec_par = reinterpret_cast<int32_t*>(ws + p.dec_par);
   a.num_seqs = num_seqs; a.nd = num_decodes; a.T = T; a.Hq = Hq; a.Hkv = Hkv; a.G = p.G;
   a.bs = block_size;
   a.bs_shift = __builtin_ctz(static_cast<unsigned>(block_size));
-  a.part = p.part; a.max_parts = std::max(p.max_parts, 1); a.head_blocks = p.head_blocks;
+  a.head_blocks = p.head_blocks; a.hw = p.hw; a.ups = p.ups;
   a.bmq = p.bmq; a.q_blocks = p.q_blocks; a.n_chunk = p.n_chunk; a.nsplit = p.nsplit;
   a.scale_log2 = scale * 1.4426950408889634f;
 

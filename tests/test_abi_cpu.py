@@ -229,8 +229,12 @@ def test_workspace_grows_with_context_and_rows():
     a = f(65, 64, 512, 448, 4097, 4097, 32, 32, 128)
     b = f(129, 128, 576, 448, 4097, 4097, 32, 32, 128)
     assert 0 < a < b
-    # decode partitions grow to at most 4096 keys: ceil(300000 / 4096) = 74 partials per head,
-    # plus a 16-byte work-list entry per partition and the queue counter
-    assert f(2, 1, 2, 1, 300000, 300000, 8, 8, 128) <= (74 * 8 * 130 * 4 + 8 * 8 * 130 * 4 + 74 * 16
-                                                        + 6 * 256)
+    # Decode partials: one slot per (unit, wave) pair, at most units + 8192 waves slots of
+    # min(16, G) heads x (D + 2) floats, whatever the context length; plus the row stage offsets,
+    # the per-wave start units and four parameters (each region 256-byte aligned).
+    one_row = f(1, 1, 1, 1, 300000, 300000, 8, 8, 128)
+    assert one_row == f(1, 1, 1, 1, 3000, 3000, 8, 8, 128)
+    assert one_row <= (8 + 8192) * 1 * 130 * 4 + 2 * 4 + 8192 * 4 + 16 + 5 * 256
+    gqa = f(4, 4, 4, 1, 5000, 5000, 56, 8, 128)        # group of 7 heads per unit
+    assert gqa <= (4 * 8 + 8192) * 7 * 130 * 4 + 5 * 4 + 8192 * 4 + 16 + 5 * 256
     assert f(0, 0, 0, 0, 0, 0, 32, 32, 128) == 0
