@@ -92,6 +92,14 @@ def isolation_pass(g, metas, qrots, outs, w, reps: int):
         h = meta.host
         dev = {kk: vv.to(g.device) for kk, vv in h.items()}
         cu_chunk = (dev["cu_seqlens_q"][nd:] - nd).contiguous()
+        # Each launch shape plans its own split (a chunk-only launch splits keys further).
+        Hq, Hkv, D = g.runner.Hq, g.runner.Hkv, g.runner.D
+        need = [cb.cb_attn_workspace_bytes(nd, nd, nd, 1, meta.max_decode_context_len,
+                                           meta.max_decode_context_len, Hq, Hkv, D)]
+        if T > nd:
+            need.append(cb.cb_attn_workspace_bytes(meta.num_seqs - nd, 0, T - nd, meta.max_q_len, 0,
+                                                   meta.max_context_len, Hq, Hkv, D))
+        g.runner.ensure_workspace(max(need))
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
         for e in ev:
             e.record()

@@ -36,10 +36,16 @@ namespace {
 #define CB_DECODE_MIN_STAGES 8        // shortest decode stage range per wave (32-key stages)
 #endif
 #ifndef CB_CHUNK_MIN_TILES
-#define CB_CHUNK_MIN_TILES 512        // split chunk keys until at least this many tiles
+#define CB_CHUNK_MIN_TILES 512        // split chunk keys until at least this many tiles (no decodes)
 #endif
-#ifndef CB_DECODE_WAVES_PER_CU
-#define CB_DECODE_WAVES_PER_CU 8      // resident decode waves per compute unit (LDS-limited)
+#ifndef CB_CHUNK_MIN_TILES_MIXED
+#define CB_CHUNK_MIN_TILES_MIXED 256  // the same beside decode rows (one workgroup slot per CU)
+#endif
+#ifndef CB_DECODE_WG_PER_CU
+#define CB_DECODE_WG_PER_CU 2         // four-wave decode workgroups per CU without chunk tiles
+#endif
+#ifndef CB_DECODE_WG_PER_CU_MIXED
+#define CB_DECODE_WG_PER_CU_MIXED 1   // the same beside chunk tiles
 #endif
 
 constexpr int kChunkRows = 128;   // rows per chunk tile: 4 waves x 32
@@ -82,7 +88,8 @@ Plan make_plan(int32_t num_seqs, int32_t nd, int32_t T, int32_t max_q_len, int32
   if (p.n_chunk > 0) {
     p.q_blocks = (std::max(max_q_len, 1) + p.bmq - 1) / p.bmq;
     const int64_t tiles = static_cast<int64_t>(p.n_chunk) * p.q_blocks * Hkv;
-    while (p.nsplit < kMaxSplit && tiles * p.nsplit < CB_CHUNK_MIN_TILES &&
+    const int64_t min_tiles = nd > 0 ? CB_CHUNK_MIN_TILES_MIXED : CB_CHUNK_MIN_TILES;
+    while (p.nsplit < kMaxSplit && tiles * p.nsplit < min_tiles &&
            max_ctx / (2 * p.nsplit) >= 2 * kChunkKeys)
       p.nsplit *= 2;
   }
@@ -415,26 +422,34 @@ __global__ __launch_bounds__(1024) void decode_prep_kernel(AttnArgs a, int32_t n
 // last one.  The next sub-range's query and block ids are loaded right after a copy is issued
 // (waiting for that copy also covers them) and its first K/V stage is copied during the current
 // sub-range's last stage, so the wave keeps one stage in flight from start to end.
+// LDS of one decode wave: a K stage, a V stage and the sub-range's block ids.
 template <typename T, int D>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 2 : 1))) void decode_kernel(
-    AttnArgs a, const int32_t* __restrict__ seq_start, const int32_t* __restrict__ wave_unit,
-    const int32_t* __restrict__ par, const int32_t* __restrict__ ctx_lens, const int32_t* __restrict__ cu_blocks) {
+struct DecodeLds {
+  static constexpr int ROW = D * sizeof(T);
+  static constexpr int V = kDecodeKeys * ROW;
+  static constexpr int BLK = 2 * kDecodeKeys * ROW;
+  static constexpr int BYTES = BLK + kSubBlocks * 4;
+  static_assert(BYTES % 1024 == 0, "wave slices keep 1 KB alignment");
+};
+
+template <typename T, int D>
+__device__ __forceinline__ void decode_wave(const AttnArgs& a, const int32_t* seq_start, const int32_t* wave_unit,
+                                            const int32_t* par, const int32_t* ctx_lens, const int32_t* cu_blocks,
+                                            int32_t w, int lane, char* lds) {
   constexpr int KS = D / 32;          // 32-slot contraction steps over the head dimension
   constexpr int DT = D / 16;          // 16-dim output tiles
   constexpr int ROW = D * sizeof(T);  // bytes per key row in LDS
   constexpr int RPI = 1024 / ROW;     // key rows per 1 KB copy instruction
   constexpr int NCP = kDecodeKeys / RPI;
   constexpr int NBR = kSubBlocks / 64;   // block ids per lane of one sub-range
-  __shared__ __attribute__((aligned(1024))) char sK[kDecodeKeys * ROW];
-  __shared__ __attribute__((aligned(1024))) char sV[kDecodeKeys * ROW];
-  __shared__ int32_t sBlk[kSubBlocks];
+  char* sK = lds;
+  char* sV = lds + DecodeLds<T, D>::V;
+  int32_t* sBlk = reinterpret_cast<int32_t*>(lds + DecodeLds<T, D>::BLK);
 
   const int32_t S = par[0], L = par[1], W = par[2];   // uniform, read-only here: scalar loads
-  const int32_t w = blockIdx.x;
   if (w >= W) return;
   const int32_t pos_end = min(S, (w + 1) * L);
 
-  const int lane = threadIdx.x;
   const int32_t col = lane & 15;      // head owned by this lane in S^T / P^T / O^T
   const int32_t grp = lane >> 4;      // slot group
   const int bsh = a.bs_shift;
@@ -545,8 +560,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(sizeof(T) ==
   Frag<T> qf[KS], qn[KS];
   Item cur = take(cur_c);
   fetch(cur, blk, qf);
-  publish_blocks(cur, blk);
-  __syncthreads();
+  publish_blocks(cur, blk);          // LDS operations of one wave complete in order
   issue(cur, cur.k_lo);
 
   float m_run = kNegInf, l_run = 0.f;
@@ -662,25 +676,31 @@ __device__ __forceinline__ void store4<float>(float* dst, float x0, float x1, fl
   *reinterpret_cast<float4*>(dst) = make_float4(x0, x1, x2, x3);
 }
 
+// LDS of one chunk tile: the K and V stage rings and a block-id window.
 template <typename T, int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 2 : 1))) void chunk_kernel(AttnArgs a, int32_t n_tiles, int32_t per_xcd) {
+struct ChunkLds {
+  static constexpr int ROW = D * sizeof(T);
+  static constexpr int NS = sizeof(T) == 2 ? kChunkStages : 2;   // float stages are twice as large
+  static constexpr int STAGE = kChunkKeys * ROW;
+  static constexpr int V = NS * STAGE;
+  static constexpr int BLK = 2 * NS * STAGE;
+  static constexpr int BYTES = BLK + kBlockWindow * 4;
+};
+
+template <typename T, int D>
+__device__ __forceinline__ void chunk_tile(const AttnArgs& a, int32_t tile, char* lds) {
   constexpr int KS = D / 16;          // 16-slot contraction steps over the head dimension
   constexpr int MT = D / 32;          // 32-dim output tiles
   constexpr int ROW = D * sizeof(T);  // bytes per key row in LDS
   constexpr int RPI = 1024 / ROW;     // key rows per 1 KB copy instruction
   constexpr int NCPW = kChunkKeys / RPI / 4;    // copy instructions per wave per tensor
   constexpr int CPW = 2 * NCPW;                 // copy instructions per wave per stage
-  constexpr int NS = sizeof(T) == 2 ? kChunkStages : 2;   // float stages are twice as large
-  constexpr int STAGE = kChunkKeys * ROW;       // bytes of K (and of V) per stage
-  __shared__ __attribute__((aligned(1024))) char sK[NS * STAGE];
-  __shared__ __attribute__((aligned(1024))) char sV[NS * STAGE];
-  __shared__ int32_t sBlk[kBlockWindow];       // a window of the sequence's block table
+  constexpr int NS = ChunkLds<T, D>::NS;
+  constexpr int STAGE = ChunkLds<T, D>::STAGE;  // bytes of K (and of V) per stage
+  char* sK = lds;
+  char* sV = lds + ChunkLds<T, D>::V;
+  int32_t* sBlk = reinterpret_cast<int32_t*>(lds + ChunkLds<T, D>::BLK);   // block-table window
 
-  // XCD-aware order: workgroup b runs on XCD b % 8; give each XCD a contiguous run of logical
-  // tiles so that the tiles sharing one (chunk, KV head) K/V stream share that XCD's L2.
-  const int32_t bid = blockIdx.x;
-  const int32_t tile = (bid & 7) * per_xcd + (bid >> 3);
-  if (tile >= n_tiles) return;
   int32_t t = tile;
   const int32_t sp = t % a.nsplit; t /= a.nsplit;
   const int32_t qb = t % a.q_blocks; t /= a.q_blocks;
@@ -913,6 +933,38 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) =
 }
 
 // ---------------------------------------------------------------------------------------------
+// One launch for both row kinds: workgroups [0, n_dec_wg) hold four independent decode waves
+// each (waves 4 b .. 4 b + 3 of the stage split), the rest are chunk tiles.  The decode
+// workgroups are dispatched first and stay for the whole decode split, so chunk tiles run on the
+// compute units' other workgroup slots while the decode waves stream the cache.
+// ---------------------------------------------------------------------------------------------
+template <typename T, int D>
+constexpr int attn_lds_bytes() {
+  return 4 * DecodeLds<T, D>::BYTES > ChunkLds<T, D>::BYTES ? 4 * DecodeLds<T, D>::BYTES : ChunkLds<T, D>::BYTES;
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 2 : 1))) void attn_kernel(
+    AttnArgs a, const int32_t* __restrict__ seq_start, const int32_t* __restrict__ wave_unit,
+    const int32_t* __restrict__ par, const int32_t* __restrict__ ctx_lens, const int32_t* __restrict__ cu_blocks,
+    int32_t n_dec_wg, int32_t n_tiles, int32_t per_xcd) {
+  __shared__ __attribute__((aligned(1024))) char lds[attn_lds_bytes<T, D>()];
+  const int32_t b = blockIdx.x;
+  if (b < n_dec_wg) {
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+    decode_wave<T, D>(a, seq_start, wave_unit, par, ctx_lens, cu_blocks, 4 * b + wave,
+                      static_cast<int>(threadIdx.x & 63), lds + wave * DecodeLds<T, D>::BYTES);
+  } else {
+    // XCD-aware order: workgroup b runs on XCD b % 8 (n_dec_wg is a multiple of 8); each XCD
+    // gets a contiguous run of logical tiles, so the tiles sharing one (chunk, KV head) K/V
+    // stream share that XCD's L2.
+    const int32_t cb = b - n_dec_wg;
+    const int32_t tile = (cb & 7) * per_xcd + (cb >> 3);
+    if (tile < n_tiles) chunk_tile<T, D>(a, tile, lds);
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
 // Merge of split partials: m = max m_p, w_p = 2^(m_p - m), out = sum w_p o_p / sum w_p l_p.
 // ---------------------------------------------------------------------------------------------
 template <typename T, int D>
@@ -1018,32 +1070,33 @@ int compute_units(hipStream_t st) {
   return cached[dev];
 }
 
-// Decode work list, decode split, chunk tiles and combine in order on the caller's stream.
-// (Running the chunk kernel on a second stream beside the decode split was measured slower: the
-// cross-queue join before the combine cost more than the overlap saved.)
+// Decode stage split (prep), the attention kernel (decode waves and chunk tiles together) and the
+// combine, in order on the caller's stream.
 template <typename T, int D>
 int launch_all(hipStream_t st, const AttnArgs& a, const Plan& p, void* const* events) {
   auto rec = [&](int i) {
     if (events && events[i]) (void)hipEventRecord(static_cast<hipEvent_t>(events[i]), st);
   };
+  // Decode workgroups: one per compute unit beside chunk tiles, two when there are none.
+  int32_t n_dec_wg = 0;
   if (a.nd > 0) {
-    const int32_t n_waves = std::min(kMaxDecodeWaves, CB_DECODE_WAVES_PER_CU * compute_units(st));
-    decode_prep_kernel<<<dim3(1), dim3(1024), 0, st>>>(a, n_waves);
+    const int cus8 = (compute_units(st) + 7) / 8 * 8;
+    n_dec_wg = std::min(kMaxDecodeWaves / 4, (a.n_chunk > 0 ? CB_DECODE_WG_PER_CU_MIXED : CB_DECODE_WG_PER_CU) * cus8);
+    decode_prep_kernel<<<dim3(1), dim3(1024), 0, st>>>(a, 4 * n_dec_wg);
     if (hipGetLastError() != hipSuccess) return CB_ERR_HIP;
+  }
+  const int64_t n_tiles = a.n_chunk > 0 ? static_cast<int64_t>(a.n_chunk) * a.q_blocks * a.Hkv * a.nsplit : 0;
+  const int64_t per_xcd = (n_tiles + 7) / 8;
+  const int64_t grid = n_dec_wg + per_xcd * 8;
+  if (grid > 0x7fffffff) return CB_ERR_INVALID;
+  if (grid > 0) {
     rec(0);
-    decode_kernel<T, D><<<dim3(static_cast<uint32_t>(n_waves)), dim3(64), 0, st>>>(
-        a, a.dec_seq, a.dec_wave, a.dec_par, a.ctx_lens, a.cu_blocks);
+    rec(2);
+    attn_kernel<T, D><<<dim3(static_cast<uint32_t>(grid)), dim3(256), 0, st>>>(
+        a, a.dec_seq, a.dec_wave, a.dec_par, a.ctx_lens, a.cu_blocks, n_dec_wg,
+        static_cast<int32_t>(n_tiles), static_cast<int32_t>(per_xcd));
     if (hipGetLastError() != hipSuccess) return CB_ERR_HIP;
     rec(1);
-  }
-  if (a.n_chunk > 0) {
-    const int64_t n_tiles = static_cast<int64_t>(a.n_chunk) * a.q_blocks * a.Hkv * a.nsplit;
-    const int64_t per_xcd = (n_tiles + 7) / 8;
-    if (per_xcd * 8 > 0x7fffffff) return CB_ERR_INVALID;
-    rec(2);
-    chunk_kernel<T, D><<<dim3(static_cast<uint32_t>(per_xcd * 8)), dim3(256), 0, st>>>(
-        a, static_cast<int32_t>(n_tiles), static_cast<int32_t>(per_xcd));
-    if (hipGetLastError() != hipSuccess) return CB_ERR_HIP;
     rec(3);
   }
   const int32_t n_chunk_rows = a.nsplit > 1 ? a.T - a.nd : 0;
