@@ -180,9 +180,12 @@ int cb_rope_kv_append(void* stream, int32_t dtype, int32_t T, int32_t Hq, int32_
  * block_size in {8, 16, 32, 64, 128, 256}.
  *
  * workspace: device memory of at least cb_attn_workspace_bytes(...) bytes for the same
- * arguments (float32 partial results of split-context work), 256-byte aligned; CB_ERR_CAPACITY
- * if workspace_bytes is smaller.  Calls that share a workspace must not overlap in time.
- * Execution: three kernels in order on the stream (decode split, chunk tiles, combine).
+ * arguments (float32 partial results of split-context work and the decode work split),
+ * 256-byte aligned; CB_ERR_CAPACITY if workspace_bytes is smaller.  Calls that share a
+ * workspace must not overlap in time.  Its size does not grow with decode context lengths.
+ * Execution: up to three kernels in order on the stream: the decode work split (one
+ * workgroup, only with decode rows), the attention kernel (decode waves and chunk tiles in one
+ * launch) and the combine (only when some row's work was split).
  * Layouts (device): q, out [T, Hq, D]; caches as above; cu_seqlens_q, cu_blocks [num_seqs + 1];
  * context_lens [num_seqs]; block_table [cu_blocks[num_seqs]].  out must not overlap q.
  * ------------------------------------------------------------------------------------------- */
@@ -200,9 +203,9 @@ int cb_mixed_paged_attention(void* stream, int32_t dtype, int32_t num_seqs, int3
                              void* workspace, size_t workspace_bytes);
 
 /* The same operation, recording caller-created HIP events (hipEvent_t, passed as void*) on the
- * stream around its kernels for timing: events[0] / events[1] before / after the decode kernel,
- * events[2] / events[3] before / after the chunk kernel, events[4] / events[5] before / after
- * the combine kernel.  events may be NULL and any entry may be NULL. */
+ * stream around its kernels for timing: events[0] / events[1] and events[2] / events[3] before /
+ * after the attention kernel (decode and chunk rows share it), events[4] / events[5] before /
+ * after the combine kernel.  events may be NULL and any entry may be NULL. */
 int cb_mixed_paged_attention_timed(void* stream, int32_t dtype, int32_t num_seqs,
                                    int32_t num_decodes, int32_t T, int32_t max_q_len,
                                    int32_t max_decode_ctx, int32_t max_ctx, int32_t Hq,
