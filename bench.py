@@ -245,10 +245,18 @@ def main():
         return meta.num_tokens, k
 
     if args.calib_copy_mib:
-        src = torch.ones(args.calib_copy_mib << 19, dtype=torch.bfloat16, device=dev)
+        # One device-to-device hipMemcpyAsync (the runtime's copy kernel) of a known size.
+        import ctypes
+        hip = ctypes.CDLL("libamdhip64.so")
+        nbytes = args.calib_copy_mib << 20
+        src = torch.ones(nbytes // 2, dtype=torch.bfloat16, device=dev)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
-        dst.copy_(src)
+        rc = hip.hipMemcpyAsync(ctypes.c_void_p(dst.data_ptr()), ctypes.c_void_p(src.data_ptr()),
+                                ctypes.c_size_t(nbytes), ctypes.c_int(3),   # hipMemcpyDeviceToDevice
+                                ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"hipMemcpyAsync failed: {rc}")
         torch.cuda.synchronize()
         del src, dst
     for _ in range(args.warmup):
