@@ -39,7 +39,7 @@ namespace {
 #define CB_CHUNK_MIN_TILES 512        // split chunk keys until at least this many tiles (no decodes)
 #endif
 #ifndef CB_CHUNK_MIN_TILES_MIXED
-#define CB_CHUNK_MIN_TILES_MIXED 256  // the same beside decode rows (one workgroup slot per CU)
+#define CB_CHUNK_MIN_TILES_MIXED 128  // the same beside decode rows, whose streaming covers long tiles
 #endif
 #ifndef CB_DECODE_WG_PER_CU
 #define CB_DECODE_WG_PER_CU 2         // four-wave decode workgroups per CU without chunk tiles
