@@ -61,6 +61,7 @@ EXPORTS = {
     "cb_sched_pending_prompts": (ctypes.c_int, [_vp, _pi32]),
     "cb_sched_free_blocks": (ctypes.c_int, [_vp, _pi32]),
     "cb_build_step": (ctypes.c_int, [_vp, _i32, ctypes.POINTER(cb_step)]),
+    "cb_copy_host_to_device": (ctypes.c_int, [_vp, _vp, _vp, _sz]),
     "cb_rope_cos_sin": (ctypes.c_int, [ctypes.POINTER(ctypes.c_float), _i32, _i32, _f64]),
     "cb_rope_kv_append": (ctypes.c_int, [_vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp,
                                          _vp, _vp, _vp, _i32, _vp, _vp, _vp, _i64]),
@@ -254,6 +255,16 @@ def cb_rope_cos_sin(max_pos: int, D: int, base: float = 10000.0) -> torch.Tensor
 
 
 # ---- device ops ----------------------------------------------------------------------------------
+
+def cb_copy_host_to_device(src, dst, stream=None):
+    """src: pinned host tensor; dst: device tensor of at least as many bytes (kernel copy on the
+    stream, no copy engine)."""
+    nbytes = src.numel() * src.element_size()
+    if not src.is_pinned() or dst.numel() * dst.element_size() < nbytes:
+        raise ValueError("cb_copy_host_to_device: src must be pinned and dst large enough")
+    _check(_lib().cb_copy_host_to_device(_stream(dst, stream), _ptr(src), _ptr(dst), nbytes),
+           "cb_copy_host_to_device")
+
 
 def cb_rope_kv_append(q, k, v, positions, slot_mapping, cos_sin, q_out, k_cache, v_cache,
                       stream=None):

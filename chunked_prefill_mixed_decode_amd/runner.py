@@ -1,4 +1,4 @@
-"""One mixed step on one GPU: build (C++), one metadata copy, rope + append, attention.
+"""One mixed step on one GPU: build (C++), metadata pull (kernel), rope + append, attention.
 
 ``MixedStepRunner`` owns the device side of a serving layer for one head geometry: the paged
 K/V caches (``[num_blocks, Hkv, block_size, D]``), the rotary table, a ring of two pinned
@@ -33,15 +33,13 @@ class MixedStepRunner:
             self.k_cache.view(ity).fill_(SENTINEL_BITS[dtype])
             self.v_cache.view(ity).fill_(SENTINEL_BITS[dtype])
         self.cos_sin = cb.cb_rope_cos_sin(max_pos, D, rope_base).to(self.device)
-        # Two pinned host buffers and two device buffers.  Step n's metadata is copied on a copy
-        # stream while step n-1 still computes; the compute stream waits for that copy, and the
-        # copy of step n+2 into the same device buffer waits for step n's kernels.
+        # Two pinned host buffers and two device buffers.  Step n's metadata is pulled onto the
+        # device by a kernel on the compute stream (so device buffer i is rewritten in stream
+        # order); host buffer i is rewritten (step n + 2) only after that kernel has finished.
         self.bufs = [cb.StepBuffers(cap_seqs, cap_tokens, cap_blocks) for _ in range(2)]
         self.dev_flat = [torch.empty_like(b.flat, device=self.device) for b in self.bufs]
-        self.copied = [None, None]                 # copy out of host buffer i finished
-        self.consumed = [None, None]               # kernels reading device buffer i finished
+        self.copied = [None, None]                 # kernel reading host buffer i finished
         self.ring = 0
-        self.copy_stream = torch.cuda.Stream(device=self.device)
         self.workspace = torch.empty(0, dtype=torch.uint8, device=self.device)
 
     # ---- host builder + metadata copy ----------------------------------------------------------
@@ -56,26 +54,16 @@ class MixedStepRunner:
         return meta
 
     def upload(self, meta: cb.StepMeta) -> dict:
-        """One asynchronous host-to-device copy of the step's metadata on the copy stream; the
-        current stream waits for it.  Returns device int32 views."""
+        """cb_copy_host_to_device of the step's metadata on the current stream (a kernel, so the
+        kernels that follow need no cross-queue wait).  Returns device int32 views."""
         i = meta.buf_index
         buf, dev = self.bufs[i], self.dev_flat[i]
-        compute = torch.cuda.current_stream(self.device)
-        with torch.cuda.stream(self.copy_stream):
-            if self.consumed[i] is not None:
-                self.copy_stream.wait_event(self.consumed[i])
-            dev.copy_(buf.flat, non_blocking=True)
-            ev = torch.cuda.Event()
-            ev.record(self.copy_stream)
-        self.copied[i] = ev
-        compute.wait_event(ev)
-        return {k: dev[buf.offsets[k]:buf.offsets[k] + n] for k, n in meta.lengths().items()}
-
-    def release(self, meta: cb.StepMeta):
-        """Mark the end of the kernels that read this step's device metadata."""
+        stream = torch.cuda.current_stream(self.device)
+        cb.cb_copy_host_to_device(buf.flat, dev, stream=stream)
         ev = torch.cuda.Event()
-        ev.record(torch.cuda.current_stream(self.device))
-        self.consumed[meta.buf_index] = ev
+        ev.record(stream)
+        self.copied[i] = ev
+        return {k: dev[buf.offsets[k]:buf.offsets[k] + n] for k, n in meta.lengths().items()}
 
     # ---- device work ---------------------------------------------------------------------------
     def append(self, dev: dict, q, k, v, q_out):
@@ -105,4 +93,3 @@ class MixedStepRunner:
             num_seqs=meta.num_seqs, num_decodes=meta.num_decodes, max_q_len=meta.max_q_len,
             max_decode_ctx=meta.max_decode_context_len, max_ctx=meta.max_context_len,
             scale=self.scale, events=events)
-        self.release(meta)

@@ -121,6 +121,16 @@ typedef struct {
  * needed sizes are then stored in cap_seqs / cap_tokens / cap_blocks), CB_ERR_INVALID. */
 int cb_build_step(cb_sched* s, int32_t token_budget, cb_step* out);
 
+/* Step metadata to the device (device work on the stream).  [P3] §06: the round's rows and
+ * sequences carry these arrays; the builder writes them into host memory once per step.  Copies
+ * nbytes from src, pinned host memory (hipHostMalloc, e.g. a pinned torch tensor), to dst, device
+ * memory, with a kernel on the stream -- no copy engine, so the consumers on the same stream need
+ * no cross-queue wait.  The kernel reads src with system-scope loads (no GPU caching), so src may
+ * be rewritten once the copy has completed (e.g. after an event recorded behind it).  src, dst
+ * and nbytes must be multiples of 8; CB_ERR_INVALID when they are not or when src is not pinned
+ * host memory; CB_ERR_HIP when the launch fails. */
+int cb_copy_host_to_device(void* stream, const void* src, void* dst, size_t nbytes);
+
 /* ---------------------------------------------------------------------------------------------
  * Rotary table (host).  [P3] §07: the rotary phase follows the absolute position, so a chunk's
  * rows must not restart at 0.  The variant is this library's reading (the pages fix none):

@@ -301,3 +301,20 @@ def test_rope_append_skips_invalid_rows(dev):
     written = (kb != -1).any(dim=-1)            # [nb, Hkv, bs]
     assert written.sum().item() == 2            # only row 0 (slot 0), one entry per KV head
     assert written[0, :, 0].all()
+
+
+def test_host_copy_sees_every_rewrite(dev):
+    """cb_copy_host_to_device: the kernel copy reproduces the pinned bytes exactly, also after the
+    host rewrites the same buffer (no stale GPU-cached host data), and rejects misalignment."""
+    from chunked_prefill_mixed_decode_amd import binding as cb
+    g = torch.Generator().manual_seed(7)
+    src = torch.empty(12345 * 2, dtype=torch.int32).pin_memory()
+    dst = torch.empty(src.numel(), dtype=torch.int32, device=dev)
+    for rnd in range(3):
+        src.copy_(torch.randint(-2**31, 2**31 - 1, (src.numel(),), generator=g, dtype=torch.int64).to(torch.int32))
+        cb.cb_copy_host_to_device(src, dst)
+        torch.cuda.synchronize()
+        assert torch.equal(dst.cpu(), src), f"round {rnd}"
+    lib = cb._lib()
+    assert lib.cb_copy_host_to_device(None, src.data_ptr() + 4, dst.data_ptr(), 8) == cb.CB_ERR_INVALID
+    assert lib.cb_copy_host_to_device(None, src.data_ptr(), dst.data_ptr(), 12) == cb.CB_ERR_INVALID
