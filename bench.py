@@ -96,9 +96,11 @@ def committed_traffic(kernel: str):
     return rec["kernels"][kernel]["traffic_bytes"]
 
 
-def isolation_pass(g, metas, qrots, outs, w, reps: int):
+def isolation_pass(g, metas, qrots, outs, w, reps: int, flush=None):
     """Decode-only and chunk-only launches of each step's metadata, timed with HIP events on the
-    launch stream: per-kernel durations without the other kernel running beside it."""
+    launch stream: per-kernel durations without the other kernel running beside it.  Decode
+    launches report attention + combine time.  With ``flush`` (a device tensor), it is rewritten
+    before every launch so that L2 and the MALL hold none of the step's data (cold cache)."""
     import torch
     cb = g.cb
     dec, chk = [], []
@@ -119,15 +121,20 @@ def isolation_pass(g, metas, qrots, outs, w, reps: int):
         for e in ev:
             e.record()
         for _ in range(reps):
-            cb.cb_mixed_paged_attention(
-                qrots[k][:nd], g.runner.k_cache, g.runner.v_cache, dev["cu_seqlens_q"],
-                dev["context_lens"], dev["cu_blocks"], dev["block_table"], outs[k][:nd],
-                g.runner.workspace, num_seqs=nd, num_decodes=nd, max_q_len=1,
-                max_decode_ctx=meta.max_decode_context_len, max_ctx=meta.max_decode_context_len,
-                scale=g.runner.scale, events=[ev[0], ev[1], None, None, None, None])
-            torch.cuda.synchronize()
-            dec.append((k, ev[0].elapsed_time(ev[1])))
+            if nd > 0:
+                if flush is not None:
+                    flush.add_(1)
+                cb.cb_mixed_paged_attention(
+                    qrots[k][:nd], g.runner.k_cache, g.runner.v_cache, dev["cu_seqlens_q"],
+                    dev["context_lens"], dev["cu_blocks"], dev["block_table"], outs[k][:nd],
+                    g.runner.workspace, num_seqs=nd, num_decodes=nd, max_q_len=1,
+                    max_decode_ctx=meta.max_decode_context_len, max_ctx=meta.max_decode_context_len,
+                    scale=g.runner.scale, events=[ev[0], ev[1], None, None, ev[4], ev[5]])
+                torch.cuda.synchronize()
+                dec.append((k, ev[0].elapsed_time(ev[1]) + ev[4].elapsed_time(ev[5])))
             if T > nd:
+                if flush is not None:
+                    flush.add_(1)
                 cb.cb_mixed_paged_attention(
                     qrots[k][nd:], g.runner.k_cache, g.runner.v_cache, cu_chunk,
                     dev["context_lens"][nd:], dev["cu_blocks"][nd:], dev["block_table"], outs[k][nd:],
@@ -137,6 +144,33 @@ def isolation_pass(g, metas, qrots, outs, w, reps: int):
                 torch.cuda.synchronize()
                 chk.append((k, ev[2].elapsed_time(ev[3])))
     return dec, chk
+
+
+def pct(xs, q):
+    xs = sorted(xs)
+    return xs[min(len(xs) - 1, max(0, int(round(q * (len(xs) - 1)))))]
+
+
+def summarize_isolated(dec, chk, metas, w, elt):
+    """Roofline fractions of isolated launches: decode rows (bytes over attention + combine time)
+    against HBM, chunk rows (FLOPs over chunk time) against bf16 MFMA, totals and per step."""
+    dec_s = sum(t for _, t in dec) / 1e3
+    chk_s = sum(t for _, t in chk) / 1e3
+    dbytes = sum(decode_bytes(metas[k], w, elt) for k, _ in dec)
+    cflops = sum(chunk_flops(metas[k], w) for k, _ in chk)
+    per_step = {}
+    for k, t in chk:
+        per_step.setdefault(k, []).append(t)
+    out = {"decode_avg_us": dec_s / max(1, len(dec)) * 1e6,
+           "decode_GBps": dbytes / max(dec_s, 1e-12) / 1e9,
+           "decode_frac_hbm": dbytes / max(dec_s, 1e-12) / 1e9 / HBM_PEAK_GBS,
+           "chunk_avg_us": chk_s / max(1, len(chk)) * 1e6,
+           "chunk_TFLOPs": cflops / max(chk_s, 1e-12) / 1e12,
+           "chunk_frac_mfma": cflops / max(chk_s, 1e-12) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+           "chunk_flops_per_step": cflops / max(1, len(chk)),
+           "chunk_TFLOPs_per_step": {str(k): chunk_flops(metas[k], w) / (sum(v) / len(v) / 1e3) / 1e12
+                                     for k, v in sorted(per_step.items())}}
+    return out
 
 
 def cpu_baseline(w, step_index: int):
@@ -214,7 +248,15 @@ def main():
     cb = g.cb
     snapshot = cb.cb_sched_clone(g.sched)
 
-    # One dry cycle learns each step's metadata; its inputs are generated and kept in HBM.
+    # One dry cycle learns each step's metadata; its inputs are generated and kept in HBM.  A
+    # workload without a fixed step count cycles until its last prompt has had its last chunk.
+    if cb_steps is None:
+        p2 = cb.cb_sched_clone(snapshot)
+        b2 = cb.StepBuffers(*g.runner.bufs[0].cap)
+        cb_steps = 0
+        while cb.cb_sched_pending_prompts(p2) > 0 and cb_steps < w.max_steps:
+            cb.cb_build_step(p2, w.budget, b2)
+            cb_steps += 1
     inputs, metas, ws = [], [], 0
     probe = cb.cb_sched_clone(snapshot)
     bufs = cb.StepBuffers(*g.runner.bufs[0].cap)
@@ -299,11 +341,22 @@ def main():
     attn_avg_s = sum(dec_ms) / len(dec_ms) / 1e3
     achieved = sum(abytes) / len(abytes) / attn_avg_s / 1e9
 
-    iso_dec, iso_chk = isolation_pass(g, metas, qrots, outs, w, reps=3)
-    iso_dec_s = sum(t for _, t in iso_dec) / 1e3
-    iso_chk_s = sum(t for _, t in iso_chk) / 1e3
-    iso_bytes = sum(decode_bytes(metas[k], w, elt) for k, _ in iso_dec)
-    iso_flops = sum(chunk_flops(metas[k], w) for k, _ in iso_chk)
+    # End-to-end latency: host wall time from cb_build_step to stream sync after attention.
+    e2e = []
+    for _ in range(min(args.steps, 3 * cb_steps)):
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        one_step()
+        torch.cuda.synchronize()
+        e2e.append((time.perf_counter() - t1) * 1e3)
+
+    print("[bench] isolated launches (warm, then cold)...", file=sys.stderr, flush=True)
+    iso = summarize_isolated(*isolation_pass(g, metas, qrots, outs, w, reps=3), metas, w, elt)
+    iso["note"] = "decode-only and chunk-only launches of the same step metadata, 3 reps per step"
+    flush = torch.zeros(128 << 20, dtype=torch.int32, device=dev)   # 512 MiB: L2 and MALL
+    iso_cold = summarize_isolated(*isolation_pass(g, metas, qrots, outs, w, reps=2, flush=flush), metas, w, elt)
+    iso_cold["note"] = "as isolated, with a 512 MiB device write before every launch (L2 and MALL cold)"
+    del flush
     traffic = committed_traffic("attn_kernel")
 
     res = {
@@ -321,27 +374,23 @@ def main():
         "data": "synthetic (seeded SplitMix64 normal-quantile activations; seeded workload structure)",
         "config": {"workload": w.name, "heads_q": w.Hq, "heads_kv": w.Hkv, "head_dim": w.D,
                    "block_size": w.block_size, "token_budget": w.budget,
-                   "decodes": len(w.decode_ctx), "prompt_len": w.prompts[0][0],
+                   "decodes": len(w.decode_ctx), "prompts": [list(p) for p in w.prompts],
                    "steps_per_cycle": cb_steps, "parallelism": "1 GPU"},
         "roofline": {"bound": "hbm", "kernel": "attn_kernel (decode waves + chunk tiles, one launch)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "bytes_per_launch": sum(abytes) / len(abytes), "avg_launch_us": attn_avg_s * 1e6},
-        "isolated": {"decode_avg_us": iso_dec_s / len(iso_dec) * 1e6,
-                     "decode_GBps": iso_bytes / iso_dec_s / 1e9,
-                     "decode_frac_hbm": iso_bytes / iso_dec_s / 1e9 / HBM_PEAK_GBS,
-                     "chunk_avg_us": iso_chk_s / max(1, len(iso_chk)) * 1e6,
-                     "chunk_TFLOPs": iso_flops / max(iso_chk_s, 1e-12) / 1e12,
-                     "chunk_frac_mfma": iso_flops / max(iso_chk_s, 1e-12) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
-                     "chunk_flops_per_step": iso_flops / max(1, len(iso_chk)),
-                     "note": "decode-only and chunk-only launches of the same step metadata, 3 reps per step"},
+        "isolated": iso,
+        "isolated_cold": iso_cold,
         "combine_avg_us": sum(cmb_ms) / len(cmb_ms) * 1e3,
         "device_step_us": sum(dev_step_ms) / len(dev_step_ms) * 1e3,
+        "device_step_us_p10_p50_p90": [pct(dev_step_ms, q) * 1e3 for q in (0.1, 0.5, 0.9)],
+        "end_to_end_ms_p10_p50_p90": [pct(e2e, q) for q in (0.1, 0.5, 0.9)],
         "event_sampled_steps": len(sampled),
     }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)...", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_step)
+        res["cpu_baseline"] = cpu_baseline(w, min(args.cpu_sample_step, cb_steps - 1))
     line = json.dumps(res)
     print(line, flush=True)
     if args.json_out:
