@@ -24,6 +24,7 @@
 // Softmax runs in base 2: weights are 2^(s c - m) with c = scale * log2(e) and m the running
 // maximum of s c.
 #include <algorithm>
+#include <type_traits>
 
 #include "cb.h"
 #include "common.h"
@@ -287,69 +288,67 @@ __device__ __forceinline__ void wait_vm_barrier() {
 // The operands of one 32-key chunk stage (bf16): K rows (KS ds_read_b128) and V^T (two
 // ds_read_b64_tr_b16 per 32x16 piece, the second 16 keys further down), issued back to back
 // and waited for together inside one asm block.  ka[ks] / va[2 mt + h] are the LDS addresses
-// lds_row_frag / lds_vt_frag32 would read (piece ps = 0); ps = 1 is 16 rows further.
+// lds_row_frag / lds_vt_frag32 would read in ring buffer 0 (piece ps = 0); OFF selects the ring
+// buffer (an immediate offset), and ps = 1 is 16 rows further.
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 template <int D> struct StageRegs;
 template <> struct StageRegs<128> {
   u32x4 k[8];
   u32x2 v[2][8];   // [ps][2 mt + h]
+  template <int OFF>
   __device__ __forceinline__ void read(const uint32_t (&ka)[8], const uint32_t (&va)[8]) {
     asm volatile(
-        "ds_read_b128 %0, %24\n\t"
-        "ds_read_b128 %1, %25\n\t"
-        "ds_read_b128 %2, %26\n\t"
-        "ds_read_b128 %3, %27\n\t"
-        "ds_read_b128 %4, %28\n\t"
-        "ds_read_b128 %5, %29\n\t"
-        "ds_read_b128 %6, %30\n\t"
-        "ds_read_b128 %7, %31\n\t"
-        "ds_read_b64_tr_b16 %8, %32\n\t"
-        "ds_read_b64_tr_b16 %9, %33\n\t"
-        "ds_read_b64_tr_b16 %10, %34\n\t"
-        "ds_read_b64_tr_b16 %11, %35\n\t"
-        "ds_read_b64_tr_b16 %12, %36\n\t"
-        "ds_read_b64_tr_b16 %13, %37\n\t"
-        "ds_read_b64_tr_b16 %14, %38\n\t"
-        "ds_read_b64_tr_b16 %15, %39\n\t"
-        "ds_read_b64_tr_b16 %16, %32 offset:4096\n\t"
-        "ds_read_b64_tr_b16 %17, %33 offset:4096\n\t"
-        "ds_read_b64_tr_b16 %18, %34 offset:4096\n\t"
-        "ds_read_b64_tr_b16 %19, %35 offset:4096\n\t"
-        "ds_read_b64_tr_b16 %20, %36 offset:4096\n\t"
-        "ds_read_b64_tr_b16 %21, %37 offset:4096\n\t"
-        "ds_read_b64_tr_b16 %22, %38 offset:4096\n\t"
-        "ds_read_b64_tr_b16 %23, %39 offset:4096\n\t"
+        "ds_read_b128 %0, %24 offset:%40\n\t"
+        "ds_read_b128 %1, %25 offset:%40\n\t"
+        "ds_read_b128 %2, %26 offset:%40\n\t"
+        "ds_read_b128 %3, %27 offset:%40\n\t"
+        "ds_read_b128 %4, %28 offset:%40\n\t"
+        "ds_read_b128 %5, %29 offset:%40\n\t"
+        "ds_read_b128 %6, %30 offset:%40\n\t"
+        "ds_read_b128 %7, %31 offset:%40\n\t"
+        "ds_read_b64_tr_b16 %8, %32 offset:%40\n\t"
+        "ds_read_b64_tr_b16 %9, %33 offset:%40\n\t"
+        "ds_read_b64_tr_b16 %10, %34 offset:%40\n\t"
+        "ds_read_b64_tr_b16 %11, %35 offset:%40\n\t"
+        "ds_read_b64_tr_b16 %12, %36 offset:%40\n\t"
+        "ds_read_b64_tr_b16 %13, %37 offset:%40\n\t"
+        "ds_read_b64_tr_b16 %14, %38 offset:%40\n\t"
+        "ds_read_b64_tr_b16 %15, %39 offset:%40\n\t"
+        "ds_read_b64_tr_b16 %16, %32 offset:%41\n\t"
+        "ds_read_b64_tr_b16 %17, %33 offset:%41\n\t"
+        "ds_read_b64_tr_b16 %18, %34 offset:%41\n\t"
+        "ds_read_b64_tr_b16 %19, %35 offset:%41\n\t"
+        "ds_read_b64_tr_b16 %20, %36 offset:%41\n\t"
+        "ds_read_b64_tr_b16 %21, %37 offset:%41\n\t"
+        "ds_read_b64_tr_b16 %22, %38 offset:%41\n\t"
+        "ds_read_b64_tr_b16 %23, %39 offset:%41\n\t"
         "s_waitcnt lgkmcnt(0)"
-        : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(k[4]), "=&v"(k[5]), "=&v"(k[6]),
-          "=&v"(k[7]), "=&v"(v[0][0]), "=&v"(v[0][1]), "=&v"(v[0][2]), "=&v"(v[0][3]), "=&v"(v[0][4]),
-          "=&v"(v[0][5]), "=&v"(v[0][6]), "=&v"(v[0][7]), "=&v"(v[1][0]), "=&v"(v[1][1]), "=&v"(v[1][2]),
-          "=&v"(v[1][3]), "=&v"(v[1][4]), "=&v"(v[1][5]), "=&v"(v[1][6]), "=&v"(v[1][7])
-        : "v"(ka[0]), "v"(ka[1]), "v"(ka[2]), "v"(ka[3]), "v"(ka[4]), "v"(ka[5]), "v"(ka[6]), "v"(ka[7]),
-          "v"(va[0]), "v"(va[1]), "v"(va[2]), "v"(va[3]), "v"(va[4]), "v"(va[5]), "v"(va[6]), "v"(va[7]));
+        : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(k[4]), "=&v"(k[5]), "=&v"(k[6]), "=&v"(k[7]), "=&v"(v[0][0]), "=&v"(v[0][1]), "=&v"(v[0][2]), "=&v"(v[0][3]), "=&v"(v[0][4]), "=&v"(v[0][5]), "=&v"(v[0][6]), "=&v"(v[0][7]), "=&v"(v[1][0]), "=&v"(v[1][1]), "=&v"(v[1][2]), "=&v"(v[1][3]), "=&v"(v[1][4]), "=&v"(v[1][5]), "=&v"(v[1][6]), "=&v"(v[1][7])
+        : "v"(ka[0]), "v"(ka[1]), "v"(ka[2]), "v"(ka[3]), "v"(ka[4]), "v"(ka[5]), "v"(ka[6]), "v"(ka[7]), "v"(va[0]), "v"(va[1]), "v"(va[2]), "v"(va[3]), "v"(va[4]), "v"(va[5]), "v"(va[6]), "v"(va[7]), "n"(OFF), "n"(OFF + 4096));
   }
 };
 template <> struct StageRegs<64> {
   u32x4 k[4];
-  u32x2 v[2][4];
+  u32x2 v[2][4];   // [ps][2 mt + h]
+  template <int OFF>
   __device__ __forceinline__ void read(const uint32_t (&ka)[4], const uint32_t (&va)[4]) {
     asm volatile(
-        "ds_read_b128 %0, %12\n\t"
-        "ds_read_b128 %1, %13\n\t"
-        "ds_read_b128 %2, %14\n\t"
-        "ds_read_b128 %3, %15\n\t"
-        "ds_read_b64_tr_b16 %4, %16\n\t"
-        "ds_read_b64_tr_b16 %5, %17\n\t"
-        "ds_read_b64_tr_b16 %6, %18\n\t"
-        "ds_read_b64_tr_b16 %7, %19\n\t"
-        "ds_read_b64_tr_b16 %8, %16 offset:2048\n\t"
-        "ds_read_b64_tr_b16 %9, %17 offset:2048\n\t"
-        "ds_read_b64_tr_b16 %10, %18 offset:2048\n\t"
-        "ds_read_b64_tr_b16 %11, %19 offset:2048\n\t"
+        "ds_read_b128 %0, %12 offset:%20\n\t"
+        "ds_read_b128 %1, %13 offset:%20\n\t"
+        "ds_read_b128 %2, %14 offset:%20\n\t"
+        "ds_read_b128 %3, %15 offset:%20\n\t"
+        "ds_read_b64_tr_b16 %4, %16 offset:%20\n\t"
+        "ds_read_b64_tr_b16 %5, %17 offset:%20\n\t"
+        "ds_read_b64_tr_b16 %6, %18 offset:%20\n\t"
+        "ds_read_b64_tr_b16 %7, %19 offset:%20\n\t"
+        "ds_read_b64_tr_b16 %8, %16 offset:%21\n\t"
+        "ds_read_b64_tr_b16 %9, %17 offset:%21\n\t"
+        "ds_read_b64_tr_b16 %10, %18 offset:%21\n\t"
+        "ds_read_b64_tr_b16 %11, %19 offset:%21\n\t"
         "s_waitcnt lgkmcnt(0)"
-        : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(v[0][0]), "=&v"(v[0][1]),
-          "=&v"(v[0][2]), "=&v"(v[0][3]), "=&v"(v[1][0]), "=&v"(v[1][1]), "=&v"(v[1][2]), "=&v"(v[1][3])
-        : "v"(ka[0]), "v"(ka[1]), "v"(ka[2]), "v"(ka[3]), "v"(va[0]), "v"(va[1]), "v"(va[2]), "v"(va[3]));
+        : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(v[0][0]), "=&v"(v[0][1]), "=&v"(v[0][2]), "=&v"(v[0][3]), "=&v"(v[1][0]), "=&v"(v[1][1]), "=&v"(v[1][2]), "=&v"(v[1][3])
+        : "v"(ka[0]), "v"(ka[1]), "v"(ka[2]), "v"(ka[3]), "v"(va[0]), "v"(va[1]), "v"(va[2]), "v"(va[3]), "n"(OFF), "n"(OFF + 2048));
   }
 };
 
@@ -720,7 +719,7 @@ __device__ __forceinline__ void chunk_tile(const AttnArgs& a, int32_t tile, char
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: copy targets stay scalar
   const int col = lane & 31;          // query row of this lane in S^T / P^T / O^T
   const int half = lane >> 5;         // slot group
   const int rr = 32 * wave + col;     // row within the tile
@@ -795,13 +794,15 @@ __device__ __forceinline__ void chunk_tile(const AttnArgs& a, int32_t tile, char
     else wait_vm_barrier<0>();
   };
 
-  // Loop-invariant LDS read offsets of this lane within a stage buffer (bf16 operand reads).
+  // Loop-invariant LDS read addresses of this lane in ring buffer 0 (bf16 operand reads; the
+  // buffer is selected by an immediate offset).
   uint32_t ka[KS], va[KS];
   if constexpr (sizeof(T) == 2) {
+    const uint32_t k_base = lds_addr(sK), v_base = lds_addr(sV);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int b0 = 2 * (16 * ks + 8 * half);
-      ka[ks] = col * ROW + 16 * lds_chunk(b0 >> 4, col, ROW);
+      ka[ks] = k_base + col * ROW + 16 * lds_chunk(b0 >> 4, col, ROW);
     }
     const int grp = lane >> 4, ii = lane & 15, jj = ii >> 2, qd = ii & 3;
 #pragma unroll
@@ -810,7 +811,7 @@ __device__ __forceinline__ void chunk_tile(const AttnArgs& a, int32_t tile, char
       for (int h = 0; h < 2; ++h) {
         const int e = 32 * mt + 16 * (grp & 1) + 4 * qd;
         const int r = 8 * h + 4 * (grp >> 1) + jj;
-        va[2 * mt + h] = r * ROW + 16 * lds_chunk((2 * e) >> 4, r, ROW) + ((2 * e) & 15);
+        va[2 * mt + h] = v_base + r * ROW + 16 * lds_chunk((2 * e) >> 4, r, ROW) + ((2 * e) & 15);
       }
   }
 
@@ -825,27 +826,21 @@ __device__ __forceinline__ void chunk_tile(const AttnArgs& a, int32_t tile, char
     // Stages whose keys all lie in blocks [win_lo, win_lo + kBlockWindow) (a multiple of 32 keys).
     const int64_t key_end = static_cast<int64_t>(win_lo + kBlockWindow) << bsh;
     const int32_t j_end = kv_end <= key_end ? n_st : static_cast<int32_t>(min<int64_t>(n_st, key_end / kChunkKeys - kt_lo));
-#pragma unroll
-    for (int p = 0; p < NS - 1; ++p)
-      if (j + p < j_end) issue(kt_lo + j + p, (j + p) % NS);
-    for (; j < j_end; ++j) {
-      const int32_t kt = kt_lo + j;
-      const int buf = j % NS;
-      wait_stage(min(NS - 2, j_end - 1 - j));    // every wave's copy of stage j has landed
-      if (j + NS - 1 < j_end) issue(kt + NS - 1, (j + NS - 1) % NS);
+    // The ring restarts at buffer 0 in every window; unrolled by NS, each stage's buffer is a
+    // compile-time constant (immediate LDS offsets).
+    const int32_t j0 = j;
+    auto stage = [&](int32_t jj, auto B) {
+      constexpr int buf = decltype(B)::value;
+      constexpr int next_buf = (buf + NS - 1) % NS;
+      const int32_t kt = kt_lo + jj;
+      wait_stage(min(NS - 2, j_end - 1 - jj));   // every wave's copy of stage jj has landed
+      if (jj + NS - 1 < j_end) issue(kt + NS - 1, next_buf);
 
       Frag<T> kf[KS];
       Frag<T> vt[2][MT];
       if constexpr (sizeof(T) == 2) {
         StageRegs<D> sr;
-        uint32_t kaa[KS], vaa[KS];
-        const uint32_t base_k = lds_addr(sK + buf * STAGE), base_v = lds_addr(sV + buf * STAGE);
-#pragma unroll
-        for (int i = 0; i < KS; ++i) {
-          kaa[i] = base_k + ka[i];
-          vaa[i] = base_v + va[i];
-        }
-        sr.read(kaa, vaa);
+        sr.template read<buf * STAGE>(ka, va);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) kf[ks].u = make_uint4(sr.k[ks].x, sr.k[ks].y, sr.k[ks].z, sr.k[ks].w);
 #pragma unroll
@@ -903,6 +898,23 @@ __device__ __forceinline__ void chunk_tile(const AttnArgs& a, int32_t tile, char
         pf.set_all(pv);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) mma32_k16(o[mt], vt[ps][mt], pf);
+      }
+    };
+#pragma unroll
+    for (int p = 0; p < NS - 1; ++p)
+      if (j0 + p < j_end) issue(kt_lo + j0 + p, p);
+    while (j < j_end) {
+      stage(j, std::integral_constant<int, 0>{});
+      if (++j == j_end) break;
+      stage(j, std::integral_constant<int, 1>{});
+      if (++j == j_end) break;
+      if constexpr (NS > 2) {
+        stage(j, std::integral_constant<int, 2 % NS>{});
+        if (++j == j_end) break;
+      }
+      if constexpr (NS > 3) {
+        stage(j, std::integral_constant<int, 3 % NS>{});
+        if (++j == j_end) break;
       }
     }
   }
