@@ -378,17 +378,27 @@ __device__ __forceinline__ int32_t block_scan_1024(int32_t v, int32_t* scan) {
   return scan[tid];
 }
 
+constexpr int kPrepRows = 8192;   // decode rows whose stage offsets the prep workgroup keeps in LDS
+
 __global__ __launch_bounds__(1024) void decode_prep_kernel(AttnArgs a, int32_t n_waves) {
   __shared__ int32_t scan[1024];
+  __shared__ int32_t seq_lds[kPrepRows + 1];
   __shared__ int32_t carry;
   const int tid = threadIdx.x;
+  // The searches below read the row offsets from LDS when they fit (one LDS round trip per
+  // search step instead of a global one).
+  const bool in_lds = a.nd <= kPrepRows;
+  const int32_t* seq = in_lds ? seq_lds : a.dec_seq;
   if (tid == 0) carry = 0;
   __syncthreads();
   for (int32_t base = 0; base < a.nd; base += 1024) {
     const int32_t s = base + tid;
     const int32_t n = s < a.nd ? decode_stages(a.ctx_lens[s]) * a.ups : 0;
     const int32_t incl = block_scan_1024(n, scan);
-    if (s < a.nd) a.dec_seq[s] = carry + incl - n;
+    if (s < a.nd) {
+      a.dec_seq[s] = carry + incl - n;
+      if (in_lds) seq_lds[s] = carry + incl - n;
+    }
     __syncthreads();                                  // every thread has read carry
     if (tid == 1023) carry += scan[1023];
     __syncthreads();
@@ -398,20 +408,22 @@ __global__ __launch_bounds__(1024) void decode_prep_kernel(AttnArgs a, int32_t n
   const int32_t W = (S + L - 1) / L;
   if (tid == 0) {
     a.dec_seq[a.nd] = S;
+    if (in_lds) seq_lds[a.nd] = S;
     a.dec_par[0] = S;
     a.dec_par[1] = L;
     a.dec_par[2] = W;
   }
-  __syncthreads();                                    // dec_seq is complete for the workgroup
+  __syncthreads();                                    // the row offsets are complete for the workgroup
   for (int32_t w = tid; w < W; w += 1024) {
     const int32_t pos = w * L;
-    int32_t lo = 0, hi = a.nd;                        // dec_seq[lo] <= pos < dec_seq[hi]
+    int32_t lo = 0, hi = a.nd;                        // seq[lo] <= pos < seq[hi]
     while (hi - lo > 1) {
       const int32_t mid = (lo + hi) >> 1;
-      if (a.dec_seq[mid] <= pos) lo = mid;
+      if (seq[mid] <= pos) lo = mid;
       else hi = mid;
     }
-    a.dec_wave[w] = lo * a.ups + (pos - a.dec_seq[lo]) / decode_stages(a.ctx_lens[lo]);
+    // The row's units each have (seq[lo + 1] - seq[lo]) / ups stages (> 0: pos falls inside it).
+    a.dec_wave[w] = lo * a.ups + (pos - seq[lo]) / ((seq[lo + 1] - seq[lo]) / a.ups);
   }
 }
 

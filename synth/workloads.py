@@ -148,7 +148,13 @@ def small(i: int) -> Workload:
     if i == 7:   # float32 at head dim 128
         ctx = rng.integers(20, 300, size=4, endpoint=True)
         return _make("small7_d128_f32", "f32", 4, 4, 128, 16, 160, ctx, ((400, 0),), 3, 2007, rng)
+    if i == 8:   # decode-heavy: 24 decodes U{1500..3000} x 16 heads, ~27K 32-key decode stages,
+        # so the stage split spreads each unit over several waves and the combine merges several
+        # partials per row and head
+        ctx = rng.integers(1500, 3000, size=24, endpoint=True)
+        return _make("small8_decode_tail_bf16", "bf16", 16, 16, 128, 16, 324, ctx, ((600, 0),), 3,
+                     2008, rng)
     raise KeyError(i)
 
 
-SMALL = (1, 2, 3, 4, 5, 6, 7)
+SMALL = (1, 2, 3, 4, 5, 6, 7, 8)
