@@ -21,6 +21,7 @@ LIB_PATH = os.environ.get("CB_LIBCB_PATH") or os.path.join(_PKG, "libcb.so")
 CB_OK, CB_ERR_INVALID, CB_ERR_DECODE_OVER_BUDGET, CB_ERR_OUT_OF_BLOCKS, CB_ERR_CAPACITY, CB_ERR_HIP = (
     0, -1, -2, -3, -4, -5)
 CB_F32, CB_BF16 = 0, 1
+CB_POLICY_DECODE_FIRST, CB_POLICY_PREFILL_FIRST, CB_POLICY_FAIR_SHARE = 0, 1, 2
 
 _i32, _i64, _sz, _vp, _f32, _f64 = (ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t,
                                     ctypes.c_void_p, ctypes.c_float, ctypes.c_double)
@@ -34,7 +35,9 @@ class CbError(RuntimeError):
 
 
 class cb_sched_config(ctypes.Structure):
-    _fields_ = [("block_size", _i32), ("num_blocks", _i32), ("free_list", _pi32), ("max_chunk", _i32)]
+    _fields_ = [("block_size", _i32), ("num_blocks", _i32), ("free_list", _pi32), ("max_chunk", _i32),
+                ("prefill_floor", _i32), ("max_partial_prefills", _i32), ("max_num_seqs", _i32),
+                ("policy", _i32), ("decode_share_pct", _i32), ("prefill_quota_pct", _i32)]
 
 
 class cb_step(ctypes.Structure):
@@ -58,6 +61,7 @@ EXPORTS = {
     "cb_sched_add_running": (ctypes.c_int, [_vp, _i32, _pi32]),
     "cb_sched_add_prompt": (ctypes.c_int, [_vp, _i32, _i32, _pi32]),
     "cb_sched_get_blocks": (ctypes.c_int, [_vp, _i32, _pi32, _i32, _pi32]),
+    "cb_sched_finish": (ctypes.c_int, [_vp, _i32]),
     "cb_sched_pending_prompts": (ctypes.c_int, [_vp, _pi32]),
     "cb_sched_free_blocks": (ctypes.c_int, [_vp, _pi32]),
     "cb_build_step": (ctypes.c_int, [_vp, _i32, ctypes.POINTER(cb_step)]),
@@ -133,8 +137,13 @@ class Sched:
             self.handle = None
 
 
-def cb_sched_create(block_size: int, num_blocks: int, free_list=None, max_chunk: int = 0) -> Sched:
-    cfg = cb_sched_config(block_size, num_blocks, None, max_chunk)
+def cb_sched_create(block_size: int, num_blocks: int, free_list=None, max_chunk: int = 0,
+                    prefill_floor: int = 0, max_partial_prefills: int = 0, max_num_seqs: int = 0,
+                    policy: int = CB_POLICY_DECODE_FIRST, decode_share_pct: int = 0,
+                    prefill_quota_pct: int = 0) -> Sched:
+    cfg = cb_sched_config(block_size, num_blocks, None, max_chunk, prefill_floor,
+                          max_partial_prefills, max_num_seqs, policy, decode_share_pct,
+                          prefill_quota_pct)
     keep = None
     if free_list is not None:
         keep = (ctypes.c_int32 * len(free_list))(*free_list)
@@ -183,6 +192,10 @@ def cb_sched_free_blocks(s: Sched) -> int:
     n = ctypes.c_int32()
     _check(_lib().cb_sched_free_blocks(s.handle, ctypes.byref(n)), "cb_sched_free_blocks")
     return n.value
+
+
+def cb_sched_finish(s: Sched, req_id: int) -> None:
+    _check(_lib().cb_sched_finish(s.handle, req_id), "cb_sched_finish")
 
 
 STEP_ARRAYS = ("seq_ids", "cu_seqlens_q", "context_lens", "cu_blocks", "block_table",

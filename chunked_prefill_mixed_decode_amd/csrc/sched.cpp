@@ -7,6 +7,9 @@
 // inequality, error when decodes alone exceed the budget, per-row positions / slots / block
 // table / context length, atomic commit, whole-prompt reservation) and "Splitting Prefill From
 // Decode Inside a Step" ("The arithmetic of chunk boundaries": reserve before the first chunk).
+// The optional caps and priority policies (per-request cap, the proposed floor, partial-prefill
+// and sequence caps, prefill-first / fair share / prefill quota) follow the readings documented
+// with cb_sched_config in cb.h.
 //
 // A build runs in two phases.  Phase 1 checks everything that can fail (budget, blocks,
 // capacities) and pre-allocates host memory without touching the logical state; phase 2 commits
@@ -14,6 +17,7 @@
 #include <algorithm>
 #include <cstdint>
 #include <new>
+#include <numeric>
 #include <vector>
 
 #include "cb.h"
@@ -24,6 +28,7 @@ struct RunningReq {
   int32_t rid;
   int32_t ctx;                   // tokens in the cache
   std::vector<int32_t> blocks;
+  int32_t waited = 0;            // consecutive steps this decode did not run
 };
 
 struct WaitingReq {
@@ -41,6 +46,12 @@ inline int32_t ceil_div(int64_t a, int64_t b) { return static_cast<int32_t>((a +
 struct cb_sched {
   int32_t bs = 0;
   int32_t max_chunk = 0;
+  int32_t prefill_floor = 0;
+  int32_t max_partial = 0;
+  int32_t max_seqs = 0;
+  int32_t policy = CB_POLICY_DECODE_FIRST;
+  int32_t decode_share_pct = 50;
+  int32_t quota_pct = 0;
   std::vector<int32_t> free_list;  // free blocks are free_list[free_head..]
   size_t free_head = 0;
   std::vector<RunningReq> running;
@@ -68,11 +79,22 @@ const char* cb_status_string(int status) {
 int cb_sched_create(const cb_sched_config* cfg, cb_sched** out) {
   if (!cfg || !out || cfg->block_size < 1 || cfg->num_blocks < 0 || cfg->max_chunk < 0)
     return CB_ERR_INVALID;
+  if (cfg->prefill_floor < 0 || cfg->max_partial_prefills < 0 || cfg->max_num_seqs < 0 ||
+      cfg->policy < CB_POLICY_DECODE_FIRST || cfg->policy > CB_POLICY_FAIR_SHARE ||
+      cfg->decode_share_pct < 0 || cfg->decode_share_pct > 99 || cfg->prefill_quota_pct < 0 ||
+      cfg->prefill_quota_pct > 100)
+    return CB_ERR_INVALID;
   *out = nullptr;
   try {
     auto* s = new cb_sched();
     s->bs = cfg->block_size;
     s->max_chunk = cfg->max_chunk;
+    s->prefill_floor = cfg->prefill_floor;
+    s->max_partial = cfg->max_partial_prefills;
+    s->max_seqs = cfg->max_num_seqs;
+    s->policy = cfg->policy;
+    s->decode_share_pct = cfg->decode_share_pct ? cfg->decode_share_pct : 50;
+    s->quota_pct = cfg->prefill_quota_pct;
     s->free_list.resize(cfg->num_blocks);
     if (cfg->free_list) {
       std::vector<char> seen(cfg->num_blocks, 0);
@@ -173,6 +195,29 @@ int cb_sched_free_blocks(const cb_sched* s, int32_t* n) {
   return CB_OK;
 }
 
+int cb_sched_finish(cb_sched* s, int32_t req_id) {
+  if (!s) return CB_ERR_INVALID;
+  std::vector<int32_t>* bl = nullptr;
+  size_t ri = s->running.size(), wi = s->waiting.size();
+  for (size_t i = 0; i < s->running.size(); ++i)
+    if (s->running[i].rid == req_id) { ri = i; bl = &s->running[i].blocks; }
+  for (size_t i = 0; i < s->waiting.size() && !bl; ++i)
+    if (s->waiting[i].rid == req_id && s->waiting[i].done == s->waiting[i].len) { wi = i; bl = &s->waiting[i].blocks; }
+  if (!bl) return CB_ERR_INVALID;
+  try {
+    if (s->free_head > 0 && s->free_head * 2 >= s->free_list.size()) {   // drop the used prefix
+      s->free_list.erase(s->free_list.begin(), s->free_list.begin() + s->free_head);
+      s->free_head = 0;
+    }
+    s->free_list.insert(s->free_list.end(), bl->begin(), bl->end());
+  } catch (const std::bad_alloc&) {
+    return CB_ERR_CAPACITY;
+  }
+  if (ri < s->running.size()) s->running.erase(s->running.begin() + ri);
+  else s->waiting.erase(s->waiting.begin() + wi);
+  return CB_OK;
+}
+
 }  // extern "C"
 
 namespace {
@@ -181,51 +226,136 @@ int build_step_impl(cb_sched* s, int32_t token_budget, cb_step* out) {
   const int32_t bs = s->bs;
 
   // ---------------- phase 1: plan without touching the logical state ----------------
-  // Decodes are the running requests in order, then prompts that finished last step (FCFS).
+  // Decode candidates are the running requests in order, then prompts that finished last step
+  // (FCFS); candidate i < n_run is running[i], the others graduating[i - n_run].
   std::vector<int32_t> graduating;  // indices into waiting
   for (size_t i = 0; i < s->waiting.size(); ++i)
     if (s->waiting[i].done == s->waiting[i].len) graduating.push_back(static_cast<int32_t>(i));
-  const int64_t nd = static_cast<int64_t>(s->running.size()) + graduating.size();
-  if (nd > token_budget) return CB_ERR_DECODE_OVER_BUDGET;
-
+  const int64_t n_run = static_cast<int64_t>(s->running.size());
+  const int64_t nd_all = n_run + static_cast<int64_t>(graduating.size());
+  const int64_t n_prompts = static_cast<int64_t>(s->waiting.size() - graduating.size());
+  auto cand_ctx = [&](int64_t i) { return i < n_run ? s->running[i].ctx : s->waiting[graduating[i - n_run]].len; };
+  auto cand_nblocks = [&](int64_t i) {
+    return static_cast<int64_t>(i < n_run ? s->running[i].blocks.size() : s->waiting[graduating[i - n_run]].blocks.size());
+  };
+  auto cand_waited = [&](int64_t i) { return i < n_run ? s->running[i].waited : 0; };
   // A decode at position ctx needs a fresh block when its blocks are exactly full.
-  size_t decode_need = 0;
-  int64_t blocks_emitted = 0;
-  int32_t max_ctx = 0, max_dctx = 0;
-  for (const auto& r : s->running) {
-    decode_need += (static_cast<int64_t>(r.ctx) == static_cast<int64_t>(bs) * static_cast<int64_t>(r.blocks.size()));
-    blocks_emitted += ceil_div(r.ctx + 1, bs);
-    max_dctx = std::max(max_dctx, r.ctx + 1);
-  }
-  for (int32_t i : graduating) {
-    const auto& w = s->waiting[i];
-    decode_need += (static_cast<int64_t>(w.len) == static_cast<int64_t>(bs) * static_cast<int64_t>(w.blocks.size()));
-    blocks_emitted += ceil_div(w.len + 1, bs);
-    max_dctx = std::max(max_dctx, w.len + 1);
-  }
-  if (decode_need > s->free_count()) return CB_ERR_OUT_OF_BLOCKS;
-  max_ctx = max_dctx;
+  auto needs_block = [&](int64_t i) { return static_cast<int64_t>(cand_ctx(i)) == static_cast<int64_t>(bs) * cand_nblocks(i); };
 
-  struct Chunk { int32_t widx, take, reserve; };
+  const int64_t seq_cap = s->max_seqs > 0 ? s->max_seqs : nd_all + n_prompts;
+  const bool strict = s->policy == CB_POLICY_DECODE_FIRST && s->quota_pct == 0;
+  int64_t dec_limit = 0;
+  if (strict) {
+    if (nd_all > token_budget || nd_all > seq_cap) return CB_ERR_DECODE_OVER_BUDGET;
+    dec_limit = nd_all;
+  } else if (s->policy == CB_POLICY_DECODE_FIRST) {
+    const int64_t reserve = n_prompts > 0 ? (static_cast<int64_t>(s->quota_pct) * token_budget + 99) / 100 : 0;
+    dec_limit = std::min({nd_all, token_budget - reserve, seq_cap});
+  } else if (s->policy == CB_POLICY_FAIR_SHARE) {
+    dec_limit = std::min({nd_all, (static_cast<int64_t>(s->decode_share_pct) * token_budget + 99) / 100, seq_cap});
+  }
+  // Longest-waiting decodes first, running order among equals.
+  std::vector<int32_t> order(static_cast<size_t>(nd_all));
+  std::iota(order.begin(), order.end(), 0);
+  std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) { return cand_waited(x) > cand_waited(y); });
+  std::vector<char> chosen(static_cast<size_t>(nd_all), 0);
+  for (int64_t k = 0; k < dec_limit; ++k) chosen[order[k]] = 1;
+  int64_t n_chosen = dec_limit;
+  int64_t left = token_budget - n_chosen;
+  int64_t nseq = n_chosen;
+  // Blocks of the chosen decodes come before any prompt's reservation.
+  int64_t free_avail = static_cast<int64_t>(s->free_count());
+  for (int64_t i = 0; i < nd_all; ++i) free_avail -= (chosen[i] && needs_block(i));
+  if (free_avail < 0) return CB_ERR_OUT_OF_BLOCKS;
+
+  // Prompt walk, first pass (FCFS).
+  struct Chunk { int32_t widx; int64_t take; int32_t reserve; };
   std::vector<Chunk> chunks;
-  int64_t left = token_budget - nd;
-  size_t free_avail = s->free_count() - decode_need;
-  int32_t max_q = nd > 0 ? 1 : 0;
-  for (size_t i = 0; i < s->waiting.size() && left > 0; ++i) {
+  int64_t partial = 0;
+  for (size_t i = 0; i < s->waiting.size(); ++i) {
     const auto& w = s->waiting[i];
     if (w.done == w.len) continue;  // graduating this step
+    if (left == 0 || nseq >= seq_cap) break;
+    const int64_t rem = w.len - w.done;
+    int64_t g = std::min(rem, left);
+    if (s->max_chunk > 0) g = std::min<int64_t>(g, s->max_chunk);
+    if (s->prefill_floor > 0) g = std::min<int64_t>(g, s->prefill_floor);
+    if (s->max_partial > 0 && g < rem && partial >= s->max_partial) continue;  // skipped this step
     int32_t reserve = 0;
     if (!w.reserved) {
       reserve = ceil_div(w.len, bs) - static_cast<int32_t>(w.blocks.size());
-      if (static_cast<size_t>(reserve) > free_avail) break;  // strict FCFS: the head waits
+      if (reserve > free_avail) break;  // strict FCFS: the head waits for blocks
       free_avail -= reserve;
     }
-    int64_t take = std::min<int64_t>(w.len - w.done, left);
-    if (s->max_chunk > 0) take = std::min<int64_t>(take, s->max_chunk);
-    chunks.push_back({static_cast<int32_t>(i), static_cast<int32_t>(take), reserve});
-    left -= take;
-    max_q = std::max<int32_t>(max_q, static_cast<int32_t>(take));
-    const int32_t ctx = w.done + static_cast<int32_t>(take);
+    chunks.push_back({static_cast<int32_t>(i), g, reserve});
+    partial += g < rem;
+    ++nseq;
+    left -= g;
+  }
+  // Floor: the budget left is shared evenly among the admitted prompts with tokens to go.
+  if (s->prefill_floor > 0) {
+    auto room = [&](const Chunk& c) {
+      const auto& w = s->waiting[c.widx];
+      int64_t top = w.len - w.done;
+      if (s->max_chunk > 0) top = std::min<int64_t>(top, s->max_chunk);
+      return top - c.take;
+    };
+    while (left > 0) {
+      int64_t n_active = 0;
+      for (const auto& c : chunks) n_active += room(c) > 0;
+      if (n_active == 0) break;
+      const int64_t share = left / n_active;
+      if (share == 0) {
+        for (auto& c : chunks) {
+          if (left == 0) break;
+          if (room(c) > 0) {
+            ++c.take;
+            --left;
+          }
+        }
+        break;
+      }
+      std::vector<char> active(chunks.size());
+      for (size_t k = 0; k < chunks.size(); ++k) active[k] = room(chunks[k]) > 0;
+      for (size_t k = 0; k < chunks.size(); ++k) {
+        if (!active[k]) continue;
+        const int64_t d = std::min(room(chunks[k]), share);
+        chunks[k].take += d;
+        left -= d;
+      }
+    }
+  }
+  // Decodes that did not get their turn take what the prompts left (every mode but plain
+  // decode-first, where all of them already run).
+  if (!strict && left > 0) {
+    int64_t extra = std::min({nd_all - n_chosen, left, seq_cap - nseq});
+    for (int64_t k = 0; k < nd_all && extra > 0; ++k) {
+      const int32_t i = order[k];
+      if (chosen[i]) continue;
+      chosen[i] = 1;
+      free_avail -= needs_block(i);
+      --extra;
+      ++n_chosen;
+      ++nseq;
+      --left;
+    }
+    if (free_avail < 0) return CB_ERR_OUT_OF_BLOCKS;
+  }
+  const int64_t nd = n_chosen;
+
+  int64_t blocks_emitted = 0;
+  int32_t max_ctx = 0, max_dctx = 0;
+  for (int64_t i = 0; i < nd_all; ++i) {
+    if (!chosen[i]) continue;
+    blocks_emitted += ceil_div(cand_ctx(i) + 1, bs);
+    max_dctx = std::max(max_dctx, cand_ctx(i) + 1);
+  }
+  max_ctx = max_dctx;
+  int32_t max_q = nd > 0 ? 1 : 0;
+  for (const auto& c : chunks) {
+    const auto& w = s->waiting[c.widx];
+    max_q = std::max<int32_t>(max_q, static_cast<int32_t>(c.take));
+    const int32_t ctx = w.done + static_cast<int32_t>(c.take);
     blocks_emitted += ceil_div(ctx, bs);
     max_ctx = std::max(max_ctx, ctx);
   }
@@ -253,7 +383,7 @@ int build_step_impl(cb_sched* s, int32_t token_budget, cb_step* out) {
   // ---------------- phase 2: commit and emit (no failure past this point) ----------------
   for (int32_t i : graduating) {
     auto& w = s->waiting[i];
-    s->running.push_back(RunningReq{w.rid, w.len, std::move(w.blocks)});
+    s->running.push_back(RunningReq{w.rid, w.len, std::move(w.blocks), 0});
   }
 
   int32_t seq = 0, row = 0, nblk = 0;
@@ -275,7 +405,13 @@ int build_step_impl(cb_sched* s, int32_t token_budget, cb_step* out) {
     out->cu_blocks[seq] = nblk;
   };
 
-  for (auto& r : s->running) {
+  for (size_t i = 0; i < s->running.size(); ++i) {
+    auto& r = s->running[i];
+    if (!chosen[i]) {
+      ++r.waited;
+      continue;
+    }
+    r.waited = 0;
     if (static_cast<int64_t>(r.ctx) == static_cast<int64_t>(bs) * static_cast<int64_t>(r.blocks.size()))
       r.blocks.push_back(s->pop_block());
     emit(r.rid, r.ctx, 1, r.blocks);
@@ -287,8 +423,8 @@ int build_step_impl(cb_sched* s, int32_t token_budget, cb_step* out) {
       for (int32_t j = 0; j < c.reserve; ++j) w.blocks.push_back(s->pop_block());
       w.reserved = true;
     }
-    emit(w.rid, w.done, c.take, w.blocks);
-    w.done += c.take;
+    emit(w.rid, w.done, static_cast<int32_t>(c.take), w.blocks);
+    w.done += static_cast<int32_t>(c.take);
   }
   if (!graduating.empty()) {  // compact the queue in place (no allocation)
     size_t g = 0, wpos = 0;

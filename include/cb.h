@@ -63,6 +63,33 @@ const char* cb_status_string(int status);
  * stops there; a decode that needs a block when none is free fails with CB_ERR_OUT_OF_BLOCKS (no
  * preemption).  Request ids are assigned 0, 1, 2, ... in the order requests are added.
  * A cb_sched is not thread-safe; distinct objects are independent.
+ *
+ * Optional caps and priority policies (cb_sched_config; all off by default, and then the plan is
+ * the decode-first one above):
+ *   max_chunk            per-request cap on a step's take: [P2] "Chunked prefill as a rate
+ *                        control"; also [P4]'s shipped long-prefill threshold, which is the same
+ *                        ceiling ("The fix").
+ *   prefill_floor        [P4]'s proposed floor (closing section).  Reading: a first FCFS pass
+ *                        grants each admitted prompt min(remaining, floor, budget left); the budget
+ *                        still left is then shared evenly among the admitted prompts that have
+ *                        tokens to go (each bounded by its remaining tokens and max_chunk), an
+ *                        indivisible rest going one token each in FCFS order.
+ *   max_partial_prefills [P3] §10.  Reading: a prompt whose first-pass grant leaves it unfinished
+ *                        is admitted only while fewer than this many admitted prompts stay
+ *                        unfinished; otherwise it is skipped this step (prompts behind it that
+ *                        finish within the step may still be admitted).
+ *   max_num_seqs         [P3] §10: sequences per step; the prompt walk stops at the cap.
+ *   policy               [P2] "Choosing the priority order": CB_POLICY_DECODE_FIRST, CB_POLICY_
+ *                        PREFILL_FIRST (the prompt walk gets the whole budget, decodes run in what
+ *                        is left), CB_POLICY_FAIR_SHARE (decodes get up to decode_share_pct of the
+ *                        budget, prompts the rest; a class's unused share goes to the other).
+ *   prefill_quota_pct    [P3] §08 and §16: under decode-first, while prompts wait, decodes use at
+ *                        most the budget minus ceil(pct * budget / 100).
+ * Under prefill-first, fair share, a quota, or a sequence cap with one of these, a decode that does
+ * not fit waits for a later step instead of failing: the decodes that have waited longest run
+ * first (running order breaks ties) and are emitted in running order; a decode deferred still
+ * holds its blocks.  Under plain decode-first, more decodes than the budget or max_num_seqs fail
+ * with CB_ERR_DECODE_OVER_BUDGET. 
  * ------------------------------------------------------------------------------------------- */
 typedef struct cb_sched cb_sched;
 
@@ -73,7 +100,15 @@ typedef struct {
                                 copied at create); NULL = 0, 1, ..., num_blocks - 1            */
   int32_t max_chunk;         /* 0 = no per-prompt cap (default); > 0 caps every chunk
                                 ([P2] "Chunked prefill as a rate control")                     */
+  int32_t prefill_floor;     /* 0 = off; > 0: the floor described above                        */
+  int32_t max_partial_prefills; /* 0 = no cap                                                  */
+  int32_t max_num_seqs;      /* 0 = no cap                                                     */
+  int32_t policy;            /* CB_POLICY_*; 0 = decode-first                                  */
+  int32_t decode_share_pct;  /* fair share: decodes' share of the budget, 1..99; 0 = 50        */
+  int32_t prefill_quota_pct; /* 0..100; 0 = off                                                */
 } cb_sched_config;
+
+enum { CB_POLICY_DECODE_FIRST = 0, CB_POLICY_PREFILL_FIRST = 1, CB_POLICY_FAIR_SHARE = 2 };
 
 /* Create a builder; *out receives it.  CB_ERR_INVALID on bad geometry or free list. */
 int cb_sched_create(const cb_sched_config* cfg, cb_sched** out);
@@ -97,6 +132,11 @@ int cb_sched_get_blocks(const cb_sched* s, int32_t req_id, int32_t* out, int32_t
 int cb_sched_pending_prompts(const cb_sched* s, int32_t* n);
 /* *n = blocks left in the free pool. */
 int cb_sched_free_blocks(const cb_sched* s, int32_t* n);
+/* Retire a request that has produced its last token: a running decode, or a prompt whose last
+ * chunk has run.  Its blocks are appended, in its block order, to the back of the free list.
+ * CB_ERR_INVALID for an unknown id or a prompt with tokens still to compute.  (The pages' decodes
+ * end when their output is complete; this call is how a caller, e.g. a step simulator, says so.) */
+int cb_sched_finish(cb_sched* s, int32_t req_id);
 
 /* One step's metadata.  The caller sets the capacities and the seven array pointers (host
  * memory; pinned memory lets the copy to the device run asynchronously); the library fills the

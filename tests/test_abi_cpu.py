@@ -119,17 +119,25 @@ def scenario(draw):
         st.tuples(st.just("run"), st.integers(0, 40)),
         st.tuples(st.just("prompt"), st.integers(0, 50), st.integers(-1, 50)),
         st.tuples(st.just("build"), st.integers(0, 24)),
+        st.tuples(st.just("finish"), st.integers(0, 40)),
         st.tuples(st.just("clone"), st.just(0))), max_size=40))
-    cap = draw(st.sampled_from([0, 0, 3]))
-    return bs, nb, perm, ops, cap
+    cfg = {"max_chunk": draw(st.sampled_from([0, 0, 3])),
+           "prefill_floor": draw(st.sampled_from([0, 0, 2, 5])),
+           "max_partial_prefills": draw(st.sampled_from([0, 0, 1, 2])),
+           "max_num_seqs": draw(st.sampled_from([0, 0, 2, 5])),
+           "policy": draw(st.sampled_from([0, 0, 1, 2])),
+           "decode_share_pct": draw(st.sampled_from([0, 30, 75])),
+           "prefill_quota_pct": draw(st.sampled_from([0, 0, 25, 100]))}
+    return bs, nb, perm, ops, cfg
 
 
 @settings(max_examples=300, deadline=None, suppress_health_check=[HealthCheck.too_slow])
 @given(scenario())
 def test_builder_matches_oracle_random(sc):
-    bs, nb, perm, ops, cap = sc
-    ref = RefBuilder(bs, nb, perm, max_chunk=cap)
-    s = cb.cb_sched_create(bs, nb, perm, max_chunk=cap)
+    # Every cap and priority policy (decode deferral included) and request retirement, mixed.
+    bs, nb, perm, ops, cfg = sc
+    ref = RefBuilder(bs, nb, perm, **cfg)
+    s = cb.cb_sched_create(bs, nb, perm, **cfg)
     buf = cb.StepBuffers(64, 32, 256, pin=False)
     rids = []
     for op in ops:
@@ -157,6 +165,19 @@ def test_builder_matches_oracle_random(sc):
             s2 = cb.cb_sched_clone(s)
             del s
             s = s2
+        elif op[0] == "finish":
+            if not rids:
+                continue
+            r = rids[op[1] % len(rids)]
+            try:
+                ref.finish(r)
+            except BuildError as e:
+                with pytest.raises(cb.CbError) as ce:
+                    cb.cb_sched_finish(s, r)
+                assert REASON[ce.value.status] == e.reason
+            else:
+                cb.cb_sched_finish(s, r)
+                rids.remove(r)
         else:
             try:
                 plan = ref.build(op[1])

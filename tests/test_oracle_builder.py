@@ -275,3 +275,180 @@ def test_invariants_exhaustive_small():
                     if b.pending_prompts() == 0:
                         for rid, L in zip(rids, lens):
                             assert hist[rid] == L
+
+
+# ---------------------------------------------------------------------------------------------
+# Caps and priority policies.
+# ---------------------------------------------------------------------------------------------
+from oracle.builder import DECODE_FIRST, FAIR_SHARE, PREFILL_FIRST  # noqa: E402
+
+
+def test_threshold_ceiling_gives_budget_over_threshold_partial_prefills():
+    # The sference.com post, "The fix": dividing the round's budget by the per-request threshold
+    # gives the number of partial prefills run at once: 8192 // 4096 = 2, 16384 // 4096 = 4.
+    for budget, want in ((8192, 2), (16384, 4)):
+        b = RefBuilder(16, 40000, max_chunk=4096)
+        rids = [b.add_prompt(100000) for _ in range(6)]
+        plan = b.build(budget)
+        assert plan["prefill_chunks"] == [(r, 4096) for r in rids[:want]]
+        assert plan["unused_tokens"] == 0
+
+
+def test_threshold_ceiling_idles_a_lone_long_prompt_and_the_floor_does_not():
+    # The same post, caveats and closing section: with the ceiling a lone long request is capped
+    # at the threshold and the rest of the budget idles; with the proposed floor one long prefill on
+    # its own takes all of the budget and two take half each.
+    ceil_b = RefBuilder(16, 40000, max_chunk=4096)
+    ceil_b.add_prompt(100000)
+    plan = ceil_b.build(8192)
+    assert plan["num_prefill_tokens"] == 4096 and plan["unused_tokens"] == 4096
+    floor_b = RefBuilder(16, 40000, prefill_floor=4096)
+    floor_b.add_prompt(100000)
+    plan = floor_b.build(8192)
+    assert plan["num_prefill_tokens"] == 8192 and plan["unused_tokens"] == 0
+    for floor in (1024, 2048, 4096):
+        two = RefBuilder(16, 40000, prefill_floor=floor)
+        a, c = two.add_prompt(100000), two.add_prompt(100000)
+        assert two.build(8192)["prefill_chunks"] == [(a, 4096), (c, 4096)]
+
+
+def test_floor_keeps_short_prompts_whole_and_shares_the_rest_evenly():
+    # Short prompts (at most the floor) are admitted whole; the long ones get at least the floor
+    # and split what is left evenly; an odd token goes to the first of them.
+    b = RefBuilder(16, 40000, prefill_floor=1000)
+    L1, S1, L2, S2 = b.add_prompt(50000), b.add_prompt(300), b.add_prompt(50000), b.add_prompt(700)
+    plan = b.build(5001)
+    # first pass: 1000 + 300 + 1000 + 700 = 3000; 2001 left, split 1001 / 1000 between L1 and L2
+    assert plan["prefill_chunks"] == [(L1, 2001), (S1, 300), (L2, 2000), (S2, 700)]
+
+
+def test_threshold_removes_head_of_line_blocking():
+    # The sference.com post, "One slot, one request": a cold 600,000-token prompt is followed by four
+    # small prompts and two 300,000-token prompts with a 99% cache hit.  Admitted whole, the big
+    # prompt holds the round's budget until it is done (74 rounds of 8192) and all six wait behind
+    # it; with the 4096-token threshold they all finish their prefill within the first rounds.
+    def first_token_rounds(max_chunk):
+        b = RefBuilder(64, 40000, max_chunk=max_chunk)
+        b.add_prompt(600000)
+        small = [b.add_prompt(2000) for _ in range(4)]
+        cached = [b.add_prompt(300000, 297000) for _ in range(2)]
+        done = {}
+        for rnd in range(1, 80):
+            plan = b.build(8192)
+            for w in b.waiting:
+                if w.done == w.length and w.rid not in done:
+                    done[w.rid] = rnd
+            if all(r in done for r in small + cached):
+                break
+        return [done.get(r) for r in small + cached]
+    # Admitted whole (by hand): rounds 1-73 give the big prompt 8192 each; round 74 its last 1984
+    # and then 2000 to each of the first three small prompts and 208 to the fourth; round 75 (the
+    # big one now decodes) finishes the fourth and both cached prompts.
+    assert first_token_rounds(0) == [74, 74, 74, 75, 75, 75]
+    # With the threshold (by hand): round 1 big 4096, small 2000 + 2000 + 96; round 2 big 4096,
+    # small 1904 (done) + 2000, cached 192; round 3 big 4096, cached 2808 (done) + 1288; round 4
+    # big 4096, cached 1712 (done).
+    assert first_token_rounds(4096) == [1, 1, 2, 2, 3, 4]
+
+
+def test_partial_prefill_cap_skips_only_prompts_that_would_stay_unfinished():
+    b = RefBuilder(16, 4096, max_chunk=30, max_partial_prefills=1)
+    p0, p1, p2, p3 = b.add_prompt(200), b.add_prompt(200), b.add_prompt(20), b.add_prompt(200)
+    plan = b.build(100)
+    assert plan["prefill_chunks"] == [(p0, 30), (p2, 20)]
+    assert plan["unused_tokens"] == 50
+
+
+def test_sequence_cap_limits_chunks_and_rejects_too_many_strict_decodes():
+    b = RefBuilder(16, 4096, max_num_seqs=5)
+    for _ in range(4):
+        b.add_running(10)
+    p0, p1 = b.add_prompt(100), b.add_prompt(100)
+    plan = b.build(64)
+    assert plan["num_seqs"] == 5 and plan["prefill_chunks"] == [(p0, 60)]
+    over = RefBuilder(16, 4096, max_num_seqs=3)
+    for _ in range(4):
+        over.add_running(10)
+    with pytest.raises(BuildError) as e:
+        over.build(64)
+    assert e.value.reason == "decode_over_budget"
+
+
+def test_prefill_quota_lets_a_prompt_finish_beside_decodes_that_never_drain():
+    # "Chunked Prefill 的 Token 预算" §16, third exercise: reserve at least 25% of every round for
+    # prefill, build traffic whose decodes never empty, and check the long prompt still finishes.
+    # Budget 16 with 16 decodes: strict decode-first never schedules the prompt; with the quota,
+    # decodes use at most 12 tokens, the prompt gets 4 per round and finishes in 40 / 4 rounds, and
+    # with 12 decode slots for 16 decodes each decode runs at least every second round.
+    strict = RefBuilder(16, 4096)
+    quota = RefBuilder(16, 4096, prefill_quota_pct=25)
+    for b in (strict, quota):
+        for _ in range(16):
+            b.add_running(10)
+        b.add_prompt(40)
+    for _ in range(30):
+        assert strict.build(16)["prefill_chunks"] == []
+    ran = []
+    for rnd in range(10):
+        plan = quota.build(16)
+        assert plan["num_decodes"] == 12 and plan["num_prefill_tokens"] == 4
+        ran.append(set(plan["decode_ids"]))
+    assert quota.pending_prompts() == 0
+    for a, c in zip(ran, ran[1:]):
+        assert a | c == set(range(16))
+    # prompt done: its first decode (round 11) competes like any other; no prompt waits, so the
+    # quota no longer holds anything back and all 17 decodes fit a budget of 17
+    assert quota.build(17)["num_decodes"] == 17
+
+
+def test_priority_policies_split_the_budget_as_named():
+    # "Splitting Prefill From Decode Inside a Step", "Choosing the priority order".
+    def run(policy, **kw):
+        b = RefBuilder(16, 4096, policy=policy, **kw)
+        for _ in range(4):
+            b.add_running(10)
+        b.add_prompt(100)
+        return b.build(16)
+    df = run(DECODE_FIRST)
+    assert (df["num_decodes"], df["num_prefill_tokens"]) == (4, 12)
+    pf = run(PREFILL_FIRST)                      # prompts take the budget, decodes get nothing
+    assert (pf["num_decodes"], pf["num_prefill_tokens"]) == (0, 16)
+    fs = run(FAIR_SHARE, decode_share_pct=50)    # decodes need 4 of their 8: prompts get 12
+    assert (fs["num_decodes"], fs["num_prefill_tokens"]) == (4, 12)
+    fs2 = run(FAIR_SHARE, decode_share_pct=10)   # decodes' share ceil(1.6) = 2; 14 to the prompt
+    assert (fs2["num_decodes"], fs2["num_prefill_tokens"]) == (2, 14)
+
+
+def test_prefill_first_runs_decodes_in_the_budget_the_prompts_leave():
+    b = RefBuilder(16, 4096, policy=PREFILL_FIRST)
+    for _ in range(4):
+        b.add_running(10)
+    p = b.add_prompt(10)
+    plan = b.build(16)
+    assert plan["prefill_chunks"] == [(p, 10)] and plan["num_decodes"] == 4
+    assert plan["unused_tokens"] == 2
+
+
+def test_deferred_decodes_run_longest_waiting_first():
+    b = RefBuilder(16, 4096, policy=FAIR_SHARE, decode_share_pct=25)
+    ids = [b.add_running(10) for _ in range(6)]
+    b.add_prompt(1000)
+    seen = [b.build(8)["decode_ids"] for _ in range(3)]     # 2 decode slots per round
+    assert seen == [ids[0:2], ids[2:4], ids[4:6]]
+
+
+def test_finish_returns_blocks_to_the_back_of_the_pool():
+    b = RefBuilder(4, 10)
+    d = b.add_running(6)                 # blocks 0, 1
+    p = b.add_prompt(3)                  # no cached blocks yet
+    b.build(8)                           # d grows? position 6 fits block 1; p reserves block 2
+    assert b.blocks_of(d) == [0, 1] and b.blocks_of(p) == [2]
+    with pytest.raises(BuildError):
+        b.finish(99)
+    b.finish(d)
+    assert list(b.free) == [3, 4, 5, 6, 7, 8, 9, 0, 1]
+    b.finish(p)                          # its last chunk has run: it may finish before decoding
+    assert list(b.free)[-1] == 2
+    q = b.add_prompt(5)
+    with pytest.raises(BuildError):
+        b.finish(q)                      # tokens still to compute
