@@ -151,6 +151,44 @@ def pct(xs, q):
     return xs[min(len(xs) - 1, max(0, int(round(q * (len(xs) - 1)))))]
 
 
+def linear_pass(w, dev, tokens: dict, reps: int = 20):
+    """The linear layers around the step (selective batching: one weight read serves every token of
+    the step): the QKV projection [T, Hq D] -> [T, (Hq + 2 Hkv) D] and the output projection
+    [T, Hq D] -> [T, Hq D], with seeded synthetic weights, timed with HIP events on the launch
+    stream at the decode-only and the mixed step's token counts."""
+    import torch
+    from chunked_prefill_mixed_decode_amd import binding as cb
+    from synth.values import matrix_values
+    d = w.Hq * w.D
+    layers = {"qkv_projection": (d, (w.Hq + 2 * w.Hkv) * w.D, "w_qkv"), "output_projection": (d, d, "w_o")}
+    res = {}
+    for lname, (K, N, wname) in layers.items():
+        wt = matrix_values(7, wname, N, K, scale=K ** -0.5, dtype=torch.bfloat16, device=dev)
+        for tname, T in tokens.items():
+            x = matrix_values(7, "hidden", T, K, dtype=torch.bfloat16, device=dev)
+            y = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
+            nws = cb.cb_linear_workspace_bytes(T, N, K)
+            ws = torch.empty(nws, dtype=torch.uint8, device=dev) if nws else None
+            cb.cb_linear(x, wt, y, ws)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                cb.cb_linear(x, wt, y, ws)
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) / reps * 1e3
+            flop = 2 * T * K * N
+            wbytes = K * N * 2
+            res[f"{lname}_{tname}"] = {
+                "tokens": T, "K": K, "N": N, "us": us, "TFLOPs": flop / us / 1e6,
+                "frac_mfma": flop / us / 1e6 / MFMA_BF16_PEAK_TFLOPS,
+                "weight_GBps": wbytes / us / 1e3,
+                "flop_per_weight_byte": flop / wbytes, "k_splits": nws // (T * N * 4) if nws else 1}
+            del x, y, ws
+        del wt
+    return res
+
+
 def summarize_isolated(dec, chk, metas, w, elt):
     """Roofline fractions of isolated launches: decode rows (bytes over attention + combine time)
     against HBM, chunk rows (FLOPs over chunk time) against bf16 MFMA, totals and per step."""
@@ -358,6 +396,8 @@ def main():
     iso_cold["note"] = "as isolated, with a 512 MiB device write before every launch (L2 and MALL cold)"
     del flush
     traffic = committed_traffic("attn_kernel")
+    lin = linear_pass(w, dev, {"decode_only": max(1, len(w.decode_ctx)),
+                               "mixed_step": max(m.num_tokens for m in metas)}) if w.dtype == "bf16" else None
 
     res = {
         "metric": METRIC,
@@ -382,6 +422,7 @@ def main():
                      "bytes_per_launch": sum(abytes) / len(abytes), "avg_launch_us": attn_avg_s * 1e6},
         "isolated": iso,
         "isolated_cold": iso_cold,
+        "linear_layers": lin,
         "combine_avg_us": sum(cmb_ms) / len(cmb_ms) * 1e3,
         "device_step_us": sum(dev_step_ms) / len(dev_step_ms) * 1e3,
         "device_step_us_p10_p50_p90": [pct(dev_step_ms, q) * 1e3 for q in (0.1, 0.5, 0.9)],

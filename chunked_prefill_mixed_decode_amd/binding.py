@@ -62,6 +62,8 @@ EXPORTS = {
     "cb_sched_add_prompt": (ctypes.c_int, [_vp, _i32, _i32, _pi32]),
     "cb_sched_get_blocks": (ctypes.c_int, [_vp, _i32, _pi32, _i32, _pi32]),
     "cb_sched_finish": (ctypes.c_int, [_vp, _i32]),
+    "cb_linear_workspace_bytes": (_sz, [_i32, _i32, _i32]),
+    "cb_linear": (ctypes.c_int, [_vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz]),
     "cb_sched_pending_prompts": (ctypes.c_int, [_vp, _pi32]),
     "cb_sched_free_blocks": (ctypes.c_int, [_vp, _pi32]),
     "cb_build_step": (ctypes.c_int, [_vp, _i32, ctypes.POINTER(cb_step)]),
@@ -289,6 +291,25 @@ def cb_rope_kv_append(q, k, v, positions, slot_mapping, cos_sin, q_out, k_cache,
         _stream(k, stream), dtype_code(k.dtype), T, max(Hq, 1), Hkv, D, bs, _ptr(q), _ptr(k), _ptr(v),
         _ptr(positions), _ptr(slot_mapping), _ptr(cos_sin), cos_sin.shape[0], _ptr(q_out),
         _ptr(k_cache), _ptr(v_cache), nb), "cb_rope_kv_append")
+
+
+def cb_linear_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(_lib().cb_linear_workspace_bytes(M, N, K))
+
+
+def cb_linear(x, w, y, workspace=None, stream=None):
+    """y [M, N] = x [M, K] . w [N, K]^T (bfloat16 device tensors, contiguous); ``workspace`` a device
+    tensor of at least cb_linear_workspace_bytes(M, N, K) bytes when that is not 0."""
+    M, K = x.shape
+    N = w.shape[0]
+    if w.shape[1] != K or tuple(y.shape) != (M, N):
+        raise ValueError("cb_linear: shapes do not match")
+    for t in (x, w, y):
+        if not t.is_contiguous():
+            raise ValueError("cb_linear: tensors must be contiguous")
+    nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(_lib().cb_linear(_stream(x, stream), dtype_code(x.dtype), M, N, K, _ptr(x), _ptr(w), _ptr(y),
+                            _ptr(workspace), nbytes), "cb_linear")
 
 
 def cb_attn_workspace_bytes(num_seqs, num_decodes, T, max_q_len, max_decode_ctx, max_ctx, Hq, Hkv, D) -> int:

@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libcb.so")
 
-SOURCES = ["sched.cpp", "host_copy.hip", "rope_append.hip", "attention.hip"]
+SOURCES = ["sched.cpp", "host_copy.hip", "rope_append.hip", "attention.hip", "linear.hip"]
 ARCH = "gfx950"
 
 

@@ -1,0 +1,233 @@
+// Linear layers around the attention step on gfx950: y[M, N] = x[M, K] . w[N, K]^T in bfloat16
+// with float32 accumulation -- the QKV projection before the rotary step and the output
+// projection after attention.
+//
+// "Chunked Prefill: Ending the Great Stall" §02: selective batching runs the linear layers over
+// all tokens of an iteration (decode and prefill alike) while attention runs per request; its
+// piggyback roofline (and "Splitting Prefill From Decode Inside a Step", "Two kernels with
+// different limiting resources"): the weights are read once per iteration and serve every token
+// in it, so T tokens give about T FLOP per weight byte (bf16) -- weight-bandwidth bound for a
+// decode-only step, compute bound once a prefill chunk joins.
+//
+// One 256-thread workgroup per 128 x 128 output tile and K split, 64-deep K stages: the x and w
+// tiles of a stage are copied HBM -> LDS with the gfx950 16-byte LDS DMA into a ring of two
+// stage buffers (the next stage's copy in flight behind the one being multiplied; 64 KB, so two
+// workgroups share a compute unit -- measured faster than three buffers and one workgroup), rows
+// chunk-swizzled (16-byte chunk c of row r at c ^ (r mod 8), so the 32 rows an operand read
+// touches at one chunk spread over all 16-byte bank groups); each wave computes a 64 x 64 quarter
+// with v_mfma_f32_32x32x16_bf16.  Tiles are ordered so that the workgroups sharing one weight tile
+// run on one XCD (workgroup b runs on XCD b mod 8) and read it through that XCD's L2.  A layer
+// with few tiles (a decode-only step's rows) splits K so that at least 256 workgroups stream the
+// weights: each split writes float32 partials and a second kernel sums them in split order (the
+// split depends on the shape alone, so results do not depend on the device).
+#include <algorithm>
+
+#include "cb.h"
+#include "common.h"
+
+namespace cb {
+namespace {
+
+constexpr int kBM = 128, kBN = 128, kBK = 64;
+constexpr int kRowBytes = kBK * 2;                 // bytes of one tile row in one stage
+constexpr int kTileBytes = kBM * kRowBytes;        // 16 KB (the x tile; the w tile is the same)
+#ifndef CB_LINEAR_STAGES
+#define CB_LINEAR_STAGES 2                         // LDS ring depth (stage buffers of 32 KB)
+#endif
+#ifndef CB_LINEAR_MIN_WG
+#define CB_LINEAR_MIN_WG 256                       // K is split until the grid has this many
+#endif
+constexpr int kStages = CB_LINEAR_STAGES;
+static_assert(kStages == 2 || kStages == 3, "ring depth");
+constexpr int kCopiesPerStage = 8;                 // DMA instructions per wave per stage
+constexpr int64_t kMinWorkgroups = CB_LINEAR_MIN_WG;
+constexpr int kMaxSplit = 16;
+constexpr int kMinStagesPerSplit = 4;
+static_assert(kBM == kBN, "one copy layout for both operands");
+
+// K splits for a shape: the smallest power of two giving kMinWorkgroups workgroups, at most
+// kMaxSplit, dividing the K stages evenly and keeping kMinStagesPerSplit stages per split.
+int32_t k_splits(int64_t tiles, int32_t K) {
+  const int32_t stages = K / kBK;
+  int32_t s = 1;
+  while (s < kMaxSplit && tiles * s < kMinWorkgroups && stages % (2 * s) == 0 &&
+         stages / (2 * s) >= kMinStagesPerSplit)
+    s *= 2;
+  return s;
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)(p)));
+}
+// One 16-byte-per-lane LDS DMA: lane l's 16 bytes from src land at lds_dst + 16 l.  Issued from
+// inline asm, so the compiler adds no waits for it; the loop below waits for its copies itself.
+// M0 carries the wave-uniform LDS destination (saved and restored; one wait state after writing it).
+__device__ __forceinline__ void dma16(const void* src, const char* lds_dst) {
+  const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(lds_dst));
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(dst));
+}
+__device__ __forceinline__ int swz(int c, int r) { return c ^ (r & 7); }
+
+__global__ __launch_bounds__(256) void linear_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict__ w,
+                                                     bf16_t* __restrict__ y, float* __restrict__ part,
+                                                     int32_t M, int32_t N, int32_t K, int32_t m_tiles,
+                                                     int32_t splits, int32_t items, int32_t per_xcd) {
+  __shared__ __attribute__((aligned(1024))) char lds[kStages * 2 * kTileBytes];   // [stage][x | w]
+  const int32_t b = blockIdx.x;
+  const int32_t it = (b & 7) * per_xcd + (b >> 3);   // item = (tile, split), split fastest
+  if (it >= items) return;
+  const int32_t t = it / splits, split = it - t * splits;
+  const int32_t m0 = (t % m_tiles) * kBM, n0 = (t / m_tiles) * kBN;
+  const int32_t nk = K / kBK / splits, kt0 = split * nk;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // Copy j of this wave fills tile bytes [1024 (4 wave + j), + 1024): rows 8 (4 wave + j) + lane / 8,
+  // physical chunk lane % 8 (logical chunk lane % 8 ^ row % 8).  Rows of x past M repeat row M - 1
+  // (their results are not stored).
+  const char* xs[4];
+  const char* ws[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = 8 * (4 * wave + j) + (lane >> 3);
+    const int c = swz(lane & 7, r);
+    xs[j] = reinterpret_cast<const char*>(x + static_cast<int64_t>(std::min(m0 + r, M - 1)) * K) + 16 * c;
+    ws[j] = reinterpret_cast<const char*>(w + static_cast<int64_t>(n0 + r) * K) + 16 * c;
+  }
+  auto issue = [&](int32_t kt, int buf) {
+    const char* xt = lds + buf * 2 * kTileBytes;
+    const char* wt = xt + kTileBytes;
+    const int64_t koff = static_cast<int64_t>(kt0 + kt) * kRowBytes;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      dma16(xs[j] + koff, xt + 1024 * (4 * wave + j));
+      dma16(ws[j] + koff, wt + 1024 * (4 * wave + j));
+    }
+  };
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int lr = lane & 31, lh = lane >> 5;
+  // Copies run kStages - 1 stages ahead of the matrix work.
+  for (int p = 0; p < kStages - 1; ++p)
+    if (p < nk) issue(p, p);
+  for (int32_t kt = 0; kt < nk; ++kt) {
+    // This wave's copies of stage kt have landed once at most the later stages' copies already
+    // issued are outstanding (copies complete in issue order); after the barrier every wave's have,
+    // and every wave has finished reading stage kt - 1's buffer, which the next copy overwrites.
+    if (kStages == 3 && kt + 1 < nk) asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kCopiesPerStage) : "memory");
+    else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    if (kt + kStages - 1 < nk) issue(kt + kStages - 1, (kt + kStages - 1) % kStages);
+    const char* xt = lds + (kt % kStages) * 2 * kTileBytes;
+    const char* wt = xt + kTileBytes;
+#pragma unroll
+    for (int kk = 0; kk < kBK / 16; ++kk) {
+      const int c = 2 * kk + lh;                   // 16-byte chunk: slots 8 (l / 32) .. + 7 of step kk
+      Frag<bf16_t> a[2], bw[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int r = 64 * wm + 32 * i + lr;
+        a[i].u = *reinterpret_cast<const uint4*>(xt + r * kRowBytes + 16 * swz(c, r));
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int r = 64 * wn + 32 * j + lr;
+        bw[j].u = *reinterpret_cast<const uint4*>(wt + r * kRowBytes + 16 * swz(c, r));
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) mma32_k16(acc[i][j], a[i], bw[j]);
+    }
+  }
+
+  // acc[i][j] register r: row 64 wm + 32 i + acc32_row(lane, r), column 64 wn + 32 j + lane % 32.
+  float* pt = splits > 1 ? part + static_cast<int64_t>(split) * M * N : nullptr;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int32_t row = m0 + 64 * wm + 32 * i + acc32_row(lane, r);
+      if (row >= M) continue;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int64_t o = static_cast<int64_t>(row) * N + n0 + 64 * wn + 32 * j + lr;
+        if (pt) pt[o] = acc[i][j][r];
+        else reinterpret_cast<uint16_t*>(y)[o] = f32_to_bf16_bits(acc[i][j][r]);
+      }
+    }
+}
+
+// y = the splits' partials summed in split order, rounded once to bfloat16 (4 outputs a thread).
+__global__ __launch_bounds__(256) void linear_reduce_kernel(const float* __restrict__ part, bf16_t* __restrict__ y,
+                                                            int64_t n4, int64_t stride, int32_t splits) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n4; i += static_cast<int64_t>(gridDim.x) * 256) {
+    float4 s = reinterpret_cast<const float4*>(part)[i];
+    for (int32_t k = 1; k < splits; ++k) {
+      const float4 v = reinterpret_cast<const float4*>(part + k * stride)[i];
+      s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+    }
+    reinterpret_cast<uint2*>(y)[i] = make_uint2(pack_bf16x2(s.x, s.y), pack_bf16x2(s.z, s.w));
+  }
+}
+
+}  // namespace
+}  // namespace cb
+
+extern "C" size_t cb_linear_workspace_bytes(int32_t M, int32_t N, int32_t K) {
+  using namespace cb;
+  if (M < 1 || N < 1 || K < 1 || N % kBN || K % kBK) return 0;
+  const int64_t tiles = ((static_cast<int64_t>(M) + kBM - 1) / kBM) * (N / kBN);
+  const int32_t s = k_splits(tiles, K);
+  return s > 1 ? static_cast<size_t>(s) * M * N * sizeof(float) : 0;
+}
+
+extern "C" int cb_linear(void* stream, int32_t dtype, int32_t M, int32_t N, int32_t K, const void* x,
+                         const void* w, void* y, void* workspace, size_t workspace_bytes) {
+  using namespace cb;
+  if (dtype != CB_BF16) return CB_ERR_INVALID;
+  if (M < 0 || N < 1 || K < 1 || N % kBN || K % kBK) return CB_ERR_INVALID;
+  if (M == 0) return CB_OK;
+  if (!x || !w || !y) return CB_ERR_INVALID;
+  for (const void* p : {x, w, static_cast<const void*>(y)})
+    if (reinterpret_cast<uintptr_t>(p) & 15u) return CB_ERR_INVALID;
+  const int64_t m_tiles = (static_cast<int64_t>(M) + kBM - 1) / kBM;
+  const int64_t tiles = m_tiles * (N / kBN);
+  const int32_t splits = k_splits(tiles, K);
+  if (splits > 1) {
+    if (workspace_bytes < cb_linear_workspace_bytes(M, N, K)) return CB_ERR_CAPACITY;
+    if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 15u)) return CB_ERR_INVALID;
+  }
+  const int64_t items = tiles * splits;
+  const int64_t per_xcd = (items + 7) / 8;
+  if (per_xcd * 8 > 0x7fffffff) return CB_ERR_INVALID;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  float* part = static_cast<float*>(workspace);
+  linear_kernel<<<dim3(static_cast<uint32_t>(per_xcd * 8)), dim3(256), 0, st>>>(
+      static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(w), static_cast<bf16_t*>(y), part, M, N, K,
+      static_cast<int32_t>(m_tiles), splits, static_cast<int32_t>(items), static_cast<int32_t>(per_xcd));
+  if (hipGetLastError() != hipSuccess) return CB_ERR_HIP;
+  if (splits > 1) {
+    const int64_t n4 = static_cast<int64_t>(M) * N / 4;
+    const int64_t grid = std::min<int64_t>((n4 + 255) / 256, 4096);
+    linear_reduce_kernel<<<dim3(static_cast<uint32_t>(grid)), dim3(256), 0, st>>>(
+        part, static_cast<bf16_t*>(y), n4, static_cast<int64_t>(M) * N, splits);
+    if (hipGetLastError() != hipSuccess) return CB_ERR_HIP;
+  }
+  return CB_OK;
+}

@@ -172,6 +172,25 @@ int cb_build_step(cb_sched* s, int32_t token_budget, cb_step* out);
 int cb_copy_host_to_device(void* stream, const void* src, void* dst, size_t nbytes);
 
 /* ---------------------------------------------------------------------------------------------
+ * Linear layers (device).  [P1] §02: selective batching runs the linear layers of an iteration
+ * over all its tokens, decode and prefill alike; [P1]'s piggyback roofline and [P2] "Two kernels
+ * with different limiting resources": one step reads the weights once, so T tokens perform about
+ * T FLOP per bf16 weight byte.  y[m, n] = sum_k x[m, k] * w[n, k]: x [M, K] (the step's token rows,
+ * e.g. hidden states before the QKV projection or attention outputs before the output
+ * projection), w [N, K] (out_features x in_features), y [M, N]; row-major bfloat16 device
+ * memory, float32 accumulation, one rounding to bfloat16 per output.  dtype must be CB_BF16;
+ * M >= 0 (0 = nothing to do), N a multiple of 128, K a multiple of 64; x, w and y 16-byte aligned
+ * and y not overlapping x or w.  A shape with few output tiles splits K over several workgroups:
+ * their float32 partials go to the caller's device workspace (16-byte aligned, at least
+ * cb_linear_workspace_bytes(M, N, K) bytes; NULL when that is 0) and are summed in a fixed order,
+ * so results are bitwise reproducible and depend on the shape only.  Asynchronous on the stream;
+ * CB_ERR_INVALID on a bad argument, CB_ERR_CAPACITY when the workspace is too small, CB_ERR_HIP
+ * when a launch fails. */
+size_t cb_linear_workspace_bytes(int32_t M, int32_t N, int32_t K);
+int cb_linear(void* stream, int32_t dtype, int32_t M, int32_t N, int32_t K, const void* x,
+              const void* w, void* y, void* workspace, size_t workspace_bytes);
+
+/* ---------------------------------------------------------------------------------------------
  * Rotary table (host).  [P3] §07: the rotary phase follows the absolute position, so a chunk's
  * rows must not restart at 0.  The variant is this library's reading (the pages fix none):
  * rotate-half over the full head dimension, theta_i = base^(-2i/D) in double precision,

@@ -6,10 +6,15 @@ binding) never touches it, and this package imports nothing from the product pat
 
 Parts, each a plain and slow restatement of what the pages define:
 
-* ``builder``   -- the decode-first, FCFS, token-budget batch builder and its block pool.
+* ``builder``   -- the decode-first, FCFS, token-budget batch builder and its block pool, with
+                   the optional caps and priority policies.
 * ``rope``      -- the rotary table and its fp32 evaluation; bf16 round-to-nearest-even.
 * ``attention`` -- non-chunked full-prefill causal attention in fp64 for any set of rows, and the
                    expected contents of the paged KV cache.
+* ``linear``    -- the linear layers around attention (x . w^T in fp64) and the bound a float32
+                   sum rounded to bfloat16 stays within.
+* ``sim``       -- a step-by-step simulation over the reference builder: time to first token and
+                   time between tokens, in steps.
 
 Pinned by the ``-m "not gpu"`` tests against the pages' printed examples, closed forms,
 invariants and brute force.  One convention has no pin in the pages: the rotary variant

@@ -152,3 +152,29 @@ def rows_values(seed: int, tensor: str, reqs, pos, n_heads: int, dim: int,
         ctr = rb[:, None, None] + hd[None, :, :]
         out[r0:r0 + rows] = table[_lsr(splitmix64_at(seed, ctr), 64 - TABLE_BITS)]
     return out
+
+
+# ---- matrices (linear-layer weights and hidden states) -----------------------------------------
+# A matrix named ``name`` draws from its own SplitMix64 stream: seed' = seed + MATRIX_SEED[name] *
+# gamma, number ``row * cols + col``.  Values are the same normal-quantile table entries, times
+# ``scale`` in fp32 (one rounding), then rounded into ``dtype``.
+MATRIX_SEED = {"hidden": 101, "w_qkv": 102, "w_o": 103, "attn_out": 104}
+
+
+def matrix_values(seed: int, name: str, rows: int, cols: int, scale: float = 1.0,
+                  dtype: torch.dtype = torch.float32, device="cpu",
+                  max_elems: int = 1 << 25) -> torch.Tensor:
+    """A ``[rows, cols]`` matrix of approximately N(0, scale**2) values."""
+    if rows < 0 or cols < 0:
+        raise ValueError("bad shape")
+    s = _signed(seed + MATRIX_SEED[name] * GAMMA)
+    table = quantile_table(torch.float32, device)
+    out = torch.empty((rows, cols), dtype=dtype, device=device)
+    step = max(1, max_elems // max(1, cols))
+    col = torch.arange(cols, dtype=torch.int64, device=device)
+    for r0 in range(0, rows, step):
+        r = torch.arange(r0, min(rows, r0 + step), dtype=torch.int64, device=device)
+        ctr = r[:, None] * cols + col[None, :]
+        v = table[_lsr(splitmix64_at(s, ctr), 64 - TABLE_BITS)]
+        out[r0:r0 + step] = (v * torch.tensor(scale, dtype=torch.float32, device=device)).to(dtype)
+    return out

@@ -259,3 +259,16 @@ def test_workspace_grows_with_context_and_rows():
     gqa = f(4, 4, 4, 1, 5000, 5000, 56, 8, 128)        # group of 7 heads per unit
     assert gqa <= (4 * 8 + 8192) * 7 * 130 * 4 + 5 * 4 + 8192 * 4 + 16 + 5 * 256
     assert f(0, 0, 0, 0, 0, 0, 32, 32, 128) == 0
+
+
+def test_linear_workspace_depends_on_the_shape_only():
+    f = cb.cb_linear_workspace_bytes
+    # enough 128 x 128 tiles: no split, no workspace
+    assert f(512, 12288, 4096) == 0
+    # few tiles: K splits (a power of two dividing the 64-deep stages, >= 4 stages each)
+    s = f(64, 4096, 4096) // (64 * 4096 * 4)
+    assert s in (2, 4, 8, 16) and f(64, 4096, 4096) == s * 64 * 4096 * 4
+    assert f(64, 4096, 64 * 34) % (64 * 4096 * 4) == 0 and (34 % (f(64, 4096, 64 * 34) // (64 * 4096 * 4) or 1)) == 0
+    assert f(1, 128, 64) == 0                               # one stage: nothing to split
+    for bad in ((0, 128, 64), (4, 100, 64), (4, 128, 96)):
+        assert f(*bad) == 0
