@@ -78,10 +78,15 @@ def chunk_flops(meta, w) -> int:
     return int((pos + 1).sum()) * 4 * w.D * w.Hq
 
 
-def committed_traffic(kernel: str):
+TRAFFIC_WORKLOAD = "cfg2_7b_b512_bf16"     # the workload the committed counter summary covers
+
+
+def committed_traffic(kernel: str, workload: str):
     """HBM bytes per launch of ``kernel`` from the committed counter summary, or None when the
-    attention source has changed since the counters were taken."""
+    summary covers another workload or the attention source has changed since it was taken."""
     import hashlib
+    if workload != TRAFFIC_WORKLOAD:
+        return None
     path = os.path.join(ROOT, "profiles", "hbm_traffic_b512_7b_layer.json")
     src = os.path.join(ROOT, "chunked_prefill_mixed_decode_amd", "csrc", "attention.hip")
     try:
@@ -395,7 +400,7 @@ def main():
     iso_cold = summarize_isolated(*isolation_pass(g, metas, qrots, outs, w, reps=2, flush=flush), metas, w, elt)
     iso_cold["note"] = "as isolated, with a 512 MiB device write before every launch (L2 and MALL cold)"
     del flush
-    traffic = committed_traffic("attn_kernel")
+    traffic = committed_traffic("attn_kernel", w.name)
     lin = linear_pass(w, dev, {"decode_only": max(1, len(w.decode_ctx)),
                                "mixed_step": max(m.num_tokens for m in metas)}) if w.dtype == "bf16" else None
 
