@@ -49,6 +49,10 @@ def parse():
                     help="record the per-kernel and per-step HIP events on every n-th timed step "
                          "(each event record costs the GPU a few microseconds; 7 is coprime with "
                          "the ten-step cycle, so every step kind is sampled)")
+    ap.add_argument("--graphs", action="store_true",
+                    help="also time the same steps replayed from HIP graphs (one graph per step of "
+                         "the cycle, captured on its first occurrence) and report it beside the "
+                         "eager figures")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one device copy of this many MiB before timing (a known-size kernel "
                          "for scaling profiler byte counters)")
@@ -384,6 +388,43 @@ def main():
     attn_avg_s = sum(dec_ms) / len(dec_ms) / 1e3
     achieved = sum(abytes) / len(abytes) / attn_avg_s / 1e9
 
+    graph_rep = None
+    if args.graphs:
+        from chunked_prefill_mixed_decode_amd.runner import StepGraphs
+        graphs = StepGraphs(g.runner)
+        state["sched"], state["k"] = cb.cb_sched_clone(snapshot), 0
+
+        def graph_step():
+            k = state["k"]
+            meta = g.runner.build(state["sched"], w.budget)
+            q, kk, vv = inputs[k]
+
+            def launch(dev_meta):
+                g.runner.append(dev_meta, q, kk, vv, qrots[k])
+                g.runner.attend(meta, dev_meta, qrots[k], outs[k])
+            mode = graphs.step(meta, launch)
+            state["k"] = k + 1
+            if state["k"] == cb_steps:
+                state["k"] = 0
+                state["sched"] = cb.cb_sched_clone(snapshot)
+            return meta.num_tokens, mode
+        for _ in range(2 * cb_steps):                  # capture every step of the cycle
+            graph_step()
+        torch.cuda.synchronize()
+        gtok, modes = 0, set()
+        t1 = time.perf_counter()
+        for _ in range(args.steps):
+            n, mode = graph_step()
+            gtok += n
+            modes.add(mode)
+        torch.cuda.synchronize()
+        gel = time.perf_counter() - t1
+        graph_rep = {"value": gtok / gel, "unit": "tokens/s", "ms_per_step": gel / args.steps * 1e3,
+                     "eager_ms_per_step": el / args.steps * 1e3, "graphs": len(graphs.graphs),
+                     "all_replayed": modes == {"replay"},
+                     "note": "the same steps replayed from one HIP graph per step of the cycle"}
+        state["sched"], state["k"] = cb.cb_sched_clone(snapshot), 0
+
     # End-to-end latency: host wall time from cb_build_step to stream sync after attention.
     e2e = []
     for _ in range(min(args.steps, 3 * cb_steps)):
@@ -433,6 +474,7 @@ def main():
         "device_step_us_p10_p50_p90": [pct(dev_step_ms, q) * 1e3 for q in (0.1, 0.5, 0.9)],
         "end_to_end_ms_p10_p50_p90": [pct(e2e, q) for q in (0.1, 0.5, 0.9)],
         "event_sampled_steps": len(sampled),
+        "graph_replay": graph_rep,
     }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)...", file=sys.stderr, flush=True)

@@ -56,14 +56,22 @@ class MixedStepRunner:
     def upload(self, meta: cb.StepMeta) -> dict:
         """cb_copy_host_to_device of the step's metadata on the current stream (a kernel, so the
         kernels that follow need no cross-queue wait).  Returns device int32 views."""
+        dev = self.pull(meta)
+        self.mark_pulled(meta)
+        return dev
+
+    def pull(self, meta: cb.StepMeta) -> dict:
+        """The metadata-pull kernel alone (device work only; see upload)."""
         i = meta.buf_index
         buf, dev = self.bufs[i], self.dev_flat[i]
-        stream = torch.cuda.current_stream(self.device)
-        cb.cb_copy_host_to_device(buf.flat, dev, stream=stream)
-        ev = torch.cuda.Event()
-        ev.record(stream)
-        self.copied[i] = ev
+        cb.cb_copy_host_to_device(buf.flat, dev, stream=torch.cuda.current_stream(self.device))
         return {k: dev[buf.offsets[k]:buf.offsets[k] + n] for k, n in meta.lengths().items()}
+
+    def mark_pulled(self, meta: cb.StepMeta):
+        """Record that the pinned buffer of ``meta`` may be rewritten once the stream gets here."""
+        ev = torch.cuda.Event()
+        ev.record(torch.cuda.current_stream(self.device))
+        self.copied[meta.buf_index] = ev
 
     # ---- device work ---------------------------------------------------------------------------
     def append(self, dev: dict, q, k, v, q_out):
@@ -93,3 +101,54 @@ class MixedStepRunner:
             num_seqs=meta.num_seqs, num_decodes=meta.num_decodes, max_q_len=meta.max_q_len,
             max_decode_ctx=meta.max_decode_context_len, max_ctx=meta.max_context_len,
             scale=self.scale, events=events)
+
+
+class StepGraphs:
+    """Whole steps (metadata pull, rope + append, attention) replayed from HIP graphs.
+
+    A captured step bakes in every pointer and every scalar its launches take (token count,
+    sequence counts, the longest query and context, the split plan), so a graph serves exactly the
+    steps whose launch parameters equal those it was captured with: ``key(meta)`` below, plus the
+    pinned buffer the step was built into (the pull reads it by address).  The caller keeps the
+    step's device tensors (inputs, q_rot, out) at fixed addresses per key and sizes the workspace
+    before the first capture (a reallocation drops every graph).  The first step with a new key
+    runs eagerly once (the capture's warm-up) and is then captured; later ones replay.  No timing
+    events are recorded inside a graph, and nothing in the captured work clears memory with a
+    memset.
+    """
+
+    def __init__(self, runner: MixedStepRunner):
+        self.runner = runner
+        self.graphs = {}
+        self.workspace_ptr = None
+        self.side = torch.cuda.Stream(device=runner.device)
+
+    @staticmethod
+    def key(meta: cb.StepMeta) -> tuple:
+        return (meta.buf_index, meta.num_seqs, meta.num_decodes, meta.num_tokens, meta.max_q_len,
+                meta.max_context_len, meta.max_decode_context_len)
+
+    def step(self, meta: cb.StepMeta, launch) -> str:
+        """Run ``launch(dev)`` -- the step's device work after the pull, given the device views --
+        for ``meta``: replayed when a graph for its key exists, else eagerly and then captured.
+        Returns "replay" or "captured"."""
+        r = self.runner
+        if self.workspace_ptr != r.workspace.data_ptr():
+            self.graphs.clear()
+            self.workspace_ptr = r.workspace.data_ptr()
+        k = self.key(meta)
+        g = self.graphs.get(k)
+        cur = torch.cuda.current_stream(r.device)
+        if g is not None:
+            g.replay()
+            r.mark_pulled(meta)
+            return "replay"
+        launch(r.pull(meta))                       # eager run (also the capture's warm-up)
+        r.mark_pulled(meta)
+        g = torch.cuda.CUDAGraph()
+        self.side.wait_stream(cur)
+        with torch.cuda.graph(g, stream=self.side):
+            launch(r.pull(meta))
+        cur.wait_stream(self.side)
+        self.graphs[k] = g
+        return "captured"
