@@ -78,7 +78,10 @@ EXPORTS = {
     "cb_mixed_paged_attention_timed": (ctypes.c_int, [_vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                                       _i32, _i32, _i32, _i32, _i32, _f32, _vp,
                                                       _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
-                                                      _sz, ctypes.POINTER(_vp)]),
+                                                      _sz, _vp, _i32, ctypes.POINTER(_vp)]),
+    "cb_attn_decode_waves": (_i32, [_vp, _i32]),
+    "cb_decode_plan_ints": (_sz, [_i32, _i32]),
+    "cb_decode_plan": (ctypes.c_int, [_pi32, _i32, _i32, _i32, _i32, _pi32, _sz]),
 }
 
 
@@ -210,23 +213,28 @@ class StepBuffers:
     """Host int32 arrays that cb_build_step fills, packed in one flat buffer (pinned when a GPU is
     present) so that a step's metadata reaches the device in a single asynchronous copy."""
 
-    def __init__(self, cap_seqs: int, cap_tokens: int, cap_blocks: int, pin: bool | None = None):
+    def __init__(self, cap_seqs: int, cap_tokens: int, cap_blocks: int, pin: bool | None = None,
+                 plan_ints: int = 0):
         if pin is None:
             pin = torch.cuda.is_available()
         self.cap = (cap_seqs, cap_tokens, cap_blocks)
         sizes = {"seq_ids": cap_seqs, "cu_seqlens_q": cap_seqs + 1, "context_lens": cap_seqs,
                  "cu_blocks": cap_seqs + 1, "block_table": max(cap_blocks, 1),
                  "positions": max(cap_tokens, 1), "slot_mapping": max(cap_tokens, 1)}
+        names = STEP_ARRAYS
+        if plan_ints:                                  # a host-made decode plan travels along
+            sizes["decode_plan"] = plan_ints
+            names = STEP_ARRAYS + ("decode_plan",)
         self.offsets = {}
         off = 0
-        for k in STEP_ARRAYS:
+        for k in names:
             self.offsets[k] = off
             off += (sizes[k] + 63) // 64 * 64          # 256-byte aligned sub-arrays
         self.flat = torch.zeros(off, dtype=torch.int32, pin_memory=pin)
-        self.arrays = {k: self.flat[self.offsets[k]:self.offsets[k] + sizes[k]] for k in STEP_ARRAYS}
+        self.arrays = {k: self.flat[self.offsets[k]:self.offsets[k] + sizes[k]] for k in names}
         self.step = cb_step()
-        for k, t in self.arrays.items():
-            setattr(self.step, k, _i32ptr(t))
+        for k in STEP_ARRAYS:
+            setattr(self.step, k, _i32ptr(self.arrays[k]))
 
 
 @dataclasses.dataclass
@@ -317,20 +325,50 @@ def cb_attn_workspace_bytes(num_seqs, num_decodes, T, max_q_len, max_decode_ctx,
                                               max_ctx, Hq, Hkv, D))
 
 
+def cb_attn_decode_waves(device_or_stream=None, has_chunks: bool = True) -> int:
+    """Decode waves an attention call launches on the device of the stream (default: current)."""
+    st = device_or_stream
+    if st is None or isinstance(st, (torch.device, int, str)):
+        st = torch.cuda.current_stream(st).cuda_stream
+    elif isinstance(st, torch.cuda.Stream):
+        st = st.cuda_stream
+    return int(_lib().cb_attn_decode_waves(ctypes.c_void_p(st), int(bool(has_chunks))))
+
+
+def cb_decode_plan_ints(num_decodes: int, n_waves: int) -> int:
+    return int(_lib().cb_decode_plan_ints(num_decodes, n_waves))
+
+
+def cb_decode_plan(context_lens, Hq: int, Hkv: int, n_waves: int, out) -> None:
+    """context_lens: host int32 tensor of the decode rows' context lengths; out: host int32 tensor
+    of at least cb_decode_plan_ints(len(context_lens), n_waves) entries."""
+    if context_lens.dtype != torch.int32 or out.dtype != torch.int32 or context_lens.is_cuda or out.is_cuda:
+        raise ValueError("cb_decode_plan: int32 host tensors")
+    if not context_lens.is_contiguous() or not out.is_contiguous():
+        raise ValueError("cb_decode_plan: contiguous tensors")
+    _check(_lib().cb_decode_plan(_i32ptr(context_lens), context_lens.numel(), Hq, Hkv, n_waves,
+                                 _i32ptr(out), out.numel()), "cb_decode_plan")
+
+
 def cb_mixed_paged_attention(q, k_cache, v_cache, cu_seqlens_q, context_lens, cu_blocks,
                              block_table, out, workspace, *, num_seqs, num_decodes, max_q_len,
-                             max_decode_ctx, max_ctx, scale, stream=None, events=None):
-    """q, out [T, Hq, D]; caches [nb, Hkv, bs, D]; int32 metadata on the device."""
+                             max_decode_ctx, max_ctx, scale, stream=None, events=None,
+                             decode_plan=None, plan_waves: int = 0):
+    """q, out [T, Hq, D]; caches [nb, Hkv, bs, D]; int32 metadata on the device; decode_plan: the
+    device copy of a cb_decode_plan output (or None: the split runs on the device)."""
     T, Hq, D = q.shape
     _, Hkv, bs, _ = k_cache.shape
     args = (_stream(q, stream), dtype_code(q.dtype), num_seqs, num_decodes, T, max_q_len,
             max_decode_ctx, max_ctx, Hq, Hkv, D, bs, scale, _ptr(q), _ptr(k_cache), _ptr(v_cache),
             _ptr(cu_seqlens_q), _ptr(context_lens), _ptr(cu_blocks), _ptr(block_table), _ptr(out),
             _ptr(workspace), workspace.numel() * workspace.element_size() if workspace is not None else 0)
-    if events is None:
+    if events is None and decode_plan is None:
         _check(_lib().cb_mixed_paged_attention(*args), "cb_mixed_paged_attention")
     else:
-        if len(events) != 6:
-            raise ValueError("events: six torch.cuda.Event (or None) entries")
-        ev = (_vp * 6)(*[ctypes.c_void_p(e.cuda_event) if e is not None else None for e in events])
-        _check(_lib().cb_mixed_paged_attention_timed(*args, ev), "cb_mixed_paged_attention_timed")
+        ev = None
+        if events is not None:
+            if len(events) != 6:
+                raise ValueError("events: six torch.cuda.Event (or None) entries")
+            ev = (_vp * 6)(*[ctypes.c_void_p(e.cuda_event) if e is not None else None for e in events])
+        _check(_lib().cb_mixed_paged_attention_timed(*args, _ptr(decode_plan), plan_waves, ev),
+               "cb_mixed_paged_attention_timed")

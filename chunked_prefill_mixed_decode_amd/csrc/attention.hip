@@ -1094,20 +1094,28 @@ int compute_units(hipStream_t st) {
   return cached[dev];
 }
 
-// Decode stage split (prep), the attention kernel (decode waves and chunk tiles together) and the
-// combine, in order on the caller's stream.
+// Decode waves of an attention launch on the stream's device: four per decode workgroup, one
+// workgroup per compute unit beside chunk tiles, two when there are none.
+int32_t decode_waves(hipStream_t st, bool has_chunks) {
+  const int cus8 = (compute_units(st) + 7) / 8 * 8;
+  return 4 * std::min(kMaxDecodeWaves / 4, (has_chunks ? CB_DECODE_WG_PER_CU_MIXED : CB_DECODE_WG_PER_CU) * cus8);
+}
+
+// The launches of one call, in order on the caller's stream: the decode stage split (skipped with
+// a host-made plan, which a.dec_seq / dec_wave / dec_par then point into), the attention kernel
+// (decode waves and chunk tiles together) and the combine.
 template <typename T, int D>
-int launch_all(hipStream_t st, const AttnArgs& a, const Plan& p, void* const* events) {
+int launch_all(hipStream_t st, const AttnArgs& a, const Plan& p, void* const* events, bool planned) {
   auto rec = [&](int i) {
     if (events && events[i]) (void)hipEventRecord(static_cast<hipEvent_t>(events[i]), st);
   };
-  // Decode workgroups: one per compute unit beside chunk tiles, two when there are none.
   int32_t n_dec_wg = 0;
   if (a.nd > 0) {
-    const int cus8 = (compute_units(st) + 7) / 8 * 8;
-    n_dec_wg = std::min(kMaxDecodeWaves / 4, (a.n_chunk > 0 ? CB_DECODE_WG_PER_CU_MIXED : CB_DECODE_WG_PER_CU) * cus8);
-    decode_prep_kernel<<<dim3(1), dim3(1024), 0, st>>>(a, 4 * n_dec_wg);
-    if (hipGetLastError() != hipSuccess) return CB_ERR_HIP;
+    n_dec_wg = decode_waves(st, a.n_chunk > 0) / 4;
+    if (!planned) {
+      decode_prep_kernel<<<dim3(1), dim3(1024), 0, st>>>(a, 4 * n_dec_wg);
+      if (hipGetLastError() != hipSuccess) return CB_ERR_HIP;
+    }
   }
   const int64_t n_tiles = a.n_chunk > 0 ? static_cast<int64_t>(a.n_chunk) * a.q_blocks * a.Hkv * a.nsplit : 0;
   const int64_t per_xcd = (n_tiles + 7) / 8;
@@ -1139,6 +1147,38 @@ int launch_all(hipStream_t st, const AttnArgs& a, const Plan& p, void* const* ev
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Host version of decode_prep_kernel's split, with the same rule, so that a launch with the plan
+// computes bit for bit what it computes after the split kernel.  Layout of out: [0] S, [1] L,
+// [2] W, [3] n_waves, then the row stage offsets seq[0..nd] (seq[nd] = S), then W start units.
+int decode_plan_host(const int32_t* ctx, int32_t nd, int32_t ups, int32_t n_waves, int32_t* out, size_t cap) {
+  if (cap < static_cast<size_t>(4 + nd + 1)) return CB_ERR_CAPACITY;
+  int32_t* seq = out + 4;
+  int64_t S = 0;
+  for (int32_t s = 0; s < nd; ++s) {
+    if (ctx[s] < 0) return CB_ERR_INVALID;
+    seq[s] = static_cast<int32_t>(S);
+    S += static_cast<int64_t>(ctx[s] > 0 ? (ctx[s] + kDecodeKeys - 1) / kDecodeKeys : 0) * ups;
+    if (S > 0x7fff0000 - static_cast<int64_t>(kMaxDecodeWaves) * 2) return CB_ERR_INVALID;
+  }
+  seq[nd] = static_cast<int32_t>(S);
+  const int32_t L = std::max<int32_t>(CB_DECODE_MIN_STAGES, static_cast<int32_t>((S + n_waves - 1) / n_waves));
+  const int32_t W = static_cast<int32_t>((S + L - 1) / L);
+  if (cap < static_cast<size_t>(4 + nd + 1 + W)) return CB_ERR_CAPACITY;
+  out[0] = static_cast<int32_t>(S);
+  out[1] = L;
+  out[2] = W;
+  out[3] = n_waves;
+  int32_t* wave = seq + nd + 1;
+  int32_t lo = 0;
+  for (int32_t w = 0; w < W; ++w) {                 // wave starts grow: walk the rows once
+    const int32_t pos = w * L;
+    while (seq[lo + 1] <= pos) ++lo;                // seq[lo] <= pos < seq[lo + 1]
+    const int32_t n_s = (seq[lo + 1] - seq[lo]) / ups;
+    wave[w] = lo * ups + (pos - seq[lo]) / n_s;
+  }
+  return CB_OK;
+}
+
 bool valid_shape(int32_t num_seqs, int32_t nd, int32_t T, int32_t max_q_len, int32_t max_dctx,
                  int32_t max_ctx, int32_t Hq, int32_t Hkv, int32_t D) {
   if (num_seqs < 0 || nd < 0 || nd > num_seqs || T < num_seqs || T - nd < num_seqs - nd) return false;
@@ -1165,13 +1205,31 @@ extern "C" size_t cb_attn_workspace_bytes(int32_t num_seqs, int32_t num_decodes,
   return cb::make_plan(num_seqs, num_decodes, T, max_q_len, max_ctx, Hq, Hkv, D).total;
 }
 
+extern "C" int32_t cb_attn_decode_waves(void* stream, int32_t has_chunks) {
+  return cb::decode_waves(static_cast<hipStream_t>(stream), has_chunks != 0);
+}
+
+extern "C" size_t cb_decode_plan_ints(int32_t num_decodes, int32_t n_waves) {
+  if (num_decodes < 0 || n_waves < 1) return 0;
+  return 4 + static_cast<size_t>(num_decodes) + 1 + static_cast<size_t>(n_waves);
+}
+
+extern "C" int cb_decode_plan(const int32_t* context_lens, int32_t num_decodes, int32_t Hq, int32_t Hkv,
+                              int32_t n_waves, int32_t* out, size_t cap_ints) {
+  if (num_decodes < 1 || !context_lens || !out || Hq < 1 || Hkv < 1 || Hq % Hkv || n_waves < 1 ||
+      n_waves > cb::kMaxDecodeWaves)
+    return CB_ERR_INVALID;
+  const int32_t ups = Hkv * ((Hq / Hkv + 15) / 16);
+  return cb::decode_plan_host(context_lens, num_decodes, ups, n_waves, out, cap_ints);
+}
+
 extern "C" int cb_mixed_paged_attention_timed(
     void* stream, int32_t dtype, int32_t num_seqs, int32_t num_decodes, int32_t T,
     int32_t max_q_len, int32_t max_decode_ctx, int32_t max_ctx, int32_t Hq, int32_t Hkv,
     int32_t D, int32_t block_size, float scale, const void* q, const void* k_cache,
     const void* v_cache, const int32_t* cu_seqlens_q, const int32_t* context_lens,
     const int32_t* cu_blocks, const int32_t* block_table, void* out, void* workspace,
-    size_t workspace_bytes, void* const* events) {
+    size_t workspace_bytes, const int32_t* decode_plan, int32_t plan_waves, void* const* events) {
   using namespace cb;
   if (dtype != CB_F32 && dtype != CB_BF16) return CB_ERR_INVALID;
   if (!valid_shape(num_seqs, num_decodes, T, max_q_len, max_decode_ctx, max_ctx, Hq, Hkv, D))
@@ -1209,10 +1267,19 @@ extern "C" int cb_mixed_paged_attention_timed(
   a.scale_log2 = scale * 1.4426950408889634f;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (dtype == CB_BF16) {
-    return D == 128 ? launch_all<bf16_t, 128>(st, a, p, events) : launch_all<bf16_t, 64>(st, a, p, events);
+  const bool planned = decode_plan != nullptr && num_decodes > 0;
+  if (planned) {
+    if (plan_waves != decode_waves(st, p.n_chunk > 0) || !aligned16(decode_plan)) return CB_ERR_INVALID;
+    int32_t* plan = const_cast<int32_t*>(decode_plan);
+    a.dec_par = plan;
+    a.dec_seq = plan + 4;
+    a.dec_wave = plan + 4 + num_decodes + 1;
   }
-  return D == 128 ? launch_all<float, 128>(st, a, p, events) : launch_all<float, 64>(st, a, p, events);
+  if (dtype == CB_BF16) {
+    return D == 128 ? launch_all<bf16_t, 128>(st, a, p, events, planned)
+                    : launch_all<bf16_t, 64>(st, a, p, events, planned);
+  }
+  return D == 128 ? launch_all<float, 128>(st, a, p, events, planned) : launch_all<float, 64>(st, a, p, events, planned);
 }
 
 extern "C" int cb_mixed_paged_attention(
@@ -1225,5 +1292,6 @@ extern "C" int cb_mixed_paged_attention(
   return cb_mixed_paged_attention_timed(stream, dtype, num_seqs, num_decodes, T, max_q_len,
                                         max_decode_ctx, max_ctx, Hq, Hkv, D, block_size, scale, q,
                                         k_cache, v_cache, cu_seqlens_q, context_lens, cu_blocks,
-                                        block_table, out, workspace, workspace_bytes, nullptr);
+                                        block_table, out, workspace, workspace_bytes, nullptr, 0,
+                                        nullptr);
 }

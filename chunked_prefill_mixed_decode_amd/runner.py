@@ -33,10 +33,14 @@ class MixedStepRunner:
             self.k_cache.view(ity).fill_(SENTINEL_BITS[dtype])
             self.v_cache.view(ity).fill_(SENTINEL_BITS[dtype])
         self.cos_sin = cb.cb_rope_cos_sin(max_pos, D, rope_base).to(self.device)
+        # The decode rows' work split is made on the host after each build (cb_decode_plan) and
+        # travels with the metadata, so the attention call launches no split kernel.
+        self.plan_waves = {h: cb.cb_attn_decode_waves(self.device, h) for h in (False, True)}
+        plan_ints = cb.cb_decode_plan_ints(cap_seqs, max(self.plan_waves.values()))
         # Two pinned host buffers and two device buffers.  Step n's metadata is pulled onto the
         # device by a kernel on the compute stream (so device buffer i is rewritten in stream
         # order); host buffer i is rewritten (step n + 2) only after that kernel has finished.
-        self.bufs = [cb.StepBuffers(cap_seqs, cap_tokens, cap_blocks) for _ in range(2)]
+        self.bufs = [cb.StepBuffers(cap_seqs, cap_tokens, cap_blocks, plan_ints=plan_ints) for _ in range(2)]
         self.dev_flat = [torch.empty_like(b.flat, device=self.device) for b in self.bufs]
         self.copied = [None, None]                 # kernel reading host buffer i finished
         self.ring = 0
@@ -51,6 +55,12 @@ class MixedStepRunner:
             self.copied[i].synchronize()
         meta = cb.cb_build_step(sched, budget, self.bufs[i])
         meta.buf_index = i
+        meta.plan_waves = 0
+        nd = meta.num_decodes
+        if nd > 0:
+            meta.plan_waves = self.plan_waves[meta.num_seqs > nd]
+            cb.cb_decode_plan(meta.host["context_lens"][:nd], self.Hq, self.Hkv, meta.plan_waves,
+                              self.bufs[i].arrays["decode_plan"])
         return meta
 
     def upload(self, meta: cb.StepMeta) -> dict:
@@ -65,7 +75,9 @@ class MixedStepRunner:
         i = meta.buf_index
         buf, dev = self.bufs[i], self.dev_flat[i]
         cb.cb_copy_host_to_device(buf.flat, dev, stream=torch.cuda.current_stream(self.device))
-        return {k: dev[buf.offsets[k]:buf.offsets[k] + n] for k, n in meta.lengths().items()}
+        views = {k: dev[buf.offsets[k]:buf.offsets[k] + n] for k, n in meta.lengths().items()}
+        views["decode_plan"] = dev[buf.offsets["decode_plan"]:]
+        return views
 
     def mark_pulled(self, meta: cb.StepMeta):
         """Record that the pinned buffer of ``meta`` may be rewritten once the stream gets here."""
@@ -100,7 +112,9 @@ class MixedStepRunner:
             dev["cu_blocks"], dev["block_table"], out, self.workspace,
             num_seqs=meta.num_seqs, num_decodes=meta.num_decodes, max_q_len=meta.max_q_len,
             max_decode_ctx=meta.max_decode_context_len, max_ctx=meta.max_context_len,
-            scale=self.scale, events=events)
+            scale=self.scale, events=events,
+            decode_plan=dev["decode_plan"] if getattr(meta, "plan_waves", 0) else None,
+            plan_waves=getattr(meta, "plan_waves", 0))
 
 
 class StepGraphs:

@@ -272,3 +272,35 @@ def test_linear_workspace_depends_on_the_shape_only():
     assert f(1, 128, 64) == 0                               # one stage: nothing to split
     for bad in ((0, 128, 64), (4, 100, 64), (4, 128, 96)):
         assert f(*bad) == 0
+
+
+def test_decode_plan_layout_and_rule():
+    # The decode rows' stage line: units (row, KV head, 16-head group) of ceil(ctx / 32) stages each,
+    # split into W contiguous shares of L = max(8, ceil(S / waves)) stages; each wave's first unit.
+    import torch
+    ctx = torch.tensor([100, 1, 4096, 33, 0, 700], dtype=torch.int32)
+    Hq, Hkv, waves = 56, 8, 40                        # group of 7 query heads: one unit per KV head
+    ups = Hkv * ((Hq // Hkv + 15) // 16)
+    n = cb.cb_decode_plan_ints(len(ctx), waves)
+    out = torch.full((n,), -7, dtype=torch.int32)
+    cb.cb_decode_plan(ctx, Hq, Hkv, waves, out)
+    stages = [(int(c) + 31) // 32 * ups for c in ctx]
+    S = sum(stages)
+    L = max(8, -(-S // waves))
+    W = -(-S // L)
+    assert out[:4].tolist() == [S, L, W, waves]
+    seq = [sum(stages[:i]) for i in range(len(ctx) + 1)]
+    assert out[4:4 + len(ctx) + 1].tolist() == seq
+    first = []
+    for w in range(W):
+        pos = w * L
+        r = max(i for i in range(len(ctx)) if seq[i] <= pos and stages[i] > 0)
+        first.append(r * ups + (pos - seq[r]) // (stages[r] // ups))
+    assert out[4 + len(ctx) + 1:4 + len(ctx) + 1 + W].tolist() == first
+    small = torch.zeros(5, dtype=torch.int32)
+    with pytest.raises(cb.CbError) as e:
+        cb.cb_decode_plan(ctx, Hq, Hkv, waves, small)
+    assert e.value.status == cb.CB_ERR_CAPACITY
+    with pytest.raises(cb.CbError) as e:
+        cb.cb_decode_plan(ctx, 10, 4, waves, out)      # Hq not a multiple of Hkv
+    assert e.value.status == cb.CB_ERR_INVALID

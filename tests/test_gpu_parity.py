@@ -318,3 +318,35 @@ def test_host_copy_sees_every_rewrite(dev):
     lib = cb._lib()
     assert lib.cb_copy_host_to_device(None, src.data_ptr() + 4, dst.data_ptr(), 8) == cb.CB_ERR_INVALID
     assert lib.cb_copy_host_to_device(None, src.data_ptr(), dst.data_ptr(), 12) == cb.CB_ERR_INVALID
+
+
+@pytest.mark.parametrize("i", [4, 8])
+def test_host_decode_plan_matches_device_split(dev, i):
+    # The runner ships a host-made decode plan (cb_decode_plan); the same call without it splits on
+    # the device.  Same rule, so the outputs must agree bit for bit; a plan made for another wave
+    # count is refused.
+    w = workloads.small(i)
+    g = GpuRun(w, dev)
+    cb = g.cb
+    for _ in range(2):
+        meta = g.runner.build(g.sched, w.budget)
+        dm = g.runner.upload(meta)
+        q, k, v = g.step_inputs(meta)
+        q_rot, out_plan, out_dev = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+        g.runner.append(dm, q, k, v, q_rot)
+        g.runner.attend(meta, dm, q_rot, out_plan)
+        assert meta.plan_waves > 0
+        kw = dict(num_seqs=meta.num_seqs, num_decodes=meta.num_decodes, max_q_len=meta.max_q_len,
+                  max_decode_ctx=meta.max_decode_context_len, max_ctx=meta.max_context_len,
+                  scale=g.runner.scale)
+        cb.cb_mixed_paged_attention(q_rot, g.runner.k_cache, g.runner.v_cache, dm["cu_seqlens_q"],
+                                    dm["context_lens"], dm["cu_blocks"], dm["block_table"], out_dev,
+                                    g.runner.workspace, **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(out_plan.view(torch.int16), out_dev.view(torch.int16))
+        with pytest.raises(cb.CbError) as e:
+            cb.cb_mixed_paged_attention(q_rot, g.runner.k_cache, g.runner.v_cache, dm["cu_seqlens_q"],
+                                        dm["context_lens"], dm["cu_blocks"], dm["block_table"], out_dev,
+                                        g.runner.workspace, decode_plan=dm["decode_plan"],
+                                        plan_waves=meta.plan_waves + 4, **kw)
+        assert e.value.status == cb.CB_ERR_INVALID
