@@ -81,7 +81,7 @@ EXPORTS = {
                                                       _sz, _vp, _i32, ctypes.POINTER(_vp)]),
     "cb_attn_decode_waves": (_i32, [_vp, _i32]),
     "cb_decode_plan_ints": (_sz, [_i32, _i32]),
-    "cb_decode_plan": (ctypes.c_int, [_pi32, _i32, _i32, _i32, _i32, _pi32, _sz]),
+    "cb_decode_plan": (ctypes.c_int, [_vp, _i32, _pi32, _i32, _i32, _i32, _pi32, _sz]),
 }
 
 
@@ -325,29 +325,41 @@ def cb_attn_workspace_bytes(num_seqs, num_decodes, T, max_q_len, max_decode_ctx,
                                               max_ctx, Hq, Hkv, D))
 
 
+def _stream_arg(device_or_stream) -> int:
+    """hipStream_t of a torch stream, or the current stream of a device (None: the current one).
+    Without a usable GPU: the null stream (the library then assumes MI355X's 256 compute units)."""
+    st = device_or_stream
+    if isinstance(st, torch.cuda.Stream):
+        return st.cuda_stream
+    if st is None or isinstance(st, (torch.device, int, str)):
+        return torch.cuda.current_stream(st).cuda_stream if torch.cuda.is_available() else 0
+    return int(st)
+
+
 def cb_attn_decode_waves(device_or_stream=None, has_chunks: bool = True) -> int:
     """Decode waves an attention call launches on the device of the stream (default: current)."""
-    st = device_or_stream
-    if st is None or isinstance(st, (torch.device, int, str)):
-        st = torch.cuda.current_stream(st).cuda_stream
-    elif isinstance(st, torch.cuda.Stream):
-        st = st.cuda_stream
-    return int(_lib().cb_attn_decode_waves(ctypes.c_void_p(st), int(bool(has_chunks))))
+    return int(_lib().cb_attn_decode_waves(ctypes.c_void_p(_stream_arg(device_or_stream)),
+                                           int(bool(has_chunks))))
 
 
 def cb_decode_plan_ints(num_decodes: int, n_waves: int) -> int:
     return int(_lib().cb_decode_plan_ints(num_decodes, n_waves))
 
 
-def cb_decode_plan(context_lens, Hq: int, Hkv: int, n_waves: int, out) -> None:
+def cb_decode_plan(context_lens, Hq: int, Hkv: int, out, device_or_stream=None,
+                   has_chunks: bool = True) -> int:
     """context_lens: host int32 tensor of the decode rows' context lengths; out: host int32 tensor
-    of at least cb_decode_plan_ints(len(context_lens), n_waves) entries."""
+    of at least cb_decode_plan_ints(len(context_lens), n_waves) entries.  The plan is for an
+    attention call on the device of the stream (default: current) with or without chunk rows;
+    returns its wave count (the call's plan_waves)."""
     if context_lens.dtype != torch.int32 or out.dtype != torch.int32 or context_lens.is_cuda or out.is_cuda:
         raise ValueError("cb_decode_plan: int32 host tensors")
     if not context_lens.is_contiguous() or not out.is_contiguous():
         raise ValueError("cb_decode_plan: contiguous tensors")
-    _check(_lib().cb_decode_plan(_i32ptr(context_lens), context_lens.numel(), Hq, Hkv, n_waves,
-                                 _i32ptr(out), out.numel()), "cb_decode_plan")
+    _check(_lib().cb_decode_plan(ctypes.c_void_p(_stream_arg(device_or_stream)), int(bool(has_chunks)),
+                                 _i32ptr(context_lens), context_lens.numel(), Hq, Hkv, _i32ptr(out),
+                                 out.numel()), "cb_decode_plan")
+    return int(out[3])
 
 
 def cb_mixed_paged_attention(q, k_cache, v_cache, cu_seqlens_q, context_lens, cu_blocks,

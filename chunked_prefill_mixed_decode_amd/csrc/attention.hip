@@ -48,6 +48,22 @@ namespace {
 #ifndef CB_DECODE_WG_PER_CU_MIXED
 #define CB_DECODE_WG_PER_CU_MIXED 1   // the same beside chunk tiles
 #endif
+// Relative streaming rates of decode workgroups (percent), from per-wave start/end clocks of
+// decode-only and mixed launches on MI355X: workgroups on odd XCDs stream ~8-12% slower than on
+// even ones, so each wave's share of the decode work is sized by its workgroup's rate.  The
+// workgroup dispatched second onto a compute unit also streams ~11% slower while the first one
+// runs, but it speeds up once that one ends: giving it less work measured no faster, so its rate
+// is left at 100.
+#ifndef CB_DECODE_RATE_SECOND
+#define CB_DECODE_RATE_SECOND 100
+#endif
+#ifndef CB_DECODE_RATE_ODD_XCD
+#define CB_DECODE_RATE_ODD_XCD 88
+#endif
+static_assert(CB_DECODE_RATE_SECOND >= 50 && CB_DECODE_RATE_SECOND <= 100 &&
+              CB_DECODE_RATE_ODD_XCD >= 50 && CB_DECODE_RATE_ODD_XCD <= 100, "decode rates in [50, 100]");
+// A split over W <= S / CB_DECODE_MIN_STAGES waves then gives every wave at least one stage.
+static_assert(CB_DECODE_MIN_STAGES * CB_DECODE_RATE_SECOND * CB_DECODE_RATE_ODD_XCD > 10000, "non-empty waves");
 
 constexpr int kChunkRows = 128;   // rows per chunk tile: 4 waves x 32
 constexpr int kChunkKeys = 32;    // keys per LDS stage of a chunk tile
@@ -69,7 +85,8 @@ constexpr int kBlockWindow = 2048;                   // block ids per LDS window
 struct Plan {
   int32_t G = 1, head_blocks = 1, hw = 1, ups = 1;
   int32_t bmq = 128, q_blocks = 0, n_chunk = 0, nsplit = 1;
-  size_t dec_o = 0, dec_ml = 0, chk_o = 0, chk_ml = 0, dec_seq = 0, dec_wave = 0, dec_par = 0, total = 0;
+  size_t dec_o = 0, dec_ml = 0, chk_o = 0, chk_ml = 0, dec_seq = 0, dec_wave = 0, dec_par = 0, dec_unit = 0;
+  size_t total = 0;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
@@ -104,6 +121,7 @@ Plan make_plan(int32_t num_seqs, int32_t nd, int32_t T, int32_t max_q_len, int32
   p.dec_seq = off;  off = align256(off + (nd > 0 ? static_cast<size_t>(nd + 1) * sizeof(int32_t) : 0));
   p.dec_wave = off; off = align256(off + (nd > 0 ? kMaxDecodeWaves * sizeof(int32_t) : 0));
   p.dec_par = off;  off = align256(off + (nd > 0 ? 4 * sizeof(int32_t) : 0));
+  p.dec_unit = off; off = align256(off + (nd > 0 ? static_cast<size_t>(nd) * p.ups * 2 * sizeof(int32_t) : 0));
   p.total = off;
   return p;
 }
@@ -123,7 +141,8 @@ struct AttnArgs {
   float* chk_ml;
   int32_t* dec_seq;      // [nd + 1] first stage of each decode row on the stage line; [nd] = total
   int32_t* dec_wave;     // [waves] unit holding each wave's first stage
-  int32_t* dec_par;      // [0] total stages S, [1] stages per wave L, [2] waves with work W
+  int32_t* dec_par;      // [0] total stages S, [1] first-round workgroups F, [2] waves with work W
+  int32_t* dec_unit;     // [units][2] waves holding each unit's first and last stage (written by them)
   int32_t num_seqs, nd, T, Hq, Hkv, G, bs, bs_shift;
   int32_t head_blocks, hw, ups;
   int32_t bmq, q_blocks, n_chunk, nsplit;
@@ -356,15 +375,40 @@ template <> struct StageRegs<64> {
 // Decode rows.
 // ---------------------------------------------------------------------------------------------
 // Work layout: a decode row s with context c has units (KV head g, 16-head block hb), each of
-// decode_stages(c) 32-key stages.  All units of all rows, in order, form one line of S stages;
-// wave w takes stages [w L, (w + 1) L), so every wave has the same work (up to one stage) and
-// a unit is shared by the few consecutive waves whose ranges meet it.  Each (unit, wave) pair
-// yields one partial (m, l, o) in slot unit + wave: both indices grow along the line, so the
-// slot is unique and a unit's partials sit in consecutive slots.
+// decode_stages(c) 32-key stages.  All units of all rows, in order, form one line of S stages,
+// cut into W = min(waves, S / CB_DECODE_MIN_STAGES) contiguous ranges (one at least when S > 0).
+// Wave w runs in workgroup w / 4; workgroup b runs on XCD b mod 8, and workgroups [0, F) are the
+// first on their compute unit (F = compute units rounded up to a multiple of 8).  Its range is
+// [start(w), start(w + 1)) with start(w) = floor(S C(w) / C(W)), C(w) the summed rates of waves
+// [0, w): every wave's work is proportional to its rate, so all end together.  A unit is shared by
+// the few consecutive waves whose ranges meet it.  Each (unit, wave) pair yields one partial
+// (m, l, o) in slot unit + wave: both indices grow along the line, so the slot is unique and a
+// unit's partials sit in consecutive slots.
 //
-// The prep workgroup scans the rows' stage counts into dec_seq (first stage of each row), picks
-// L = max(CB_DECODE_MIN_STAGES, ceil(S / waves)) and records the unit holding each wave's first
-// stage.
+// The prep workgroup scans the rows' stage counts into dec_seq (first stage of each row), picks W
+// and records the unit holding each wave's first stage; dec_par holds [S, F, W].
+__host__ __device__ __forceinline__ int64_t decode_wg_rate(int32_t b, int32_t F) {
+  return static_cast<int64_t>(b < F ? 100 : CB_DECODE_RATE_SECOND) * ((b & 1) ? CB_DECODE_RATE_ODD_XCD : 100);
+}
+__host__ __device__ __forceinline__ int64_t decode_rate_run(int64_t m) {   // m workgroups from an even index
+  return (m + 1) / 2 * 100 + m / 2 * CB_DECODE_RATE_ODD_XCD;
+}
+// C(w): summed rates of waves [0, w), four waves per workgroup (F even).
+__host__ __device__ __forceinline__ int64_t decode_rate_prefix(int32_t w, int32_t F) {
+  const int32_t b = w >> 2;
+  const int32_t n0 = b < F ? b : F;
+  return 4 * (100 * decode_rate_run(n0) + CB_DECODE_RATE_SECOND * decode_rate_run(b - n0)) +
+         (w & 3) * decode_wg_rate(b, F);
+}
+__host__ __device__ __forceinline__ int32_t decode_waves_used(int32_t S, int32_t n_waves) {
+  if (S <= 0) return 0;
+  const int32_t k = S / CB_DECODE_MIN_STAGES;
+  return k < 1 ? 1 : (k > n_waves ? n_waves : k);
+}
+// start(w) with cw = C(W).  S < 2^31 and C(W) <= kMaxDecodeWaves * 10^4, so S C(w) fits int64.
+__host__ __device__ __forceinline__ int32_t decode_wave_start(int32_t w, int32_t S, int64_t cw, int32_t F) {
+  return static_cast<int32_t>(static_cast<int64_t>(S) * decode_rate_prefix(w, F) / cw);
+}
 __device__ __forceinline__ int32_t block_scan_1024(int32_t v, int32_t* scan) {
   const int tid = threadIdx.x;
   scan[tid] = v;
@@ -380,7 +424,7 @@ __device__ __forceinline__ int32_t block_scan_1024(int32_t v, int32_t* scan) {
 
 constexpr int kPrepRows = 8192;   // decode rows whose stage offsets the prep workgroup keeps in LDS
 
-__global__ __launch_bounds__(1024) void decode_prep_kernel(AttnArgs a, int32_t n_waves) {
+__global__ __launch_bounds__(1024) void decode_prep_kernel(AttnArgs a, int32_t n_waves, int32_t F) {
   __shared__ int32_t scan[1024];
   __shared__ int32_t seq_lds[kPrepRows + 1];
   __shared__ int32_t carry;
@@ -404,18 +448,18 @@ __global__ __launch_bounds__(1024) void decode_prep_kernel(AttnArgs a, int32_t n
     __syncthreads();
   }
   const int32_t S = carry;
-  const int32_t L = max(CB_DECODE_MIN_STAGES, (S + n_waves - 1) / n_waves);
-  const int32_t W = (S + L - 1) / L;
+  const int32_t W = decode_waves_used(S, n_waves);
+  const int64_t cw = decode_rate_prefix(W, F);
   if (tid == 0) {
     a.dec_seq[a.nd] = S;
     if (in_lds) seq_lds[a.nd] = S;
     a.dec_par[0] = S;
-    a.dec_par[1] = L;
+    a.dec_par[1] = F;
     a.dec_par[2] = W;
   }
   __syncthreads();                                    // the row offsets are complete for the workgroup
   for (int32_t w = tid; w < W; w += 1024) {
-    const int32_t pos = w * L;
+    const int32_t pos = decode_wave_start(w, S, cw, F);
     int32_t lo = 0, hi = a.nd;                        // seq[lo] <= pos < seq[hi]
     while (hi - lo > 1) {
       const int32_t mid = (lo + hi) >> 1;
@@ -457,9 +501,11 @@ __device__ __forceinline__ void decode_wave(const AttnArgs& a, const int32_t* se
   char* sV = lds + DecodeLds<T, D>::V;
   int32_t* sBlk = reinterpret_cast<int32_t*>(lds + DecodeLds<T, D>::BLK);
 
-  const int32_t S = par[0], L = par[1], W = par[2];   // uniform, read-only here: scalar loads
+  const int32_t S = par[0], F = par[1], W = par[2];   // uniform, read-only here: scalar loads
   if (w >= W) return;
-  const int32_t pos_end = min(S, (w + 1) * L);
+  const int64_t cw = decode_rate_prefix(W, F);
+  const int32_t pos_begin = decode_wave_start(w, S, cw, F);
+  const int32_t pos_end = decode_wave_start(w + 1, S, cw, F);
 
   const int32_t col = lane & 15;      // head owned by this lane in S^T / P^T / O^T
   const int32_t grp = lane >> 4;      // slot group
@@ -491,7 +537,7 @@ __device__ __forceinline__ void decode_wave(const AttnArgs& a, const int32_t* se
     c.u = s * a.ups;
   };
   Cursor cur_c;
-  cur_c.pos = w * L;
+  cur_c.pos = pos_begin;
   {
     const int32_t u0 = wave_unit[w];
     load_row(cur_c, u0 / a.ups);
@@ -517,6 +563,11 @@ __device__ __forceinline__ void decode_wave(const AttnArgs& a, const int32_t* se
     it.slot = c.u + w;
     it.head_bytes = static_cast<int64_t>(g) * ((int64_t)ROW << bsh);
     it.last = sub_end == seg_end;
+    // The combine finds a unit's partials (slots u + w0 .. u + w1) from these two records.
+    if (lane == 0) {
+      if (c.pos == c.a_u) a.dec_unit[2 * c.u] = w;
+      if (sub_end == unit_end) a.dec_unit[2 * c.u + 1] = w;
+    }
     c.pos = sub_end;
     if (c.pos == unit_end && c.pos < pos_end) {
       if (c.r + 1 < a.ups) {
@@ -1011,10 +1062,8 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a, int32_t n_dec_
     const int32_t g = h / a.G, hh = h - g * a.G;
     const int32_t r = g * a.head_blocks + (hh >> 4);
     const int32_t u = row * a.ups + r;
-    const int32_t L = a.dec_par[1];
-    const int32_t a_u = a.dec_seq[row] + r * n;
-    const int32_t w0 = a_u / L;
-    P = n > 0 ? (a_u + n - 1) / L - w0 + 1 : 0;
+    const int32_t w0 = n > 0 ? a.dec_unit[2 * u] : 0;
+    P = n > 0 ? a.dec_unit[2 * u + 1] - w0 + 1 : 0;
     const int64_t base = static_cast<int64_t>(u + w0) * a.hw + (hh & 15);
     po = a.dec_o + base * D;
     pml = a.dec_ml + base * 2;
@@ -1096,8 +1145,12 @@ int compute_units(hipStream_t st) {
 
 // Decode waves of an attention launch on the stream's device: four per decode workgroup, one
 // workgroup per compute unit beside chunk tiles, two when there are none.
+// Decode workgroups dispatched first onto their compute units: the compute units rounded up to a
+// multiple of 8 (whole rounds over the XCDs).
+int32_t first_round_wgs(hipStream_t st) { return (compute_units(st) + 7) / 8 * 8; }
+
 int32_t decode_waves(hipStream_t st, bool has_chunks) {
-  const int cus8 = (compute_units(st) + 7) / 8 * 8;
+  const int cus8 = first_round_wgs(st);
   return 4 * std::min(kMaxDecodeWaves / 4, (has_chunks ? CB_DECODE_WG_PER_CU_MIXED : CB_DECODE_WG_PER_CU) * cus8);
 }
 
@@ -1113,7 +1166,7 @@ int launch_all(hipStream_t st, const AttnArgs& a, const Plan& p, void* const* ev
   if (a.nd > 0) {
     n_dec_wg = decode_waves(st, a.n_chunk > 0) / 4;
     if (!planned) {
-      decode_prep_kernel<<<dim3(1), dim3(1024), 0, st>>>(a, 4 * n_dec_wg);
+      decode_prep_kernel<<<dim3(1), dim3(1024), 0, st>>>(a, 4 * n_dec_wg, first_round_wgs(st));
       if (hipGetLastError() != hipSuccess) return CB_ERR_HIP;
     }
   }
@@ -1150,7 +1203,8 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // Host version of decode_prep_kernel's split, with the same rule, so that a launch with the plan
 // computes bit for bit what it computes after the split kernel.  Layout of out: [0] S, [1] L,
 // [2] W, [3] n_waves, then the row stage offsets seq[0..nd] (seq[nd] = S), then W start units.
-int decode_plan_host(const int32_t* ctx, int32_t nd, int32_t ups, int32_t n_waves, int32_t* out, size_t cap) {
+int decode_plan_host(const int32_t* ctx, int32_t nd, int32_t ups, int32_t n_waves, int32_t F, int32_t* out,
+                     size_t cap) {
   if (cap < static_cast<size_t>(4 + nd + 1)) return CB_ERR_CAPACITY;
   int32_t* seq = out + 4;
   int64_t S = 0;
@@ -1161,17 +1215,17 @@ int decode_plan_host(const int32_t* ctx, int32_t nd, int32_t ups, int32_t n_wave
     if (S > 0x7fff0000 - static_cast<int64_t>(kMaxDecodeWaves) * 2) return CB_ERR_INVALID;
   }
   seq[nd] = static_cast<int32_t>(S);
-  const int32_t L = std::max<int32_t>(CB_DECODE_MIN_STAGES, static_cast<int32_t>((S + n_waves - 1) / n_waves));
-  const int32_t W = static_cast<int32_t>((S + L - 1) / L);
+  const int32_t W = decode_waves_used(static_cast<int32_t>(S), n_waves);
+  const int64_t cw = decode_rate_prefix(W, F);
   if (cap < static_cast<size_t>(4 + nd + 1 + W)) return CB_ERR_CAPACITY;
   out[0] = static_cast<int32_t>(S);
-  out[1] = L;
+  out[1] = F;
   out[2] = W;
   out[3] = n_waves;
   int32_t* wave = seq + nd + 1;
   int32_t lo = 0;
   for (int32_t w = 0; w < W; ++w) {                 // wave starts grow: walk the rows once
-    const int32_t pos = w * L;
+    const int32_t pos = decode_wave_start(w, static_cast<int32_t>(S), cw, F);
     while (seq[lo + 1] <= pos) ++lo;                // seq[lo] <= pos < seq[lo + 1]
     const int32_t n_s = (seq[lo + 1] - seq[lo]) / ups;
     wave[w] = lo * ups + (pos - seq[lo]) / n_s;
@@ -1214,13 +1268,13 @@ extern "C" size_t cb_decode_plan_ints(int32_t num_decodes, int32_t n_waves) {
   return 4 + static_cast<size_t>(num_decodes) + 1 + static_cast<size_t>(n_waves);
 }
 
-extern "C" int cb_decode_plan(const int32_t* context_lens, int32_t num_decodes, int32_t Hq, int32_t Hkv,
-                              int32_t n_waves, int32_t* out, size_t cap_ints) {
-  if (num_decodes < 1 || !context_lens || !out || Hq < 1 || Hkv < 1 || Hq % Hkv || n_waves < 1 ||
-      n_waves > cb::kMaxDecodeWaves)
-    return CB_ERR_INVALID;
+extern "C" int cb_decode_plan(void* stream, int32_t has_chunks, const int32_t* context_lens,
+                              int32_t num_decodes, int32_t Hq, int32_t Hkv, int32_t* out, size_t cap_ints) {
+  if (num_decodes < 1 || !context_lens || !out || Hq < 1 || Hkv < 1 || Hq % Hkv) return CB_ERR_INVALID;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
   const int32_t ups = Hkv * ((Hq / Hkv + 15) / 16);
-  return cb::decode_plan_host(context_lens, num_decodes, ups, n_waves, out, cap_ints);
+  return cb::decode_plan_host(context_lens, num_decodes, ups, cb::decode_waves(st, has_chunks != 0),
+                              cb::first_round_wgs(st), out, cap_ints);
 }
 
 extern "C" int cb_mixed_paged_attention_timed(
@@ -1259,6 +1313,7 @@ extern "C" int cb_mixed_paged_attention_timed(
   a.dec_seq = reinterpret_cast<int32_t*>(ws + p.dec_seq);
   a.dec_wave = reinterpret_cast<int32_t*>(ws + p.dec_wave);
   a.dec_par = reinterpret_cast<int32_t*>(ws + p.dec_par);
+  a.dec_unit = reinterpret_cast<int32_t*>(ws + p.dec_unit);
   a.num_seqs = num_seqs; a.nd = num_decodes; a.T = T; a.Hq = Hq; a.Hkv = Hkv; a.G = p.G;
   a.bs = block_size;
   a.bs_shift = __builtin_ctz(static_cast<unsigned>(block_size));

@@ -58,9 +58,9 @@ class MixedStepRunner:
         meta.plan_waves = 0
         nd = meta.num_decodes
         if nd > 0:
-            meta.plan_waves = self.plan_waves[meta.num_seqs > nd]
-            cb.cb_decode_plan(meta.host["context_lens"][:nd], self.Hq, self.Hkv, meta.plan_waves,
-                              self.bufs[i].arrays["decode_plan"])
+            meta.plan_waves = cb.cb_decode_plan(meta.host["context_lens"][:nd], self.Hq, self.Hkv,
+                                                self.bufs[i].arrays["decode_plan"], self.device,
+                                                has_chunks=meta.num_seqs > nd)
         return meta
 
     def upload(self, meta: cb.StepMeta) -> dict:

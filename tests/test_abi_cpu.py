@@ -274,33 +274,54 @@ def test_linear_workspace_depends_on_the_shape_only():
         assert f(*bad) == 0
 
 
-def test_decode_plan_layout_and_rule():
-    # The decode rows' stage line: units (row, KV head, 16-head group) of ceil(ctx / 32) stages each,
-    # split into W contiguous shares of L = max(8, ceil(S / waves)) stages; each wave's first unit.
-    import torch
-    ctx = torch.tensor([100, 1, 4096, 33, 0, 700], dtype=torch.int32)
-    Hq, Hkv, waves = 56, 8, 40                        # group of 7 query heads: one unit per KV head
+def _expected_decode_plan(ctx, Hq, Hkv, n_waves, F=256):
+    # The decode rows' stage line: units (row, KV head, 16-head group) of ceil(ctx / 32) stages
+    # each; W = min(n_waves, S // 8) (at least one) contiguous ranges, wave w's share proportional to
+    # the rate of its workgroup w // 4 (percent: 100 on even XCDs, 88 on odd ones, workgroup b on
+    # XCD b mod 8; the same for the workgroups [F, 2F) dispatched second onto their compute unit);
+    # start(w) = floor(S C(w) / C(W)); then each wave's first unit.
     ups = Hkv * ((Hq // Hkv + 15) // 16)
-    n = cb.cb_decode_plan_ints(len(ctx), waves)
-    out = torch.full((n,), -7, dtype=torch.int32)
-    cb.cb_decode_plan(ctx, Hq, Hkv, waves, out)
     stages = [(int(c) + 31) // 32 * ups for c in ctx]
     S = sum(stages)
-    L = max(8, -(-S // waves))
-    W = -(-S // L)
-    assert out[:4].tolist() == [S, L, W, waves]
+    W = 0 if S == 0 else min(n_waves, max(1, S // 8))
+    rate = lambda b: (100 if b < F else 100) * (88 if b & 1 else 100)
+    C = [0]
+    for v in range(W):
+        C.append(C[-1] + rate(v // 4))
+    start = [S * C[w] // C[W] for w in range(W + 1)]
     seq = [sum(stages[:i]) for i in range(len(ctx) + 1)]
-    assert out[4:4 + len(ctx) + 1].tolist() == seq
     first = []
     for w in range(W):
-        pos = w * L
+        pos = start[w]
         r = max(i for i in range(len(ctx)) if seq[i] <= pos and stages[i] > 0)
         first.append(r * ups + (pos - seq[r]) // (stages[r] // ups))
-    assert out[4 + len(ctx) + 1:4 + len(ctx) + 1 + W].tolist() == first
+    return [S, F, W, n_waves] + seq + first, start
+
+
+def test_decode_plan_layout_and_rule():
+    import torch
+    cases = [
+        (torch.tensor([100, 1, 4096, 33, 0, 700], dtype=torch.int32), 56, 8, True),   # GQA-7: one unit per KV head
+        (torch.tensor([4096 - 37 * i for i in range(64)], dtype=torch.int32), 32, 32, False),  # both dispatch rounds
+        (torch.tensor([5, 0], dtype=torch.int32), 32, 8, True),                        # S < 8: one wave
+    ]
+    for ctx, Hq, Hkv, chunks in cases:
+        waves = cb.cb_attn_decode_waves(None, chunks)
+        assert waves == (1024 if chunks else 2048)        # MI355X: 256 compute units, 1 or 2 workgroups each
+        n = cb.cb_decode_plan_ints(len(ctx), waves)
+        out = torch.full((n,), -7, dtype=torch.int32)
+        assert cb.cb_decode_plan(ctx, Hq, Hkv, out, None, has_chunks=chunks) == waves
+        want, start = _expected_decode_plan(ctx.tolist(), Hq, Hkv, waves)
+        assert out[:len(want)].tolist() == want
+        W = want[2]
+        assert all(start[w + 1] > start[w] for w in range(W))           # every wave has work
+        if W >= 8:                                       # workgroup 0 (even XCD) takes more than 1 (odd)
+            assert start[4] - start[0] > start[8] - start[4]
+    ctx, Hq, Hkv, waves = cases[0][0], 56, 8, 1024
     small = torch.zeros(5, dtype=torch.int32)
     with pytest.raises(cb.CbError) as e:
-        cb.cb_decode_plan(ctx, Hq, Hkv, waves, small)
+        cb.cb_decode_plan(ctx, Hq, Hkv, small, None)
     assert e.value.status == cb.CB_ERR_CAPACITY
     with pytest.raises(cb.CbError) as e:
-        cb.cb_decode_plan(ctx, 10, 4, waves, out)      # Hq not a multiple of Hkv
+        cb.cb_decode_plan(ctx, 10, 4, torch.zeros(64, dtype=torch.int32), None)   # Hq not a multiple of Hkv
     assert e.value.status == cb.CB_ERR_INVALID
