@@ -359,7 +359,7 @@ def main():
     # Per-step phase events on a sample of the timed steps (created and touched once so the
     # runtime objects exist).
     every = max(1, args.event_every)
-    sampled = [i for i in range(args.steps) if i % every == every // 2]
+    sampled = [i for i in range(args.steps) if i % every == every // 2] or [args.steps - 1]   # short runs: the last
     evs = {i: [torch.cuda.Event(enable_timing=True) for _ in range(8)] for i in sampled}
     for e8 in evs.values():
         for e in e8:
