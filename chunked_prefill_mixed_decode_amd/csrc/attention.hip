@@ -196,6 +196,20 @@ __device__ __forceinline__ void lds_copy16_asm(const char* src, const char* lds_
       : "=&s"(saved)
       : "v"(src), "s"(dst));
 }
+// The same copy from a wave-uniform 64-bit base (SGPRs) plus a 32-bit per-lane offset: the
+// instruction's scalar-base form, with no per-lane 64-bit address arithmetic.
+__device__ __forceinline__ void lds_copy16_asm_s(const char* base, uint32_t voff, const char* lds_dst) {
+  const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(lds_dst));
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(base), "s"(dst));
+}
 // Wait for this wave's LDS reads before a DMA overwrites the buffer they read
 // (s_waitcnt lgkmcnt(0), vmcnt and expcnt untouched).
 __device__ __forceinline__ void lds_reads_done() { __builtin_amdgcn_s_waitcnt(0xC07F); }
@@ -756,6 +770,7 @@ __device__ __forceinline__ void chunk_tile(const AttnArgs& a, int32_t tile, char
   constexpr int ROW = D * sizeof(T);  // bytes per key row in LDS
   constexpr int RPI = 1024 / ROW;     // key rows per 1 KB copy instruction
   constexpr int NCPW = kChunkKeys / RPI / 4;    // copy instructions per wave per tensor
+  static_assert(RPI <= kMinBlock && kChunkKeys % (4 * RPI) == 0, "a copy instruction's rows share a block");
   constexpr int CPW = 2 * NCPW;                 // copy instructions per wave per stage
   constexpr int NS = ChunkLds<T, D>::NS;
   constexpr int STAGE = ChunkLds<T, D>::STAGE;  // bytes of K (and of V) per stage
@@ -836,17 +851,37 @@ __device__ __forceinline__ void chunk_tile(const AttnArgs& a, int32_t tile, char
   const int64_t head_bytes = static_cast<int64_t>(g) * ((int64_t)ROW << bsh);
   const int64_t blk_bytes = static_cast<int64_t>(a.Hkv) * ((int64_t)ROW << bsh);
   const int cp_row = lane / (ROW / 16), cp_pos = lane % (ROW / 16);
+  // One copy instruction moves RPI consecutive rows; RPI <= 8 <= bs (both powers of two) and the
+  // first row is RPI-aligned, so its rows share one cache block: the block's address is
+  // wave-uniform and each lane adds a loop-invariant offset (row in the block, swizzled chunk).
+  uint32_t lane_off[NCPW];
+#pragma unroll
+  for (int j = 0; j < NCPW; ++j)
+    lane_off[j] = cp_row * ROW + 16 * lds_chunk(cp_pos, (wave * NCPW + j) * RPI + cp_row, ROW);
   auto issue = [&](int32_t kt, int buf) {
     const int32_t k0 = kt * kChunkKeys;
+    if (k0 + kChunkKeys - 1 <= k_last) {             // every key of the stage is real
 #pragma unroll
-    for (int j = 0; j < NCPW; ++j) {
-      const int i = wave * NCPW + j;
-      const int r = i * RPI + cp_row;
-      const int32_t key = min(k0 + r, k_last);
-      const int64_t off = static_cast<int64_t>(sBlk[(key >> bsh) - win_lo]) * blk_bytes + head_bytes +
-                          static_cast<int64_t>(key & bmask) * ROW + 16 * lds_chunk(cp_pos, r, ROW);
-      lds_copy16_asm(kc + off, sK + buf * STAGE + i * 1024);
-      lds_copy16_asm(vc + off, sV + buf * STAGE + i * 1024);
+      for (int j = 0; j < NCPW; ++j) {
+        const int i = wave * NCPW + j;
+        const int32_t key0 = k0 + i * RPI;
+        const int32_t blk = __builtin_amdgcn_readfirstlane(sBlk[(key0 >> bsh) - win_lo]);
+        const int64_t base = static_cast<int64_t>(blk) * blk_bytes + head_bytes +
+                             static_cast<int64_t>(key0 & bmask) * ROW;
+        lds_copy16_asm_s(kc + base, lane_off[j], sK + buf * STAGE + i * 1024);
+        lds_copy16_asm_s(vc + base, lane_off[j], sV + buf * STAGE + i * 1024);
+      }
+    } else {                                          // keys past kv_end repeat the last one
+#pragma unroll
+      for (int j = 0; j < NCPW; ++j) {
+        const int i = wave * NCPW + j;
+        const int r = i * RPI + cp_row;
+        const int32_t key = min(k0 + r, k_last);
+        const int64_t off = static_cast<int64_t>(sBlk[(key >> bsh) - win_lo]) * blk_bytes + head_bytes +
+                            static_cast<int64_t>(key & bmask) * ROW + 16 * lds_chunk(cp_pos, r, ROW);
+        lds_copy16_asm(kc + off, sK + buf * STAGE + i * 1024);
+        lds_copy16_asm(vc + off, sV + buf * STAGE + i * 1024);
+      }
     }
   };
   // Wait for this wave's copies of the current stage (all but the `later` stages issued after
@@ -935,7 +970,7 @@ __device__ __forceinline__ void chunk_tile(const AttnArgs& a, int32_t tile, char
       float mx = st[0];
 #pragma unroll
       for (int r = 1; r < 16; ++r) mx = fmaxf(mx, st[r]);
-      mx = wave_xor_max(mx, 32);
+      mx = half_xor_max(mx);
       const float m_new = fmaxf(m_run, mx * a.scale_log2);
       const float m_use = m_new == kNegInf ? 0.f : m_new;
       const float alpha = fast_exp2(m_run - m_use);

@@ -110,6 +110,13 @@ __device__ __forceinline__ float wave_xor_max(float v, int mask) {
   return fmaxf(v, __shfl_xor(v, mask, 64));
 }
 __device__ __forceinline__ float wave_xor_sum(float v, int mask) { return v + __shfl_xor(v, mask, 64); }
+// Maximum over lanes i and i ^ 32 with gfx950's v_permlane32_swap: the two 32-lane halves trade
+// values inside the VALU (no LDS round trip, so no wait on the lane's other LDS traffic).  The
+// pair it returns is {v[i], v[i ^ 32]} in either order; the maximum does not depend on which.
+__device__ __forceinline__ float half_xor_max(float v) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+}
 
 constexpr float kNegInf = -__builtin_huge_valf();
 
