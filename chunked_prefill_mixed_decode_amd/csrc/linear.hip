@@ -9,13 +9,16 @@
 // in it, so T tokens give about T FLOP per weight byte (bf16) -- weight-bandwidth bound for a
 // decode-only step, compute bound once a prefill chunk joins.
 //
-// One 256-thread workgroup per 128 x 128 output tile and K split, 64-deep K stages: the x and w
-// tiles of a stage are copied HBM -> LDS with the gfx950 16-byte LDS DMA into a ring of two
-// stage buffers (the next stage's copy in flight behind the one being multiplied; 64 KB, so two
-// workgroups share a compute unit -- measured faster than three buffers and one workgroup), rows
-// chunk-swizzled (16-byte chunk c of row r at c ^ (r mod 8), so the 32 rows an operand read
-// touches at one chunk spread over all 16-byte bank groups); each wave computes a 64 x 64 quarter
-// with v_mfma_f32_32x32x16_bf16.  Tiles are ordered so that the workgroups sharing one weight tile
+// One 256-thread workgroup per BM x 128 output tile and K split, 64-deep K stages: the x and w
+// tiles of a stage are copied HBM -> LDS with the gfx950 16-byte LDS DMA into a ring of stage
+// buffers, rows chunk-swizzled (16-byte chunk c of row r at c ^ (r mod 8), so the 32 rows an
+// operand read touches at one chunk spread over all 16-byte bank groups); each wave computes a
+// BM/2 x 64 quarter with v_mfma_f32_32x32x16_bf16.  Two shapes: BM = 128 with two stage buffers
+// (the next stage's copy in flight behind the one being multiplied; 64 KB, two workgroups per
+// compute unit -- measured faster than three buffers and one workgroup) for the compute-bound
+// mixed step, and BM = 64 with three (72 KB, still two workgroups per unit, two stages of weights
+// in flight) for a decode-only step's few rows, where the weight stream is the whole cost and the
+// bytes in flight set its rate.  Tiles are ordered so that the workgroups sharing one weight tile
 // run on one XCD (workgroup b runs on XCD b mod 8) and read it through that XCD's L2.  A layer
 // with few tiles (a decode-only step's rows) splits K so that at least 256 workgroups stream the
 // weights: each split writes float32 partials and a second kernel sums them in split order (the
@@ -28,22 +31,27 @@
 namespace cb {
 namespace {
 
-constexpr int kBM = 128, kBN = 128, kBK = 64;
+constexpr int kBK = 64;
+constexpr int kNAlign = 128;                       // N must be a multiple of this (every tile width)
 constexpr int kRowBytes = kBK * 2;                 // bytes of one tile row in one stage
-constexpr int kTileBytes = kBM * kRowBytes;        // 16 KB (the x tile; the w tile is the same)
-#ifndef CB_LINEAR_STAGES
-#define CB_LINEAR_STAGES 2                         // LDS ring depth (stage buffers of 32 KB)
+#ifndef CB_LINEAR_SKINNY_M
+#define CB_LINEAR_SKINNY_M 64                      // M up to this: 64-row tiles, a deeper ring
+#endif
+#ifndef CB_LINEAR_SKINNY_STAGES
+#define CB_LINEAR_SKINNY_STAGES 3                  // stage buffers of those
+#endif
+#ifndef CB_LINEAR_SKINNY_BN
+#define CB_LINEAR_SKINNY_BN 64                     // and their tile width
 #endif
 #ifndef CB_LINEAR_MIN_WG
 #define CB_LINEAR_MIN_WG 256                       // K is split until the grid has this many
 #endif
-constexpr int kStages = CB_LINEAR_STAGES;
-static_assert(kStages == 2 || kStages == 3, "ring depth");
-constexpr int kCopiesPerStage = 8;                 // DMA instructions per wave per stage
 constexpr int64_t kMinWorkgroups = CB_LINEAR_MIN_WG;
 constexpr int kMaxSplit = 16;
 constexpr int kMinStagesPerSplit = 4;
-static_assert(kBM == kBN, "one copy layout for both operands");
+
+int32_t tile_rows(int32_t M) { return M <= CB_LINEAR_SKINNY_M ? 64 : 128; }
+int32_t tile_cols(int32_t M) { return M <= CB_LINEAR_SKINNY_M ? CB_LINEAR_SKINNY_BN : 128; }
 
 // K splits for a shape: the smallest power of two giving kMinWorkgroups workgroups, at most
 // kMaxSplit, dividing the K stages evenly and keeping kMinStagesPerSplit stages per split.
@@ -76,97 +84,117 @@ __device__ __forceinline__ void dma16(const void* src, const char* lds_dst) {
 }
 __device__ __forceinline__ int swz(int c, int r) { return c ^ (r & 7); }
 
+// Wait until at most `later` stages' copies of this wave are outstanding (copies complete in
+// issue order), then the workgroup barrier.
+template <int CPS>
+__device__ __forceinline__ void wait_stage_copies(int later) {
+  if (later >= 2) asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * CPS) : "memory");
+  else if (later == 1) asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(CPS) : "memory");
+  else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <int BM, int BN, int NS>
 __global__ __launch_bounds__(256) void linear_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict__ w,
                                                      bf16_t* __restrict__ y, float* __restrict__ part,
                                                      int32_t M, int32_t N, int32_t K, int32_t m_tiles,
                                                      int32_t splits, int32_t items, int32_t per_xcd) {
-  __shared__ __attribute__((aligned(1024))) char lds[kStages * 2 * kTileBytes];   // [stage][x | w]
+  static_assert((BM == 64 || BM == 128) && (BN == 64 || BN == 128) && NS >= 2 && NS <= 4, "tile shape and ring depth");
+  constexpr int XC = BM / 32;                        // x copies per wave per stage (8 rows each)
+  constexpr int WC = BN / 32;                        // w copies per wave per stage
+  constexpr int CPS = XC + WC;                       // copies per wave per stage
+  constexpr int MI = BM / 64;                        // 32-row fragments of a wave's quarter
+  constexpr int NJ = BN / 64;                        // 32-column fragments of it
+  constexpr int XBYTES = BM * kRowBytes;
+  constexpr int SBYTES = XBYTES + BN * kRowBytes;    // one stage: [x | w]
+  __shared__ __attribute__((aligned(1024))) char lds[NS * SBYTES];
   const int32_t b = blockIdx.x;
   const int32_t it = (b & 7) * per_xcd + (b >> 3);   // item = (tile, split), split fastest
   if (it >= items) return;
   const int32_t t = it / splits, split = it - t * splits;
-  const int32_t m0 = (t % m_tiles) * kBM, n0 = (t / m_tiles) * kBN;
+  const int32_t m0 = (t % m_tiles) * BM, n0 = (t / m_tiles) * BN;
   const int32_t nk = K / kBK / splits, kt0 = split * nk;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int wm = wave >> 1, wn = wave & 1;
 
-  // Copy j of this wave fills tile bytes [1024 (4 wave + j), + 1024): rows 8 (4 wave + j) + lane / 8,
-  // physical chunk lane % 8 (logical chunk lane % 8 ^ row % 8).  Rows of x past M repeat row M - 1
-  // (their results are not stored).
-  const char* xs[4];
-  const char* ws[4];
+  // Copy j of this wave fills tile bytes [1024 (XC wave + j), + 1024) of x (j < XC) and
+  // [1024 (WC wave + j), + 1024) of w: rows 8 (that index) + lane / 8, physical chunk lane % 8
+  // (logical chunk lane % 8 ^ row % 8).  Rows of x past M repeat row M - 1 (their results are
+  // not stored).
+  const char* xs[XC];
+  const char* ws[WC];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int r = 8 * (4 * wave + j) + (lane >> 3);
-    const int c = swz(lane & 7, r);
-    xs[j] = reinterpret_cast<const char*>(x + static_cast<int64_t>(std::min(m0 + r, M - 1)) * K) + 16 * c;
-    ws[j] = reinterpret_cast<const char*>(w + static_cast<int64_t>(n0 + r) * K) + 16 * c;
+  for (int j = 0; j < XC; ++j) {
+    const int r = 8 * (XC * wave + j) + (lane >> 3);
+    xs[j] = reinterpret_cast<const char*>(x + static_cast<int64_t>(std::min(m0 + r, M - 1)) * K) + 16 * swz(lane & 7, r);
+  }
+#pragma unroll
+  for (int j = 0; j < WC; ++j) {
+    const int r = 8 * (WC * wave + j) + (lane >> 3);
+    ws[j] = reinterpret_cast<const char*>(w + static_cast<int64_t>(n0 + r) * K) + 16 * swz(lane & 7, r);
   }
   auto issue = [&](int32_t kt, int buf) {
-    const char* xt = lds + buf * 2 * kTileBytes;
-    const char* wt = xt + kTileBytes;
+    const char* xt = lds + buf * SBYTES;
+    const char* wt = xt + XBYTES;
     const int64_t koff = static_cast<int64_t>(kt0 + kt) * kRowBytes;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      dma16(xs[j] + koff, xt + 1024 * (4 * wave + j));
-      dma16(ws[j] + koff, wt + 1024 * (4 * wave + j));
-    }
+    for (int j = 0; j < XC; ++j) dma16(xs[j] + koff, xt + 1024 * (XC * wave + j));
+#pragma unroll
+    for (int j = 0; j < WC; ++j) dma16(ws[j] + koff, wt + 1024 * (WC * wave + j));
   };
 
-  f32x16 acc[2][2];
+  f32x16 acc[MI][NJ];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   const int lr = lane & 31, lh = lane >> 5;
-  // Copies run kStages - 1 stages ahead of the matrix work.
-  for (int p = 0; p < kStages - 1; ++p)
+  // Copies run NS - 1 stages ahead of the matrix work.
+  for (int p = 0; p < NS - 1; ++p)
     if (p < nk) issue(p, p);
   for (int32_t kt = 0; kt < nk; ++kt) {
     // This wave's copies of stage kt have landed once at most the later stages' copies already
-    // issued are outstanding (copies complete in issue order); after the barrier every wave's have,
-    // and every wave has finished reading stage kt - 1's buffer, which the next copy overwrites.
-    if (kStages == 3 && kt + 1 < nk) asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kCopiesPerStage) : "memory");
-    else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-    if (kt + kStages - 1 < nk) issue(kt + kStages - 1, (kt + kStages - 1) % kStages);
-    const char* xt = lds + (kt % kStages) * 2 * kTileBytes;
-    const char* wt = xt + kTileBytes;
+    // issued are outstanding; after the barrier every wave's have, and every wave has finished
+    // reading stage kt - 1's buffer, which the next copy overwrites.
+    wait_stage_copies<CPS>(min(NS - 2, nk - 1 - kt));
+    if (kt + NS - 1 < nk) issue(kt + NS - 1, (kt + NS - 1) % NS);
+    const char* xt = lds + (kt % NS) * SBYTES;
+    const char* wt = xt + XBYTES;
 #pragma unroll
     for (int kk = 0; kk < kBK / 16; ++kk) {
       const int c = 2 * kk + lh;                   // 16-byte chunk: slots 8 (l / 32) .. + 7 of step kk
-      Frag<bf16_t> a[2], bw[2];
+      Frag<bf16_t> a[MI], bw[NJ];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int r = 64 * wm + 32 * i + lr;
+      for (int i = 0; i < MI; ++i) {
+        const int r = (BM / 2) * wm + 32 * i + lr;
         a[i].u = *reinterpret_cast<const uint4*>(xt + r * kRowBytes + 16 * swz(c, r));
       }
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int r = 64 * wn + 32 * j + lr;
+      for (int j = 0; j < NJ; ++j) {
+        const int r = (BN / 2) * wn + 32 * j + lr;
         bw[j].u = *reinterpret_cast<const uint4*>(wt + r * kRowBytes + 16 * swz(c, r));
       }
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) mma32_k16(acc[i][j], a[i], bw[j]);
+        for (int j = 0; j < NJ; ++j) mma32_k16(acc[i][j], a[i], bw[j]);
     }
   }
 
-  // acc[i][j] register r: row 64 wm + 32 i + acc32_row(lane, r), column 64 wn + 32 j + lane % 32.
+  // acc[i][j] register r: row (BM/2) wm + 32 i + acc32_row(lane, r), column (BN/2) wn + 32 j + lane % 32.
   float* pt = splits > 1 ? part + static_cast<int64_t>(split) * M * N : nullptr;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int32_t row = m0 + 64 * wm + 32 * i + acc32_row(lane, r);
+      const int32_t row = m0 + (BM / 2) * wm + 32 * i + acc32_row(lane, r);
       if (row >= M) continue;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int64_t o = static_cast<int64_t>(row) * N + n0 + 64 * wn + 32 * j + lr;
+      for (int j = 0; j < NJ; ++j) {
+        const int64_t o = static_cast<int64_t>(row) * N + n0 + (BN / 2) * wn + 32 * j + lr;
         if (pt) pt[o] = acc[i][j][r];
         else reinterpret_cast<uint16_t*>(y)[o] = f32_to_bf16_bits(acc[i][j][r]);
       }
@@ -191,8 +219,9 @@ __global__ __launch_bounds__(256) void linear_reduce_kernel(const float* __restr
 
 extern "C" size_t cb_linear_workspace_bytes(int32_t M, int32_t N, int32_t K) {
   using namespace cb;
-  if (M < 1 || N < 1 || K < 1 || N % kBN || K % kBK) return 0;
-  const int64_t tiles = ((static_cast<int64_t>(M) + kBM - 1) / kBM) * (N / kBN);
+  if (M < 1 || N < 1 || K < 1 || N % kNAlign || K % kBK) return 0;
+  const int32_t bm = tile_rows(M), bn = tile_cols(M);
+  const int64_t tiles = ((static_cast<int64_t>(M) + bm - 1) / bm) * (N / bn);
   const int32_t s = k_splits(tiles, K);
   return s > 1 ? static_cast<size_t>(s) * M * N * sizeof(float) : 0;
 }
@@ -201,13 +230,14 @@ extern "C" int cb_linear(void* stream, int32_t dtype, int32_t M, int32_t N, int3
                          const void* w, void* y, void* workspace, size_t workspace_bytes) {
   using namespace cb;
   if (dtype != CB_BF16) return CB_ERR_INVALID;
-  if (M < 0 || N < 1 || K < 1 || N % kBN || K % kBK) return CB_ERR_INVALID;
+  if (M < 0 || N < 1 || K < 1 || N % kNAlign || K % kBK) return CB_ERR_INVALID;
   if (M == 0) return CB_OK;
   if (!x || !w || !y) return CB_ERR_INVALID;
   for (const void* p : {x, w, static_cast<const void*>(y)})
     if (reinterpret_cast<uintptr_t>(p) & 15u) return CB_ERR_INVALID;
-  const int64_t m_tiles = (static_cast<int64_t>(M) + kBM - 1) / kBM;
-  const int64_t tiles = m_tiles * (N / kBN);
+  const int32_t bm = tile_rows(M), bn = tile_cols(M);
+  const int64_t m_tiles = (static_cast<int64_t>(M) + bm - 1) / bm;
+  const int64_t tiles = m_tiles * (N / bn);
   const int32_t splits = k_splits(tiles, K);
   if (splits > 1) {
     if (workspace_bytes < cb_linear_workspace_bytes(M, N, K)) return CB_ERR_CAPACITY;
@@ -218,7 +248,8 @@ extern "C" int cb_linear(void* stream, int32_t dtype, int32_t M, int32_t N, int3
   if (per_xcd * 8 > 0x7fffffff) return CB_ERR_INVALID;
   hipStream_t st = static_cast<hipStream_t>(stream);
   float* part = static_cast<float*>(workspace);
-  linear_kernel<<<dim3(static_cast<uint32_t>(per_xcd * 8)), dim3(256), 0, st>>>(
+  auto kernel = bm == 64 ? linear_kernel<64, CB_LINEAR_SKINNY_BN, CB_LINEAR_SKINNY_STAGES> : linear_kernel<128, 128, 2>;
+  kernel<<<dim3(static_cast<uint32_t>(per_xcd * 8)), dim3(256), 0, st>>>(
       static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(w), static_cast<bf16_t*>(y), part, M, N, K,
       static_cast<int32_t>(m_tiles), splits, static_cast<int32_t>(items), static_cast<int32_t>(per_xcd));
   if (hipGetLastError() != hipSuccess) return CB_ERR_HIP;
