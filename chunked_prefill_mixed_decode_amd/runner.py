@@ -5,6 +5,11 @@ K/V caches (``[num_blocks, Hkv, block_size, D]``), the rotary table, a ring of t
 metadata buffers, the device copy of the metadata and the attention workspace.  Each call below
 forwards to one C entry point of libcb.so; the runner only allocates and orders them on the
 current torch stream.
+
+The host stays at most two steps ahead of the device (the pinned-buffer ring), so a host stall
+longer than two steps' device time leaves the GPU idle.  Python's cyclic collector is one: a pass
+over a process's long-lived objects takes about a millisecond.  A serving loop should
+``gc.collect(); gc.freeze()`` once its set-up is done, as ``bench.py`` does.
 """
 from __future__ import annotations
 
