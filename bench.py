@@ -285,14 +285,14 @@ def main():
     import torch
 
     from synth import workloads
-    from tests.gpu_harness import GpuRun
+    from tests.gpu_harness import DeviceRun
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     w = workloads.get(args.config)
     cb_steps = w.steps
     print(f"[bench] set-up {w.name}: {len(w.decode_ctx)} decodes, {w.num_blocks} blocks", file=sys.stderr, flush=True)
-    g = GpuRun(w, dev, sentinel=False)
+    g = DeviceRun(w, dev, sentinel=False)
     cb = g.cb
     snapshot = cb.cb_sched_clone(g.sched)
 

@@ -112,11 +112,11 @@ def config5() -> Workload:
                  ((262144 + 2048, 262144),), 1, 1005, rng)
 
 
-CONFIGS = {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}
+BUILDERS = {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}
 
 
 def get(i: int) -> Workload:
-    return CONFIGS[i]()
+    return BUILDERS[i]()
 
 
 def small(i: int) -> Workload:

@@ -17,7 +17,7 @@ from oracle import attention as oattn
 from oracle import rope as orope
 from oracle.builder import RefBuilder
 from synth import values, workloads
-from tests.gpu_harness import TORCH_DTYPE, GpuRun, cached_tokens, step_caps  # noqa: F401
+from tests.gpu_harness import TORCH_DTYPE, DeviceRun, cached_tokens, step_caps  # noqa: F401
 
 TOL = {"f32": (1e-4, 0.0), "bf16": (2e-2, 1e-2)}        # (atol, rtol)
 

@@ -10,7 +10,7 @@ import pytest
 import torch
 
 from synth import workloads
-from tests.gpu_harness import GpuRun
+from tests.gpu_harness import DeviceRun
 
 pytestmark = pytest.mark.gpu
 
@@ -25,7 +25,7 @@ def dev():
 def test_graph_replay_equals_eager(dev, i):
     from chunked_prefill_mixed_decode_amd.runner import StepGraphs
     w = workloads.small(i)
-    g = GpuRun(w, dev)
+    g = DeviceRun(w, dev)
     cb = g.cb
     snap = cb.cb_sched_clone(g.sched)
     # Cycle length: steps until the prompts are done, bounded.

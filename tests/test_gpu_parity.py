@@ -13,7 +13,7 @@ import torch
 from oracle import attention as oattn
 from oracle import rope as orope
 from synth import workloads
-from tests.harness import GpuRun, OracleRun, bits_of, compare, plan_of_meta
+from tests.harness import DeviceRun, OracleRun, bits_of, compare, plan_of_meta
 
 pytestmark = pytest.mark.gpu
 
@@ -37,7 +37,7 @@ def check_metadata(meta, plan):
         assert got[k] == plan[k], k
 
 
-def check_step_kv(gpu: GpuRun, ora: OracleRun, plan, rows):
+def check_step_kv(gpu: DeviceRun, ora: OracleRun, plan, rows):
     """K/V written by the step's ``rows`` are bit-exact."""
     cu = plan["cu_seqlens_q"]
     for s in range(plan["num_seqs"]):
@@ -58,7 +58,7 @@ def check_step_kv(gpu: GpuRun, ora: OracleRun, plan, rows):
             assert not len(bad), f"{name} slots of request {rid}"
 
 
-def check_q_rot(gpu: GpuRun, ora: OracleRun, plan, q_rot, rows):
+def check_q_rot(gpu: DeviceRun, ora: OracleRun, plan, q_rot, rows):
     cu = plan["cu_seqlens_q"]
     got = q_rot.float().cpu().numpy()
     for s in range(plan["num_seqs"]):
@@ -70,7 +70,7 @@ def check_q_rot(gpu: GpuRun, ora: OracleRun, plan, q_rot, rows):
         assert np.array_equal(bits_of(got[srows], gpu.w.dtype), bits_of(want, gpu.w.dtype))
 
 
-def check_outputs(gpu: GpuRun, ora: OracleRun, plan, out, rows, tag):
+def check_outputs(gpu: DeviceRun, ora: OracleRun, plan, out, rows, tag):
     want = ora.expected_rows(plan, rows)
     got = out.float().cpu().numpy()
     rs = sorted(want)
@@ -102,7 +102,7 @@ def sample_rows(plan, n_dec, n_chunk, seed):
 def test_small_workload_every_row_every_step(dev, i):
     w = workloads.small(i)
     say(f"[{w.name}] set-up")
-    gpu = GpuRun(w, dev)
+    gpu = DeviceRun(w, dev)
     ora = OracleRun(w, value_device=dev)
     step = 0
     while (w.steps is None and ora.b.pending_prompts() > 0) or (w.steps is not None and step < w.steps):
@@ -142,7 +142,7 @@ def test_full_workload_sampled(dev, cfg):
     w = workloads.get(cfg)
     n_dec, n_chunk, every = FULL_SAMPLE[cfg]
     say(f"[{w.name}] set-up: {len(w.decode_ctx)} decodes, {w.num_blocks} blocks")
-    gpu = GpuRun(w, dev)
+    gpu = DeviceRun(w, dev)
     ora = OracleRun(w, value_device=dev)
     step = 0
     while (w.steps is None and ora.b.pending_prompts() > 0) or (w.steps is not None and step < w.steps):
@@ -169,7 +169,7 @@ def test_chunked_run_equals_monolithic_run(dev):
     # final cache; rows match the unchunked computation.
     w = workloads.small(2)
     big = w.budget * 8
-    chunked, mono = GpuRun(w, dev), GpuRun(w, dev, max_budget=big)
+    chunked, mono = DeviceRun(w, dev), DeviceRun(w, dev, max_budget=big)
     prompt = len(w.decode_ctx)
     outs_c, outs_m = {}, {}
     while True:
@@ -198,13 +198,13 @@ def test_chunked_run_equals_monolithic_run(dev):
     assert np.array_equal(a[2], b[2]) and np.array_equal(a[3], b[3])     # bit-identical K and V
 
 
-def gpu_pending(g: GpuRun) -> int:
+def gpu_pending(g: DeviceRun) -> int:
     return g.cb.cb_sched_pending_prompts(g.sched)
 
 
 def test_run_to_run_bitwise_determinism_and_decode_isolation(dev):
     w = workloads.small(4)
-    g = GpuRun(w, dev)
+    g = DeviceRun(w, dev)
     g.step()                                   # advance once so chunks have a cached prefix
     snap = g.cb.cb_sched_clone(g.sched)
     meta, out1, _ = g.step()
@@ -224,7 +224,7 @@ def test_planted_mistakes_are_caught(dev):
     # zwjcode §07: a chunk's positions restarted at 0, or its rows blind to the cached prefix,
     # give different results; planted in the oracle, they must fail the parity bar.
     w = workloads.small(3)
-    gpu, ora = GpuRun(w, dev), OracleRun(w, value_device=dev)
+    gpu, ora = DeviceRun(w, dev), OracleRun(w, value_device=dev)
     for _ in range(2):
         plan = ora.build()
         meta, out, _ = gpu.step()
@@ -269,7 +269,7 @@ def test_edge_steps(dev):
     del rng
     for w in cases:
         say(f"[{w.name}]")
-        gpu, ora = GpuRun(w, dev), OracleRun(w, value_device=dev)
+        gpu, ora = DeviceRun(w, dev), OracleRun(w, value_device=dev)
         for step in range(w.steps):
             plan = ora.build()
             meta, out, q_rot = gpu.step()
@@ -299,7 +299,7 @@ def test_block_sizes_and_group_widths(dev):
     ]
     for w in cases:
         say(f"[{w.name}]")
-        gpu, ora = GpuRun(w, dev), OracleRun(w, value_device=dev)
+        gpu, ora = DeviceRun(w, dev), OracleRun(w, value_device=dev)
         for step in range(w.steps):
             plan = ora.build()
             meta, out, q_rot = gpu.step()
@@ -355,7 +355,7 @@ def test_host_decode_plan_matches_device_split(dev, i):
     # the device.  Same rule, so the outputs must agree bit for bit; a plan made for another wave
     # count is refused.
     w = workloads.small(i)
-    g = GpuRun(w, dev)
+    g = DeviceRun(w, dev)
     cb = g.cb
     for _ in range(2):
         meta = g.runner.build(g.sched, w.budget)
