@@ -243,6 +243,13 @@ def test_device_entry_points_reject_bad_arguments_on_the_host():
     assert need > 0
     assert lib.cb_mixed_paged_attention(None, 1, 2, 1, 5, 4, 10, 10, 8, 4, 128, 16, 0.1, *([p] * 7),
                                         p, aligned, need - 1) == cb.CB_ERR_CAPACITY
+    # Empty inputs are valid and touch nothing: a step with no rows, no tokens to append, M = 0.
+    assert lib.cb_mixed_paged_attention(None, 1, 0, 0, 0, 0, 0, 0, 8, 4, 128, 16, 0.1, *([None] * 8),
+                                        None, 0) == cb.CB_OK
+    assert lib.cb_attn_workspace_bytes(0, 0, 0, 0, 0, 0, 8, 4, 128) == 0
+    assert lib.cb_rope_kv_append(None, 1, 0, 4, 4, 128, 16, None, None, None, None, None, None, 8,
+                                 None, None, None, 4) == cb.CB_OK
+    assert lib.cb_linear(None, 1, 0, 128, 64, None, None, None, None, 0) == cb.CB_OK
 
 
 def test_workspace_grows_with_context_and_rows():

@@ -284,8 +284,9 @@ def test_edge_steps(dev):
 
 def test_block_sizes_and_group_widths(dev):
     """Cache blocks of 32, 64 and 256 tokens (a 32-key chunk stage lies inside one block, the block
-    address is shared by many stages, partial blocks at both ends of a context) and a 24-head
-    group (two 16-head blocks per KV head, the second one ragged), every row of every step."""
+    address is shared by many stages, partial blocks at both ends of a context), a 24-head group
+    (two 16-head blocks per KV head, the second one ragged) and a 128-head group (eight blocks per
+    KV head; a chunk tile holds one position), every row of every step."""
     from synth.workloads import _make
     cases = [
         _make("edge_bs64_gqa4", "bf16", 8, 2, 128, 64, 200, (300, 1, 129, 700), ((500, 0), (70, 0)), 4, 3011,
@@ -296,6 +297,9 @@ def test_block_sizes_and_group_widths(dev):
               np.random.default_rng(13)),
         _make("edge_d64_bs32", "bf16", 8, 8, 64, 32, 100, (64, 65), ((150, 0),), 3, 3014,
               np.random.default_rng(14)),
+        # the widest group a chunk tile holds: 128 query heads on one KV head, one position a tile
+        _make("edge_group128", "bf16", 128, 1, 64, 16, 40, (70, 3), ((50, 0),), 2, 3015,
+              np.random.default_rng(15)),
     ]
     for w in cases:
         say(f"[{w.name}]")
