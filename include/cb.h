@@ -10,6 +10,7 @@
  *   [P1] "Chunked Prefill: Ending the Great Stall" (manishklach.github.io), §02-§05.
  *   [P2] "Splitting Prefill From Decode Inside a Step" (mercemay.com).
  *   [P3] "Chunked Prefill 的 Token 预算" (zwjcode.cn), §02-§11.
+ *   [P4] the sference.com post on prefill head-of-line blocking (by section heading).
  *
  * Conventions for every function:
  *   - The return value is a status code (CB_OK = 0, negative on error).  No C++ exception
