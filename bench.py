@@ -18,7 +18,8 @@ context and of every chunk's visible keys, plus q and out) divided by its averag
 measured with HIP events on the launch stream over the timed steps.  ``isolated`` times
 decode-only and chunk-only launches of the same metadata.
 ``cpu_baseline`` times the CPU oracle (reference builder + fp64 full-prefill attention with
-rotary embedding) on one step of the same workload.
+rotary embedding) on the workload's steps in order, whole steps until ``--cpu-budget-s`` seconds
+of oracle time (default 25) have been spent.
 """
 from __future__ import annotations
 
@@ -44,7 +45,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=2, help="workload index (default: the budget-512 layer)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-step", type=int, default=8)
+    ap.add_argument("--cpu-budget-s", type=float, default=25.0,
+                    help="oracle seconds the CPU baseline may spend (whole steps, at least one)")
     ap.add_argument("--json-out", default=None)
     ap.add_argument("--event-every", type=int, default=7,
                     help="record the per-kernel and per-step HIP events on every n-th timed step "
@@ -221,9 +223,10 @@ def summarize_isolated(dec, chk, metas, w, elt):
     return out
 
 
-def cpu_baseline(w, step_index: int):
-    """The oracle on one step: Python reference builder up to that step, then fp64 attention
-    (rotary embedding included) of all the step's rows.  Raw inputs are generated beforehand."""
+def cpu_baseline(w, n_steps: int, budget_s: float):
+    """The oracle on the cycle's steps in order (Python reference builder, then fp64 attention with
+    the rotary embedding of all of a step's rows), until budget_s seconds of oracle time have been
+    spent (at least one step).  Each step's raw inputs are generated before its timed part."""
     import numpy as np
 
     from oracle import attention as oattn
@@ -242,38 +245,44 @@ def cpu_baseline(w, step_index: int):
         b.add_running(c)
     for L, cached in w.prompts:
         b.add_prompt(L, cached)
-    for _ in range(step_index):
-        b.build(w.budget)
-    # inputs of the step (untimed): raw q/k/v of every sequence up to its last row
-    probe = b.clone().build(w.budget)
     dt = TORCH_DTYPE[w.dtype]
-    raw = {}
-    cu = probe["cu_seqlens_q"]
-    for s in range(probe["num_seqs"]):
-        rid = probe["seq_ids"][s]
-        last = probe["context_lens"][s]
-        pos = list(range(probe["positions"][cu[s]], probe["positions"][cu[s + 1] - 1] + 1))
-        raw[rid] = (values.range_values(w.seed, "k", rid, 0, last, w.Hkv, w.D, dt).float().numpy(),
-                    values.range_values(w.seed, "v", rid, 0, last, w.Hkv, w.D, dt).float().numpy(),
-                    values.token_values(w.seed, "q", rid, pos, w.Hq, w.D, dt).float().numpy())
     table = orope.cos_sin_table(w.max_position(), w.D)
-    t0 = time.perf_counter()
-    plan = b.build(w.budget)
-    cu = plan["cu_seqlens_q"]
     rows = 0
-    for s in range(plan["num_seqs"]):
-        rid = plan["seq_ids"][s]
-        k, v, q = raw[rid]
-        pos = np.array(plan["positions"][cu[s]:cu[s + 1]])
-        kh = orope.rotate_stored(k, np.arange(k.shape[0]), table, w.dtype)
-        qh = orope.rotate_stored(q, pos, table, w.dtype)
-        oattn.attend(qh, kh, v, pos, 1.0 / np.sqrt(w.D))
-        rows += len(pos)
-    el = time.perf_counter() - t0
+    el = 0.0
+    done = 0
+    for step in range(n_steps):
+        # inputs of the step (untimed): raw q/k/v of every sequence up to its last row
+        probe = b.clone().build(w.budget)
+        raw = {}
+        cu = probe["cu_seqlens_q"]
+        for s in range(probe["num_seqs"]):
+            rid = probe["seq_ids"][s]
+            last = probe["context_lens"][s]
+            pos = list(range(probe["positions"][cu[s]], probe["positions"][cu[s + 1] - 1] + 1))
+            raw[rid] = (values.range_values(w.seed, "k", rid, 0, last, w.Hkv, w.D, dt).float().numpy(),
+                        values.range_values(w.seed, "v", rid, 0, last, w.Hkv, w.D, dt).float().numpy(),
+                        values.token_values(w.seed, "q", rid, pos, w.Hq, w.D, dt).float().numpy())
+        t0 = time.perf_counter()
+        plan = b.build(w.budget)
+        cu = plan["cu_seqlens_q"]
+        for s in range(plan["num_seqs"]):
+            rid = plan["seq_ids"][s]
+            k, v, q = raw[rid]
+            pos = np.array(plan["positions"][cu[s]:cu[s + 1]])
+            kh = orope.rotate_stored(k, np.arange(k.shape[0]), table, w.dtype)
+            qh = orope.rotate_stored(q, pos, table, w.dtype)
+            oattn.attend(qh, kh, v, pos, 1.0 / np.sqrt(w.D))
+            rows += len(pos)
+        el += time.perf_counter() - t0
+        done += 1
+        del raw
+        if el >= budget_s:
+            break
     return {"value": rows / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "seconds": el,
-            "sample": f"step {step_index} of the cycle: reference builder + rotary + fp64 causal "
-                      f"attention of all {rows} rows x {w.Hq} heads (raw inputs pre-generated)"}
+            "sample": f"steps 0-{done - 1} of the {n_steps}-step cycle ({rows} rows x {w.Hq} heads): "
+                      f"reference builder + rotary + fp64 causal attention (raw inputs pre-generated), "
+                      f"stopped after {budget_s:.0f} s of oracle time"}
 
 
 def main():
@@ -485,7 +494,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)...", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(w, min(args.cpu_sample_step, cb_steps - 1))
+        res["cpu_baseline"] = cpu_baseline(w, cb_steps, args.cpu_budget_s)
     line = json.dumps(res)
     print(line, flush=True)
     if args.json_out:
