@@ -285,8 +285,10 @@ def test_edge_steps(dev):
 def test_block_sizes_and_group_widths(dev):
     """Cache blocks of 32, 64 and 256 tokens (a 32-key chunk stage lies inside one block, the block
     address is shared by many stages, partial blocks at both ends of a context), a 24-head group
-    (two 16-head blocks per KV head, the second one ragged) and a 128-head group (eight blocks per
-    KV head; a chunk tile holds one position), every row of every step."""
+    (two 16-head blocks per KV head, the second one ragged), 16- and 32-head groups (whole blocks),
+    a 128-head group (eight blocks per KV head; a chunk tile holds one position), cache blocks of
+    128 tokens, and a chunk-only step whose keys are split the maximum 8 ways; every row of every
+    step."""
     from synth.workloads import _make
     cases = [
         _make("edge_bs64_gqa4", "bf16", 8, 2, 128, 64, 200, (300, 1, 129, 700), ((500, 0), (70, 0)), 4, 3011,
@@ -299,7 +301,14 @@ def test_block_sizes_and_group_widths(dev):
               np.random.default_rng(14)),
         # the widest group a chunk tile holds: 128 query heads on one KV head, one position a tile
         _make("edge_group128", "bf16", 128, 1, 64, 16, 40, (70, 3), ((50, 0),), 2, 3015,
-              np.random.default_rng(15)),
+              np.random.default_rng(15)),        # exactly one and exactly two 16-head blocks per KV head; cache blocks of 128 tokens
+        _make("edge_group16", "bf16", 32, 2, 128, 16, 120, (200, 17), ((150, 0),), 2, 3016,
+              np.random.default_rng(16)),
+        _make("edge_group32_bs128", "bf16", 64, 2, 64, 128, 120, (300, 129), ((260, 0),), 3, 3017,
+              np.random.default_rng(17)),
+        # a 20-token chunk after 3000 cached tokens, no decodes: two tiles, keys split 8 ways
+        _make("edge_split8", "bf16", 2, 2, 128, 16, 20, (), ((3020, 3000),), 1, 3018,
+              np.random.default_rng(18)),
     ]
     for w in cases:
         say(f"[{w.name}]")
