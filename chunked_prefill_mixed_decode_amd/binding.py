@@ -81,7 +81,7 @@ EXPORTS = {
                                                       _sz, _vp, _i32, ctypes.POINTER(_vp)]),
     "cb_attn_decode_waves": (_i32, [_vp, _i32]),
     "cb_decode_plan_ints": (_sz, [_i32, _i32]),
-    "cb_decode_plan": (ctypes.c_int, [_vp, _i32, _pi32, _i32, _i32, _i32, _pi32, _sz]),
+    "cb_decode_plan": (ctypes.c_int, [_vp, _i32, _i32, _i32, _i32, _i32, _i32, _pi32, _pi32, _pi32, _sz]),
 }
 
 
@@ -346,19 +346,25 @@ def cb_decode_plan_ints(num_decodes: int, n_waves: int) -> int:
     return int(_lib().cb_decode_plan_ints(num_decodes, n_waves))
 
 
-def cb_decode_plan(context_lens, Hq: int, Hkv: int, out, device_or_stream=None,
-                   has_chunks: bool = True) -> int:
-    """context_lens: host int32 tensor of the decode rows' context lengths; out: host int32 tensor
-    of at least cb_decode_plan_ints(len(context_lens), n_waves) entries.  The plan is for an
-    attention call on the device of the stream (default: current) with or without chunk rows;
-    returns its wave count (the call's plan_waves)."""
-    if context_lens.dtype != torch.int32 or out.dtype != torch.int32 or context_lens.is_cuda or out.is_cuda:
+def cb_decode_plan(cu_seqlens_q, context_lens, num_decodes: int, max_q_len: int, max_ctx: int,
+                   Hq: int, Hkv: int, out, device_or_stream=None) -> int:
+    """Host-made decode split for an attention call over the step (num_seqs = len(context_lens)
+    rows, decode rows first) with the same shape arguments.  cu_seqlens_q, context_lens: host int32
+    tensors (cu_seqlens_q may be None when every row decodes); out: host int32 tensor of at least
+    cb_decode_plan_ints(num_decodes, n_waves) entries.  The plan is for an attention call on the
+    device of the stream (default: current); returns its wave count (the call's plan_waves)."""
+    tensors = [t for t in (cu_seqlens_q, context_lens, out) if t is not None]
+    if any(t.dtype != torch.int32 or t.is_cuda for t in tensors):
         raise ValueError("cb_decode_plan: int32 host tensors")
-    if not context_lens.is_contiguous() or not out.is_contiguous():
+    if not all(t.is_contiguous() for t in tensors):
         raise ValueError("cb_decode_plan: contiguous tensors")
-    _check(_lib().cb_decode_plan(ctypes.c_void_p(_stream_arg(device_or_stream)), int(bool(has_chunks)),
-                                 _i32ptr(context_lens), context_lens.numel(), Hq, Hkv, _i32ptr(out),
-                                 out.numel()), "cb_decode_plan")
+    num_seqs = context_lens.numel()
+    if cu_seqlens_q is not None and cu_seqlens_q.numel() < num_seqs + 1:
+        raise ValueError("cb_decode_plan: cu_seqlens_q needs num_seqs + 1 entries")
+    _check(_lib().cb_decode_plan(ctypes.c_void_p(_stream_arg(device_or_stream)), num_seqs, num_decodes,
+                                 max_q_len, max_ctx, Hq, Hkv,
+                                 _i32ptr(cu_seqlens_q) if cu_seqlens_q is not None else None,
+                                 _i32ptr(context_lens), _i32ptr(out), out.numel()), "cb_decode_plan")
     return int(out[3])
 
 

@@ -60,10 +60,27 @@ namespace {
 #ifndef CB_DECODE_RATE_ODD_XCD
 #define CB_DECODE_RATE_ODD_XCD 88
 #endif
+// A decode workgroup whose compute unit also runs a chunk tile streams ~22% slower while the tile
+// runs (per-wave clocks of mixed launches); the tile lasts about CB_DECODE_SHARE_RATIO percent of
+// one decode wave stage per key stage of the tile.  Such a workgroup's rate is lowered by
+// CB_DECODE_SHARE_SLOW percent times the fraction of the decode launch the tile is estimated to
+// last (0 turns the adjustment off; 30 measured the shortest steps of 0, 22 and 30).
+#ifndef CB_DECODE_SHARE_SLOW
+#define CB_DECODE_SHARE_SLOW 30
+#endif
+#ifndef CB_DECODE_SHARE_RATIO
+#define CB_DECODE_SHARE_RATIO 75
+#endif
 static_assert(CB_DECODE_RATE_SECOND >= 50 && CB_DECODE_RATE_SECOND <= 100 &&
               CB_DECODE_RATE_ODD_XCD >= 50 && CB_DECODE_RATE_ODD_XCD <= 100, "decode rates in [50, 100]");
-// A split over W <= S / CB_DECODE_MIN_STAGES waves then gives every wave at least one stage.
-static_assert(CB_DECODE_MIN_STAGES * CB_DECODE_RATE_SECOND * CB_DECODE_RATE_ODD_XCD > 10000, "non-empty waves");
+static_assert(CB_DECODE_SHARE_SLOW >= 0 && CB_DECODE_SHARE_SLOW <= 40 && CB_DECODE_SHARE_RATIO >= 0 &&
+              CB_DECODE_SHARE_RATIO <= 1000, "shared-unit adjustment");
+// A split over W <= S / CB_DECODE_MIN_STAGES waves then gives every wave at least one stage: the
+// slowest workgroup's rate times CB_DECODE_MIN_STAGES exceeds the fastest one's (10^4).
+static_assert(CB_DECODE_MIN_STAGES *
+                  (CB_DECODE_RATE_SECOND < 100 - CB_DECODE_SHARE_SLOW ? CB_DECODE_RATE_SECOND : 100 - CB_DECODE_SHARE_SLOW) *
+                  CB_DECODE_RATE_ODD_XCD > 10000,
+              "non-empty waves");
 
 constexpr int kChunkRows = 128;   // rows per chunk tile: 4 waves x 32
 constexpr int kChunkKeys = 32;    // keys per LDS stage of a chunk tile
@@ -85,7 +102,8 @@ constexpr int kBlockWindow = 2048;                   // block ids per LDS window
 struct Plan {
   int32_t G = 1, head_blocks = 1, hw = 1, ups = 1;
   int32_t bmq = 128, q_blocks = 0, n_chunk = 0, nsplit = 1;
-  size_t dec_o = 0, dec_ml = 0, chk_o = 0, chk_ml = 0, dec_seq = 0, dec_wave = 0, dec_par = 0, dec_unit = 0;
+  size_t dec_o = 0, dec_ml = 0, chk_o = 0, chk_ml = 0, dec_seq = 0, dec_wave = 0, dec_pos = 0, dec_par = 0,
+         dec_unit = 0;
   size_t total = 0;
 };
 
@@ -120,6 +138,7 @@ Plan make_plan(int32_t num_seqs, int32_t nd, int32_t T, int32_t max_q_len, int32
   p.chk_ml = off; off = align256(off + chk_rows * 2 * sizeof(float));
   p.dec_seq = off;  off = align256(off + (nd > 0 ? static_cast<size_t>(nd + 1) * sizeof(int32_t) : 0));
   p.dec_wave = off; off = align256(off + (nd > 0 ? kMaxDecodeWaves * sizeof(int32_t) : 0));
+  p.dec_pos = off;  off = align256(off + (nd > 0 ? (kMaxDecodeWaves + 1) * sizeof(int32_t) : 0));
   p.dec_par = off;  off = align256(off + (nd > 0 ? 4 * sizeof(int32_t) : 0));
   p.dec_unit = off; off = align256(off + (nd > 0 ? static_cast<size_t>(nd) * p.ups * 2 * sizeof(int32_t) : 0));
   p.total = off;
@@ -141,6 +160,7 @@ struct AttnArgs {
   float* chk_ml;
   int32_t* dec_seq;      // [nd + 1] first stage of each decode row on the stage line; [nd] = total
   int32_t* dec_wave;     // [waves] unit holding each wave's first stage
+  int32_t* dec_pos;      // [W + 1] first stage of each wave's range; [W] = S
   int32_t* dec_par;      // [0] total stages S, [1] first-round workgroups F, [2] waves with work W
   int32_t* dec_unit;     // [units][2] waves holding each unit's first and last stage (written by them)
   int32_t num_seqs, nd, T, Hq, Hkv, G, bs, bs_shift;
@@ -399,29 +419,85 @@ template <> struct StageRegs<64> {
 // (m, l, o) in slot unit + wave: both indices grow along the line, so the slot is unique and a
 // unit's partials sit in consecutive slots.
 //
-// The prep workgroup scans the rows' stage counts into dec_seq (first stage of each row), picks W
-// and records the unit holding each wave's first stage; dec_par holds [S, F, W].
-__host__ __device__ __forceinline__ int64_t decode_wg_rate(int32_t b, int32_t F) {
-  return static_cast<int64_t>(b < F ? 100 : CB_DECODE_RATE_SECOND) * ((b & 1) ? CB_DECODE_RATE_ODD_XCD : 100);
-}
-__host__ __device__ __forceinline__ int64_t decode_rate_run(int64_t m) {   // m workgroups from an even index
-  return (m + 1) / 2 * 100 + m / 2 * CB_DECODE_RATE_ODD_XCD;
-}
-// C(w): summed rates of waves [0, w), four waves per workgroup (F even).
-__host__ __device__ __forceinline__ int64_t decode_rate_prefix(int32_t w, int32_t F) {
-  const int32_t b = w >> 2;
-  const int32_t n0 = b < F ? b : F;
-  return 4 * (100 * decode_rate_run(n0) + CB_DECODE_RATE_SECOND * decode_rate_run(b - n0)) +
-         (w & 3) * decode_wg_rate(b, F);
-}
+// Rates (percent products): 100, or CB_DECODE_RATE_SECOND for workgroups [F, 2F), times 100 or
+// CB_DECODE_RATE_ODD_XCD by XCD parity.  Beside chunk tiles, chunk workgroup b (the b-th after
+// the decode workgroups) is dispatched onto the compute unit of decode workgroup b < F; when every
+// decode wave of the launch has work (W = waves), that workgroup's rate loses CB_DECODE_SHARE_SLOW
+// x min(1, rho) percent, rho = the tile's key stages x CB_DECODE_SHARE_RATIO / 100 over the mean
+// stages per wave S / W (the share of the decode launch the tile lasts).  Smaller decode loads
+// keep the split they have without chunk rows (W = S / CB_DECODE_MIN_STAGES either way), so
+// their results do not depend on the chunk rows beside them.
+//
+// The prep workgroup (or the host, for a plan made there, with the same integer rule) scans the
+// rows' stage counts into dec_seq (first stage of each row), picks W, and records each wave's
+// start(w) in dec_pos (dec_pos[W] = S) and the unit holding its first stage; dec_par holds
+// [S, F, W].
 __host__ __device__ __forceinline__ int32_t decode_waves_used(int32_t S, int32_t n_waves) {
   if (S <= 0) return 0;
   const int32_t k = S / CB_DECODE_MIN_STAGES;
   return k < 1 ? 1 : (k > n_waves ? n_waves : k);
 }
-// start(w) with cw = C(W).  S < 2^31 and C(W) <= kMaxDecodeWaves * 10^4, so S C(w) fits int64.
-__host__ __device__ __forceinline__ int32_t decode_wave_start(int32_t w, int32_t S, int64_t cw, int32_t F) {
-  return static_cast<int32_t>(static_cast<int64_t>(S) * decode_rate_prefix(w, F) / cw);
+
+// Chunk tiles are numbered with the key split fastest, then the query block, the KV head and
+// the chunk.  The tile's chunk s, KV head g, query block qb, split sp, the chunk's first row and
+// length d, its cached prefix c, and the split's key stages [kt_lo, kt_hi).  False when the query
+// block lies past the chunk's end (the tile has no rows).
+struct TileSpan {
+  int32_t s, g, qb, sp, row0, d, c, kt_lo, kt_hi;
+};
+struct TileGrid {
+  int32_t nd, Hkv, q_blocks, nsplit, bmq;
+  int64_t n_tiles, per_xcd;     // tiles; chunk workgroups per XCD (launch order below)
+};
+__host__ __device__ __forceinline__ bool chunk_tile_span(int32_t tile, const TileGrid& tg, const int32_t* cu_q,
+                                                         const int32_t* ctx_lens, TileSpan& t) {
+  int32_t x = tile;
+  t.sp = x % tg.nsplit; x /= tg.nsplit;
+  t.qb = x % tg.q_blocks; x /= tg.q_blocks;
+  t.g = x % tg.Hkv;
+  t.s = tg.nd + x / tg.Hkv;
+  t.row0 = cu_q[t.s];
+  t.d = cu_q[t.s + 1] - t.row0;
+  if (t.qb * tg.bmq >= t.d) return false;
+  t.c = ctx_lens[t.s] - t.d;
+  const int32_t rows = (t.qb + 1) * tg.bmq < t.d ? (t.qb + 1) * tg.bmq : t.d;
+  const int32_t total = (t.c + rows + kChunkKeys - 1) / kChunkKeys;   // stages up to the block's last key
+  const int32_t per = (total + tg.nsplit - 1) / tg.nsplit;
+  t.kt_lo = t.sp * per;
+  t.kt_hi = total < t.kt_lo + per ? total : t.kt_lo + per;
+  return true;
+}
+// Chunk workgroup cb of a launch runs tile (cb mod 8) per_xcd + cb / 8 (XCD-aware order).
+__host__ __device__ __forceinline__ int64_t chunk_wg_tile(int64_t cb, int64_t per_xcd) {
+  return (cb & 7) * per_xcd + (cb >> 3);
+}
+// Key stages of the chunk tile that shares a compute unit with decode workgroup b (0 if none).
+__host__ __device__ __forceinline__ int32_t beside_tile_stages(int32_t b, const TileGrid& tg, const int32_t* cu_q,
+                                                               const int32_t* ctx_lens) {
+  if (tg.n_tiles <= 0 || b >= 8 * tg.per_xcd) return 0;
+  const int64_t tile = chunk_wg_tile(b, tg.per_xcd);
+  TileSpan t;
+  if (tile >= tg.n_tiles || !chunk_tile_span(static_cast<int32_t>(tile), tg, cu_q, ctx_lens, t)) return 0;
+  return t.kt_hi > t.kt_lo ? t.kt_hi - t.kt_lo : 0;
+}
+// Rate of decode workgroup b (see above); ts = beside_tile_stages(b) when W = waves, else 0.
+__host__ __device__ __forceinline__ int32_t decode_wg_rate(int32_t b, int32_t F, int32_t ts, int32_t S, int32_t W) {
+  int64_t base = b < F ? 100 : CB_DECODE_RATE_SECOND;
+  if (b < F && ts > 0) {
+    const int64_t slow = static_cast<int64_t>(CB_DECODE_SHARE_SLOW) * CB_DECODE_SHARE_RATIO * ts * W / (100LL * S);
+    base -= slow < CB_DECODE_SHARE_SLOW ? slow : CB_DECODE_SHARE_SLOW;
+  }
+  return static_cast<int32_t>(base * ((b & 1) ? CB_DECODE_RATE_ODD_XCD : 100));
+}
+// start(w) from the workgroups' rate prefix P (P[b] = summed rates of workgroups [0, b)), four
+// waves per workgroup: C(w) = 4 P[w / 4] + (w mod 4) rate(w / 4).  P[b] <= 2048 x 10^4 and S <
+// 2^31, so S C(w) fits int64.
+__host__ __device__ __forceinline__ int64_t decode_rate_prefix(int32_t w, const int32_t* P) {
+  const int32_t b = w >> 2, r = w & 3;
+  return 4 * static_cast<int64_t>(P[b]) + (r ? static_cast<int64_t>(r) * (P[b + 1] - P[b]) : 0);
+}
+__host__ __device__ __forceinline__ int32_t decode_wave_start(int32_t w, int32_t S, int64_t cw, const int32_t* P) {
+  return static_cast<int32_t>(static_cast<int64_t>(S) * decode_rate_prefix(w, P) / cw);
 }
 __device__ __forceinline__ int32_t block_scan_1024(int32_t v, int32_t* scan) {
   const int tid = threadIdx.x;
@@ -438,9 +514,10 @@ __device__ __forceinline__ int32_t block_scan_1024(int32_t v, int32_t* scan) {
 
 constexpr int kPrepRows = 8192;   // decode rows whose stage offsets the prep workgroup keeps in LDS
 
-__global__ __launch_bounds__(1024) void decode_prep_kernel(AttnArgs a, int32_t n_waves, int32_t F) {
+__global__ __launch_bounds__(1024) void decode_prep_kernel(AttnArgs a, int32_t n_waves, int32_t F, TileGrid tg) {
   __shared__ int32_t scan[1024];
   __shared__ int32_t seq_lds[kPrepRows + 1];
+  __shared__ int32_t prefix[kMaxDecodeWaves / 4 + 1];   // P[b]: summed rates of workgroups [0, b)
   __shared__ int32_t carry;
   const int tid = threadIdx.x;
   // The searches below read the row offsets from LDS when they fit (one LDS round trip per
@@ -463,17 +540,34 @@ __global__ __launch_bounds__(1024) void decode_prep_kernel(AttnArgs a, int32_t n
   }
   const int32_t S = carry;
   const int32_t W = decode_waves_used(S, n_waves);
-  const int64_t cw = decode_rate_prefix(W, F);
+  const int32_t n_wg = (W + 3) >> 2;
+  __syncthreads();                                    // every thread has read carry
   if (tid == 0) {
     a.dec_seq[a.nd] = S;
     if (in_lds) seq_lds[a.nd] = S;
     a.dec_par[0] = S;
     a.dec_par[1] = F;
     a.dec_par[2] = W;
+    prefix[0] = 0;
+    carry = 0;
   }
-  __syncthreads();                                    // the row offsets are complete for the workgroup
-  for (int32_t w = tid; w < W; w += 1024) {
-    const int32_t pos = decode_wave_start(w, S, cw, F);
+  __syncthreads();
+  const bool full = W == n_waves;
+  for (int32_t base = 0; base < n_wg; base += 1024) {  // workgroup rates, scanned
+    const int32_t b = base + tid;
+    const int32_t ts = b < n_wg && full ? beside_tile_stages(b, tg, a.cu_q, a.ctx_lens) : 0;
+    const int32_t r = b < n_wg ? decode_wg_rate(b, F, ts, S, W) : 0;
+    const int32_t incl = block_scan_1024(r, scan);
+    if (b < n_wg) prefix[b + 1] = carry + incl;
+    __syncthreads();
+    if (tid == 1023) carry += scan[1023];
+    __syncthreads();
+  }
+  const int64_t cw = decode_rate_prefix(W, prefix);
+  for (int32_t w = tid; w <= W; w += 1024) {
+    const int32_t pos = w < W ? decode_wave_start(w, S, cw, prefix) : S;
+    a.dec_pos[w] = pos;
+    if (w == W) continue;
     int32_t lo = 0, hi = a.nd;                        // seq[lo] <= pos < seq[hi]
     while (hi - lo > 1) {
       const int32_t mid = (lo + hi) >> 1;
@@ -503,8 +597,8 @@ struct DecodeLds {
 
 template <typename T, int D>
 __device__ __forceinline__ void decode_wave(const AttnArgs& a, const int32_t* seq_start, const int32_t* wave_unit,
-                                            const int32_t* par, const int32_t* ctx_lens, const int32_t* cu_blocks,
-                                            int32_t w, int lane, char* lds) {
+                                            const int32_t* wave_pos, const int32_t* par, const int32_t* ctx_lens,
+                                            const int32_t* cu_blocks, int32_t w, int lane, char* lds) {
   constexpr int KS = D / 32;          // 32-slot contraction steps over the head dimension
   constexpr int DT = D / 16;          // 16-dim output tiles
   constexpr int ROW = D * sizeof(T);  // bytes per key row in LDS
@@ -515,11 +609,10 @@ __device__ __forceinline__ void decode_wave(const AttnArgs& a, const int32_t* se
   char* sV = lds + DecodeLds<T, D>::V;
   int32_t* sBlk = reinterpret_cast<int32_t*>(lds + DecodeLds<T, D>::BLK);
 
-  const int32_t S = par[0], F = par[1], W = par[2];   // uniform, read-only here: scalar loads
+  const int32_t W = par[2];             // uniform, read-only here: scalar loads
   if (w >= W) return;
-  const int64_t cw = decode_rate_prefix(W, F);
-  const int32_t pos_begin = decode_wave_start(w, S, cw, F);
-  const int32_t pos_end = decode_wave_start(w + 1, S, cw, F);
+  const int32_t pos_begin = wave_pos[w];
+  const int32_t pos_end = wave_pos[w + 1];
 
   const int32_t col = lane & 15;      // head owned by this lane in S^T / P^T / O^T
   const int32_t grp = lane >> 4;      // slot group
@@ -778,22 +871,11 @@ __device__ __forceinline__ void chunk_tile(const AttnArgs& a, int32_t tile, char
   char* sV = lds + ChunkLds<T, D>::V;
   int32_t* sBlk = reinterpret_cast<int32_t*>(lds + ChunkLds<T, D>::BLK);   // block-table window
 
-  int32_t t = tile;
-  const int32_t sp = t % a.nsplit; t /= a.nsplit;
-  const int32_t qb = t % a.q_blocks; t /= a.q_blocks;
-  const int32_t g = t % a.Hkv;
-  const int32_t s = a.nd + t / a.Hkv;
-
-  const int32_t row0 = a.cu_q[s];
-  const int32_t d = a.cu_q[s + 1] - row0;
-  if (qb * a.bmq >= d) return;
-  const int32_t ctx = a.ctx_lens[s];
-  const int32_t c = ctx - d;
+  TileSpan ts;
+  if (!chunk_tile_span(tile, TileGrid{a.nd, a.Hkv, a.q_blocks, a.nsplit, a.bmq, 0, 0}, a.cu_q, a.ctx_lens, ts)) return;
+  const int32_t sp = ts.sp, qb = ts.qb, g = ts.g, s = ts.s, row0 = ts.row0, d = ts.d, c = ts.c;
+  const int32_t kt_lo = ts.kt_lo, kt_hi = ts.kt_hi;
   const int32_t kv_end = c + min(d, (qb + 1) * a.bmq);        // past the block's last position
-  const int32_t tiles_total = (kv_end + kChunkKeys - 1) / kChunkKeys;
-  const int32_t tiles_per = (tiles_total + a.nsplit - 1) / a.nsplit;
-  const int32_t kt_lo = sp * tiles_per;
-  const int32_t kt_hi = min(tiles_total, kt_lo + tiles_per);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1056,20 +1138,21 @@ constexpr int attn_lds_bytes() {
 template <typename T, int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 2 : 1))) void attn_kernel(
     AttnArgs a, const int32_t* __restrict__ seq_start, const int32_t* __restrict__ wave_unit,
-    const int32_t* __restrict__ par, const int32_t* __restrict__ ctx_lens, const int32_t* __restrict__ cu_blocks,
-    int32_t n_dec_wg, int32_t n_tiles, int32_t per_xcd) {
+    const int32_t* __restrict__ wave_pos, const int32_t* __restrict__ par, const int32_t* __restrict__ ctx_lens,
+    const int32_t* __restrict__ cu_blocks, int32_t n_dec_wg, int32_t n_tiles, int32_t per_xcd) {
   __shared__ __attribute__((aligned(1024))) char lds[attn_lds_bytes<T, D>()];
   const int32_t b = blockIdx.x;
   if (b < n_dec_wg) {
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
-    decode_wave<T, D>(a, seq_start, wave_unit, par, ctx_lens, cu_blocks, 4 * b + wave,
+    decode_wave<T, D>(a, seq_start, wave_unit, wave_pos, par, ctx_lens, cu_blocks, 4 * b + wave,
                       static_cast<int>(threadIdx.x & 63), lds + wave * DecodeLds<T, D>::BYTES);
   } else {
     // XCD-aware order: workgroup b runs on XCD b % 8 (n_dec_wg is a multiple of 8); each XCD
     // gets a contiguous run of logical tiles, so the tiles sharing one (chunk, KV head) K/V
-    // stream share that XCD's L2.
+    // stream share that XCD's L2.  Chunk workgroup cb shares a compute unit with decode
+    // workgroup cb (the decode split accounts for it).
     const int32_t cb = b - n_dec_wg;
-    const int32_t tile = (cb & 7) * per_xcd + (cb >> 3);
+    const int32_t tile = static_cast<int32_t>(chunk_wg_tile(cb, per_xcd));
     if (tile < n_tiles) chunk_tile<T, D>(a, tile, lds);
   }
 }
@@ -1184,6 +1267,15 @@ int compute_units(hipStream_t st) {
 // multiple of 8 (whole rounds over the XCDs).
 int32_t first_round_wgs(hipStream_t st) { return (compute_units(st) + 7) / 8 * 8; }
 
+// The chunk tile grid of a launch: n_tiles tiles (numbered as chunk_tile_span reads them) on
+// 8 per_xcd chunk workgroups.
+TileGrid tile_grid(int32_t nd, int32_t Hkv, int32_t n_chunk, int32_t q_blocks, int32_t nsplit, int32_t bmq) {
+  TileGrid tg{nd, Hkv, q_blocks, nsplit, bmq, 0, 0};
+  tg.n_tiles = n_chunk > 0 ? static_cast<int64_t>(n_chunk) * q_blocks * Hkv * nsplit : 0;
+  tg.per_xcd = (tg.n_tiles + 7) / 8;
+  return tg;
+}
+
 int32_t decode_waves(hipStream_t st, bool has_chunks) {
   const int cus8 = first_round_wgs(st);
   return 4 * std::min(kMaxDecodeWaves / 4, (has_chunks ? CB_DECODE_WG_PER_CU_MIXED : CB_DECODE_WG_PER_CU) * cus8);
@@ -1197,23 +1289,23 @@ int launch_all(hipStream_t st, const AttnArgs& a, const Plan& p, void* const* ev
   auto rec = [&](int i) {
     if (events && events[i]) (void)hipEventRecord(static_cast<hipEvent_t>(events[i]), st);
   };
+  const TileGrid tg = tile_grid(a.nd, a.Hkv, a.n_chunk, a.q_blocks, a.nsplit, a.bmq);
+  const int64_t n_tiles = tg.n_tiles, per_xcd = tg.per_xcd;
   int32_t n_dec_wg = 0;
   if (a.nd > 0) {
     n_dec_wg = decode_waves(st, a.n_chunk > 0) / 4;
     if (!planned) {
-      decode_prep_kernel<<<dim3(1), dim3(1024), 0, st>>>(a, 4 * n_dec_wg, first_round_wgs(st));
+      decode_prep_kernel<<<dim3(1), dim3(1024), 0, st>>>(a, 4 * n_dec_wg, first_round_wgs(st), tg);
       if (hipGetLastError() != hipSuccess) return CB_ERR_HIP;
     }
   }
-  const int64_t n_tiles = a.n_chunk > 0 ? static_cast<int64_t>(a.n_chunk) * a.q_blocks * a.Hkv * a.nsplit : 0;
-  const int64_t per_xcd = (n_tiles + 7) / 8;
   const int64_t grid = n_dec_wg + per_xcd * 8;
   if (grid > 0x7fffffff) return CB_ERR_INVALID;
   if (grid > 0) {
     rec(0);
     rec(2);
     attn_kernel<T, D><<<dim3(static_cast<uint32_t>(grid)), dim3(256), 0, st>>>(
-        a, a.dec_seq, a.dec_wave, a.dec_par, a.ctx_lens, a.cu_blocks, n_dec_wg,
+        a, a.dec_seq, a.dec_wave, a.dec_pos, a.dec_par, a.ctx_lens, a.cu_blocks, n_dec_wg,
         static_cast<int32_t>(n_tiles), static_cast<int32_t>(per_xcd));
     if (hipGetLastError() != hipSuccess) return CB_ERR_HIP;
     rec(1);
@@ -1235,12 +1327,19 @@ int launch_all(hipStream_t st, const AttnArgs& a, const Plan& p, void* const* ev
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+size_t decode_plan_ints(int32_t nd, int32_t n_waves) {
+  return 4 + static_cast<size_t>(nd) + 1 + 2 * static_cast<size_t>(n_waves) + 1;
+}
+
 // Host version of decode_prep_kernel's split, with the same rule, so that a launch with the plan
-// computes bit for bit what it computes after the split kernel.  Layout of out: [0] S, [1] L,
-// [2] W, [3] n_waves, then the row stage offsets seq[0..nd] (seq[nd] = S), then W start units.
-int decode_plan_host(const int32_t* ctx, int32_t nd, int32_t ups, int32_t n_waves, int32_t F, int32_t* out,
-                     size_t cap) {
-  if (cap < static_cast<size_t>(4 + nd + 1)) return CB_ERR_CAPACITY;
+// computes bit for bit what it computes after the split kernel.  ctx: context lengths of all
+// rows (decode rows first); cu_q: query row offsets (read only for chunk tiles).  Layout of out:
+// [0] S, [1] F, [2] W, [3] n_waves; the row stage offsets seq[0..nd] (seq[nd] = S); n_waves slots
+// whose first W hold each wave's first unit; n_waves + 1 slots whose first W + 1 hold start(0..W).
+int decode_plan_host(const int32_t* cu_q, const int32_t* ctx, int32_t nd, int32_t ups, int32_t n_waves,
+                     int32_t F, const TileGrid& tg, int32_t* out, size_t cap) {
+  if (n_waves < 1 || n_waves > kMaxDecodeWaves) return CB_ERR_INVALID;
+  if (cap < decode_plan_ints(nd, n_waves)) return CB_ERR_CAPACITY;
   int32_t* seq = out + 4;
   int64_t S = 0;
   for (int32_t s = 0; s < nd; ++s) {
@@ -1251,20 +1350,30 @@ int decode_plan_host(const int32_t* ctx, int32_t nd, int32_t ups, int32_t n_wave
   }
   seq[nd] = static_cast<int32_t>(S);
   const int32_t W = decode_waves_used(static_cast<int32_t>(S), n_waves);
-  const int64_t cw = decode_rate_prefix(W, F);
-  if (cap < static_cast<size_t>(4 + nd + 1 + W)) return CB_ERR_CAPACITY;
+  const int32_t n_wg = (W + 3) >> 2;
+  int32_t P[kMaxDecodeWaves / 4 + 1];
+  P[0] = 0;
+  const bool full = W == n_waves;
+  for (int32_t b = 0; b < n_wg; ++b) {
+    const int32_t ts = full ? beside_tile_stages(b, tg, cu_q, ctx) : 0;
+    P[b + 1] = P[b] + decode_wg_rate(b, F, ts, static_cast<int32_t>(S), W);
+  }
+  const int64_t cw = decode_rate_prefix(W, P);
   out[0] = static_cast<int32_t>(S);
   out[1] = F;
   out[2] = W;
   out[3] = n_waves;
   int32_t* wave = seq + nd + 1;
+  int32_t* pos = wave + n_waves;
   int32_t lo = 0;
   for (int32_t w = 0; w < W; ++w) {                 // wave starts grow: walk the rows once
-    const int32_t pos = decode_wave_start(w, static_cast<int32_t>(S), cw, F);
-    while (seq[lo + 1] <= pos) ++lo;                // seq[lo] <= pos < seq[lo + 1]
+    const int32_t p = decode_wave_start(w, static_cast<int32_t>(S), cw, P);
+    pos[w] = p;
+    while (seq[lo + 1] <= p) ++lo;                  // seq[lo] <= p < seq[lo + 1]
     const int32_t n_s = (seq[lo + 1] - seq[lo]) / ups;
-    wave[w] = lo * ups + (pos - seq[lo]) / n_s;
+    wave[w] = lo * ups + (p - seq[lo]) / n_s;
   }
+  pos[W] = static_cast<int32_t>(S);
   return CB_OK;
 }
 
@@ -1300,16 +1409,24 @@ extern "C" int32_t cb_attn_decode_waves(void* stream, int32_t has_chunks) {
 
 extern "C" size_t cb_decode_plan_ints(int32_t num_decodes, int32_t n_waves) {
   if (num_decodes < 0 || n_waves < 1) return 0;
-  return 4 + static_cast<size_t>(num_decodes) + 1 + static_cast<size_t>(n_waves);
+  return cb::decode_plan_ints(num_decodes, n_waves);
 }
 
-extern "C" int cb_decode_plan(void* stream, int32_t has_chunks, const int32_t* context_lens,
-                              int32_t num_decodes, int32_t Hq, int32_t Hkv, int32_t* out, size_t cap_ints) {
-  if (num_decodes < 1 || !context_lens || !out || Hq < 1 || Hkv < 1 || Hq % Hkv) return CB_ERR_INVALID;
+extern "C" int cb_decode_plan(void* stream, int32_t num_seqs, int32_t num_decodes, int32_t max_q_len,
+                              int32_t max_ctx, int32_t Hq, int32_t Hkv, const int32_t* cu_seqlens_q,
+                              const int32_t* context_lens, int32_t* out, size_t cap_ints) {
+  using namespace cb;
+  if (num_decodes < 1 || num_seqs < num_decodes || !context_lens || !out) return CB_ERR_INVALID;
+  if (Hq < 1 || Hkv < 1 || Hq % Hkv || Hq / Hkv > kChunkRows) return CB_ERR_INVALID;
+  const bool chunks = num_seqs > num_decodes;
+  if (chunks && (!cu_seqlens_q || max_q_len < 1 || max_ctx < 1)) return CB_ERR_INVALID;
   const hipStream_t st = static_cast<hipStream_t>(stream);
-  const int32_t ups = Hkv * ((Hq / Hkv + 15) / 16);
-  return cb::decode_plan_host(context_lens, num_decodes, ups, cb::decode_waves(st, has_chunks != 0),
-                              cb::first_round_wgs(st), out, cap_ints);
+  // The same chunk tiling as the attention call with these shape arguments (the token count and
+  // head size only size its workspace).
+  const Plan p = make_plan(num_seqs, num_decodes, num_seqs, max_q_len, max_ctx, Hq, Hkv, 64);
+  const TileGrid tg = tile_grid(num_decodes, Hkv, p.n_chunk, p.q_blocks, p.nsplit, p.bmq);
+  return decode_plan_host(cu_seqlens_q, context_lens, num_decodes, p.ups, decode_waves(st, chunks),
+                          first_round_wgs(st), tg, out, cap_ints);
 }
 
 extern "C" int cb_mixed_paged_attention_timed(
@@ -1347,6 +1464,7 @@ extern "C" int cb_mixed_paged_attention_timed(
   a.chk_ml = reinterpret_cast<float*>(ws + p.chk_ml);
   a.dec_seq = reinterpret_cast<int32_t*>(ws + p.dec_seq);
   a.dec_wave = reinterpret_cast<int32_t*>(ws + p.dec_wave);
+  a.dec_pos = reinterpret_cast<int32_t*>(ws + p.dec_pos);
   a.dec_par = reinterpret_cast<int32_t*>(ws + p.dec_par);
   a.dec_unit = reinterpret_cast<int32_t*>(ws + p.dec_unit);
   a.num_seqs = num_seqs; a.nd = num_decodes; a.T = T; a.Hq = Hq; a.Hkv = Hkv; a.G = p.G;
@@ -1364,6 +1482,7 @@ extern "C" int cb_mixed_paged_attention_timed(
     a.dec_par = plan;
     a.dec_seq = plan + 4;
     a.dec_wave = plan + 4 + num_decodes + 1;
+    a.dec_pos = a.dec_wave + plan_waves;
   }
   if (dtype == CB_BF16) {
     return D == 128 ? launch_all<bf16_t, 128>(st, a, p, events, planned)

@@ -63,9 +63,10 @@ class MixedStepRunner:
         meta.plan_waves = 0
         nd = meta.num_decodes
         if nd > 0:
-            meta.plan_waves = cb.cb_decode_plan(meta.host["context_lens"][:nd], self.Hq, self.Hkv,
-                                                self.bufs[i].arrays["decode_plan"], self.device,
-                                                has_chunks=meta.num_seqs > nd)
+            S = meta.num_seqs
+            meta.plan_waves = cb.cb_decode_plan(meta.host["cu_seqlens_q"][:S + 1], meta.host["context_lens"][:S],
+                                                nd, meta.max_q_len, meta.max_context_len, self.Hq, self.Hkv,
+                                                self.bufs[i].arrays["decode_plan"], self.device)
         return meta
 
     def upload(self, meta: cb.StepMeta) -> dict:

@@ -277,22 +277,27 @@ int cb_mixed_paged_attention(void* stream, int32_t dtype, int32_t num_seqs, int3
  * kernel).  Decode rows stream their keys as 32-key stages of (row, KV head, 16-head group)
  * units; all units' stages, in order, form one line of S stages, cut into W contiguous ranges,
  * one per decode wave with work.  Each wave's share is proportional to the measured streaming rate
- * of its workgroup (the first or second workgroup on its compute unit, even or odd XCD), so the
- * waves end together.  cb_attn_decode_waves is the number of decode waves an attention call on
- * this stream's device launches (has_chunks: whether the step has chunk rows); cb_decode_plan_ints
- * the int32 capacity a plan needs; cb_decode_plan writes the plan for a call on the same stream's
- * device with the same has_chunks, for the step's num_decodes >= 1 decode context lengths (host
- * memory, the values cb_build_step emitted), into out (host memory): [S, F (workgroups dispatched
- * first onto their compute units), W, n_waves, stage offset of each row (num_decodes + 1), first
- * unit of each of the W waves with work].  It makes no device call beyond reading the device's
- * compute unit count once.  The device copy (16-byte aligned) is passed to the call below with its
- * n_waves (out[3]), which must equal the call's own decode wave count (else CB_ERR_INVALID).  The
- * result is bit for bit the same as with the split kernel.  CB_ERR_CAPACITY if cap_ints is too
- * small, CB_ERR_INVALID on bad arguments. */
+ * of its workgroup (the first or second workgroup on its compute unit, even or odd XCD, and, beside
+ * chunk rows, how long the chunk tile on the same compute unit runs), so the waves end together.
+ * cb_attn_decode_waves is the number of decode waves an attention call on this stream's device
+ * launches (has_chunks: whether the step has chunk rows); cb_decode_plan_ints the int32 capacity a
+ * plan needs; cb_decode_plan writes the plan for a call on the same stream's device with the same
+ * num_seqs, num_decodes >= 1, max_q_len, max_ctx, Hq and Hkv, from the step's host metadata (the
+ * values cb_build_step emitted): context_lens of all num_seqs rows, decode rows first, and
+ * cu_seqlens_q (num_seqs + 1 offsets; read only when num_seqs > num_decodes, may be NULL
+ * otherwise).  out (host memory) receives [S, F (workgroups dispatched first onto their compute
+ * units), W, n_waves], the stage offset of each decode row (num_decodes + 1), n_waves slots whose
+ * first W hold the first unit of each wave with work, and n_waves + 1 slots whose first W + 1 hold
+ * each wave's first stage and then S.  It makes no device call beyond reading the device's compute
+ * unit count once.  The device copy (16-byte aligned) is passed to the call below with its n_waves
+ * (out[3]), which must equal the call's own decode wave count (else CB_ERR_INVALID).  The result is
+ * bit for bit the same as with the split kernel.  CB_ERR_CAPACITY if cap_ints is too small,
+ * CB_ERR_INVALID on bad arguments. */
 int32_t cb_attn_decode_waves(void* stream, int32_t has_chunks);
 size_t cb_decode_plan_ints(int32_t num_decodes, int32_t n_waves);
-int cb_decode_plan(void* stream, int32_t has_chunks, const int32_t* context_lens, int32_t num_decodes,
-                   int32_t Hq, int32_t Hkv, int32_t* out, size_t cap_ints);
+int cb_decode_plan(void* stream, int32_t num_seqs, int32_t num_decodes, int32_t max_q_len, int32_t max_ctx,
+                   int32_t Hq, int32_t Hkv, const int32_t* cu_seqlens_q, const int32_t* context_lens,
+                   int32_t* out, size_t cap_ints);
 
 /* The same operation, optionally with a host-made decode plan (decode_plan: device copy of
  * cb_decode_plan's output, plan_waves its n_waves; NULL = split on the device), recording

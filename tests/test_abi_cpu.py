@@ -259,12 +259,12 @@ def test_workspace_grows_with_context_and_rows():
     assert 0 < a < b
     # Decode partials: one slot per (unit, wave) pair, at most units + 8192 waves slots of
     # min(16, G) heads x (D + 2) floats, whatever the context length; plus the row stage offsets,
-    # the per-wave start units and four parameters (each region 256-byte aligned).
+    # the per-wave start units and start stages and four parameters (each region 256-byte aligned).
     one_row = f(1, 1, 1, 1, 300000, 300000, 8, 8, 128)
     assert one_row == f(1, 1, 1, 1, 3000, 3000, 8, 8, 128)
-    assert one_row <= (8 + 8192) * 1 * 130 * 4 + 2 * 4 + 8192 * 4 + 16 + 5 * 256
+    assert one_row <= (8 + 8192) * 1 * 130 * 4 + 2 * 4 + 8192 * 4 + 8193 * 4 + 16 + 6 * 256
     gqa = f(4, 4, 4, 1, 5000, 5000, 56, 8, 128)        # group of 7 heads per unit
-    assert gqa <= (4 * 8 + 8192) * 7 * 130 * 4 + 5 * 4 + 8192 * 4 + 16 + 5 * 256
+    assert gqa <= (4 * 8 + 8192) * 7 * 130 * 4 + 5 * 4 + 8192 * 4 + 8193 * 4 + 16 + 6 * 256
     assert f(0, 0, 0, 0, 0, 0, 32, 32, 128) == 0
 
 
@@ -281,54 +281,110 @@ def test_linear_workspace_depends_on_the_shape_only():
         assert f(*bad) == 0
 
 
-def _expected_decode_plan(ctx, Hq, Hkv, n_waves, F=256):
+def _expected_decode_plan(ctx, cu_q, nd, Hq, Hkv, n_waves, max_q_len, max_ctx, F=256):
     # The decode rows' stage line: units (row, KV head, 16-head group) of ceil(ctx / 32) stages
     # each; W = min(n_waves, S // 8) (at least one) contiguous ranges, wave w's share proportional to
-    # the rate of its workgroup w // 4 (percent: 100 on even XCDs, 88 on odd ones, workgroup b on
-    # XCD b mod 8; the same for the workgroups [F, 2F) dispatched second onto their compute unit);
+    # the rate of its workgroup w // 4 (percent products: 100 on even XCDs, 88 on odd ones, workgroup
+    # b on XCD b mod 8; the same for the workgroups [F, 2F) dispatched second onto their compute unit).
+    # Beside chunk rows, decode workgroup b < F shares its compute unit with chunk workgroup b, which
+    # runs tile (b mod 8) * per_xcd + b // 8; when every wave has work (W = n_waves) its 100 drops by
+    # min(30, 30 * 75 * stages * W // (100 S)) where stages are that tile's key stages.
     # start(w) = floor(S C(w) / C(W)); then each wave's first unit.
-    ups = Hkv * ((Hq // Hkv + 15) // 16)
-    stages = [(int(c) + 31) // 32 * ups for c in ctx]
+    G = Hq // Hkv
+    ups = Hkv * ((G + 15) // 16)
+    stages = [(int(c) + 31) // 32 * ups for c in ctx[:nd]]
     S = sum(stages)
     W = 0 if S == 0 else min(n_waves, max(1, S // 8))
-    rate = lambda b: (100 if b < F else 100) * (88 if b & 1 else 100)
+    # chunk tiling of the attention call: 128 // G rows per tile; the keys split (by 2, up to 8)
+    # while a mixed launch has fewer than 128 tiles and each split keeps >= 2 x 32 keys
+    n_chunk = len(ctx) - nd
+    bmq = 128 // G
+    q_blocks = -(-max(max_q_len, 1) // bmq) if n_chunk else 0
+    nsplit = 1
+    while n_chunk and nsplit < 8 and n_chunk * q_blocks * Hkv * nsplit < 128 and max_ctx // (2 * nsplit) >= 64:
+        nsplit *= 2
+    tiles = n_chunk * q_blocks * Hkv * nsplit
+    per_xcd = -(-tiles // 8)
+
+    def tile_stages(b):
+        if tiles == 0 or b >= 8 * per_xcd:
+            return 0
+        tile = (b % 8) * per_xcd + b // 8
+        if tile >= tiles:
+            return 0
+        sp, x = tile % nsplit, tile // nsplit
+        qb, x = x % q_blocks, x // q_blocks
+        s = nd + x // Hkv
+        d = cu_q[s + 1] - cu_q[s]
+        if qb * bmq >= d:
+            return 0
+        total = -(-(ctx[s] - d + min(d, (qb + 1) * bmq)) // 32)
+        per = -(-total // nsplit)
+        return max(0, min(total, sp * per + per) - sp * per)
+
+    def rate(b):
+        base = 100
+        if b < F and W == n_waves and tile_stages(b) > 0:
+            base -= min(30, 30 * 75 * tile_stages(b) * W // (100 * S))
+        return base * (88 if b & 1 else 100)
     C = [0]
     for v in range(W):
         C.append(C[-1] + rate(v // 4))
     start = [S * C[w] // C[W] for w in range(W + 1)]
-    seq = [sum(stages[:i]) for i in range(len(ctx) + 1)]
+    seq = [sum(stages[:i]) for i in range(nd + 1)]
     first = []
     for w in range(W):
         pos = start[w]
-        r = max(i for i in range(len(ctx)) if seq[i] <= pos and stages[i] > 0)
+        r = max(i for i in range(nd) if seq[i] <= pos and stages[i] > 0)
         first.append(r * ups + (pos - seq[r]) // (stages[r] // ups))
-    return [S, F, W, n_waves] + seq + first, start
+    return [S, F, W, n_waves] + seq, first, start
 
 
 def test_decode_plan_layout_and_rule():
     import torch
-    cases = [
-        (torch.tensor([100, 1, 4096, 33, 0, 700], dtype=torch.int32), 56, 8, True),   # GQA-7: one unit per KV head
-        (torch.tensor([4096 - 37 * i for i in range(64)], dtype=torch.int32), 32, 32, False),  # both dispatch rounds
-        (torch.tensor([5, 0], dtype=torch.int32), 32, 8, True),                        # S < 8: one wave
+    nd2 = 64
+    ctx2 = [4096 - 37 * i for i in range(nd2)] + [3584 + 448]           # budget-512-like: one chunk
+    cu2 = list(range(nd2 + 1)) + [nd2 + 448]
+    ctx3 = [100, 1, 4096, 33, 0, 700] + [1064, 40]                      # GQA-7, two chunks: key splits
+    cu3 = list(range(7)) + [6 + 64, 6 + 64 + 40]
+    cases = [   # context lens, cu_seqlens_q, decodes, Hq, Hkv, max_q_len, max_ctx
+        ([100, 1, 4096, 33, 0, 700], None, 6, 56, 8, 1, 4096),         # GQA-7: one unit per KV head
+        ([4096 - 37 * i for i in range(64)], None, 64, 32, 32, 1, 4096),  # both dispatch rounds
+        ([5, 0], None, 2, 32, 8, 1, 5),                                  # S < 8: one wave
+        (ctx2, cu2, nd2, 32, 32, 448, 4096),                             # decode beside 128 tiles
+        (ctx3, cu3, 6, 56, 8, 64, 4096),
+        ([5, 0, 300], [0, 1, 2, 302], 2, 32, 8, 300, 300),             # one wave beside tiles
     ]
-    for ctx, Hq, Hkv, chunks in cases:
+    for ctx, cu, nd, Hq, Hkv, mq, mc in cases:
+        chunks = len(ctx) > nd
         waves = cb.cb_attn_decode_waves(None, chunks)
         assert waves == (1024 if chunks else 2048)        # MI355X: 256 compute units, 1 or 2 workgroups each
-        n = cb.cb_decode_plan_ints(len(ctx), waves)
+        n = cb.cb_decode_plan_ints(nd, waves)
+        assert n == 4 + nd + 1 + 2 * waves + 1
         out = torch.full((n,), -7, dtype=torch.int32)
-        assert cb.cb_decode_plan(ctx, Hq, Hkv, out, None, has_chunks=chunks) == waves
-        want, start = _expected_decode_plan(ctx.tolist(), Hq, Hkv, waves)
-        assert out[:len(want)].tolist() == want
-        W = want[2]
+        cu_t = torch.tensor(cu, dtype=torch.int32) if cu is not None else None
+        got = cb.cb_decode_plan(cu_t, torch.tensor(ctx, dtype=torch.int32), nd, mq, mc, Hq, Hkv, out, None)
+        assert got == waves
+        head, first, start = _expected_decode_plan(ctx, cu, nd, Hq, Hkv, waves, mq, mc)
+        W = head[2]
+        o = out.tolist()
+        assert o[:len(head)] == head
+        assert o[len(head):len(head) + W] == first
+        assert o[len(head) + waves:len(head) + waves + W + 1] == start
         assert all(start[w + 1] > start[w] for w in range(W))           # every wave has work
         if W >= 8:                                       # workgroup 0 (even XCD) takes more than 1 (odd)
             assert start[4] - start[0] > start[8] - start[4]
-    ctx, Hq, Hkv, waves = cases[0][0], 56, 8, 1024
+        if chunks and W == waves:                        # a workgroup beside a long tile takes less
+            share = [start[4 * b + 4] - start[4 * b] for b in range(W // 4)]
+            assert share[2] < share[2 + 128] or share[0] < share[128]
+    ctx, Hq, Hkv, waves = torch.tensor(cases[0][0], dtype=torch.int32), 56, 8, 2048
     small = torch.zeros(5, dtype=torch.int32)
     with pytest.raises(cb.CbError) as e:
-        cb.cb_decode_plan(ctx, Hq, Hkv, small, None)
+        cb.cb_decode_plan(None, ctx, 6, 1, 4096, Hq, Hkv, small, None)
     assert e.value.status == cb.CB_ERR_CAPACITY
     with pytest.raises(cb.CbError) as e:
-        cb.cb_decode_plan(ctx, 10, 4, torch.zeros(64, dtype=torch.int32), None)   # Hq not a multiple of Hkv
+        cb.cb_decode_plan(None, ctx, 6, 1, 4096, 10, 4, torch.zeros(8192, dtype=torch.int32), None)   # Hq % Hkv
+    assert e.value.status == cb.CB_ERR_INVALID
+    with pytest.raises(cb.CbError) as e:                  # chunk rows need cu_seqlens_q
+        cb.cb_decode_plan(None, ctx, 4, 2, 4096, Hq, Hkv, torch.zeros(8192, dtype=torch.int32), None)
     assert e.value.status == cb.CB_ERR_INVALID
