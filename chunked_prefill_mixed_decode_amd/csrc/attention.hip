@@ -438,8 +438,10 @@ __host__ __device__ __forceinline__ int32_t decode_waves_used(int32_t S, int32_t
   return k < 1 ? 1 : (k > n_waves ? n_waves : k);
 }
 
-// Chunk tiles are numbered with the key split fastest, then the query block, the KV head and
-// the chunk.  The tile's chunk s, KV head g, query block qb, split sp, the chunk's first row and
+// Chunk tiles are numbered with the key split fastest, then the query block (last block first:
+// under the causal mask later blocks see more keys, so a launch hands out the longest tiles of a
+// chunk first and the short ones fill in behind them), the KV head and the chunk.  The tile's
+// chunk s, KV head g, query block qb, split sp, the chunk's first row and
 // length d, its cached prefix c, and the split's key stages [kt_lo, kt_hi).  False when the query
 // block lies past the chunk's end (the tile has no rows).
 struct TileSpan {
@@ -453,7 +455,7 @@ __host__ __device__ __forceinline__ bool chunk_tile_span(int32_t tile, const Til
                                                          const int32_t* ctx_lens, TileSpan& t) {
   int32_t x = tile;
   t.sp = x % tg.nsplit; x /= tg.nsplit;
-  t.qb = x % tg.q_blocks; x /= tg.q_blocks;
+  t.qb = tg.q_blocks - 1 - x % tg.q_blocks; x /= tg.q_blocks;
   t.g = x % tg.Hkv;
   t.s = tg.nd + x / tg.Hkv;
   t.row0 = cu_q[t.s];

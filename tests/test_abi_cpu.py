@@ -313,7 +313,7 @@ def _expected_decode_plan(ctx, cu_q, nd, Hq, Hkv, n_waves, max_q_len, max_ctx, F
         if tile >= tiles:
             return 0
         sp, x = tile % nsplit, tile // nsplit
-        qb, x = x % q_blocks, x // q_blocks
+        qb, x = q_blocks - 1 - x % q_blocks, x // q_blocks   # last query block first
         s = nd + x // Hkv
         d = cu_q[s + 1] - cu_q[s]
         if qb * bmq >= d:
