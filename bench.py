@@ -441,6 +441,62 @@ def main():
                      "note": "the same steps replayed from one HIP graph per step of the cycle"}
         state["sched"], state["k"] = cb.cb_sched_clone(snapshot), 0
 
+        # Padded token buckets: launch shapes rounded up (runner.Buckets), one graph per padded
+        # shape, row buffers of the padded length per graph.  Timing only: a shape's buffers keep
+        # the inputs of the first step that used it.
+        from chunked_prefill_mixed_decode_amd.runner import Buckets
+        bk = Buckets(tokens=64, context=4096)
+        bgraphs, rows = StepGraphs(g.runner), {}
+        bmetas = []
+        for k in range(cb_steps):
+            bmetas.append(g.runner.build(state["sched"], w.budget, buckets=bk))
+        g.runner.ensure_workspace(max(g.runner.workspace_bytes(m) for m in bmetas))
+        state["sched"], state["k"] = cb.cb_sched_clone(snapshot), 0
+        pad = {"rows": 0, "real": 0}
+
+        def bucket_step(count=False):
+            k = state["k"]
+            meta = g.runner.build(state["sched"], w.budget, buckets=bk)
+            key = StepGraphs.key(meta)
+            if key not in rows:
+                T, Tp = meta.num_tokens, meta.launch_tokens
+                src = inputs[k]
+                rows[key] = [torch.cat([x, x.new_zeros((Tp - T,) + x.shape[1:])]) for x in src]
+                rows[key] += [torch.empty_like(rows[key][0]), torch.empty_like(rows[key][0])]
+            q, kk, vv, q_rot, out = rows[key]
+
+            def launch(dev_meta):
+                g.runner.append(dev_meta, q, kk, vv, q_rot)
+                g.runner.attend(meta, dev_meta, q_rot, out)
+            mode = bgraphs.step(meta, launch)
+            if count:
+                pad["rows"] += meta.launch_tokens
+                pad["real"] += meta.num_tokens
+            state["k"] = k + 1
+            if state["k"] == cb_steps:
+                state["k"] = 0
+                state["sched"] = cb.cb_sched_clone(snapshot)
+            return meta.num_tokens, mode
+        for _ in range(2 * cb_steps):
+            bucket_step()
+        torch.cuda.synchronize()
+        btok, bmodes = 0, set()
+        t1 = time.perf_counter()
+        for _ in range(args.steps):
+            n, mode = bucket_step(count=True)
+            btok += n
+            bmodes.add(mode)
+        torch.cuda.synchronize()
+        bel = time.perf_counter() - t1
+        graph_rep["bucketed"] = {
+            "value": btok / bel, "unit": "tokens/s", "ms_per_step": bel / args.steps * 1e3,
+            "graphs": len(bgraphs.graphs), "all_replayed": bmodes == {"replay"},
+            "token_bucket": bk.tokens, "context_bucket": bk.context,
+            "padded_rows_frac": pad["rows"] / pad["real"] - 1.0,
+            "note": "one HIP graph per padded launch shape (token count to a multiple of 64, "
+                    "longest query likewise, longest contexts to a multiple of 4096)"}
+        state["sched"], state["k"] = cb.cb_sched_clone(snapshot), 0
+
     # End-to-end latency: host wall time from cb_build_step to stream sync after attention.
     e2e = []
     for _ in range(min(args.steps, 3 * cb_steps)):

@@ -265,6 +265,7 @@ def cb_build_step(s: Sched, token_budget: int, buf: StepBuffers) -> StepMeta:
     scal = {k: getattr(st, k) for k in STEP_SCALARS}
     meta = StepMeta(**scal, host={})
     meta.host = {k: buf.arrays[k][:n] for k, n in meta.lengths().items()}
+    meta.launch_tokens = meta.num_tokens            # rows the step's launches cover (padding: more)
     return meta
 
 

@@ -22,6 +22,28 @@ from . import binding as cb
 SENTINEL_BITS = {torch.bfloat16: -1, torch.float32: -1}   # all-ones: a NaN that no write produces
 
 
+def round_up(x: int, step: int) -> int:
+    return -(-x // step) * step if step > 0 else x
+
+
+class Buckets:
+    """Padded launch shapes, so that steps whose exact shapes differ share one captured graph.
+
+    A step's launches take its token count and its longest query and contexts by value; rounding
+    them up gives a handful of keys instead of one per step.  The token count rounds up to a
+    multiple of ``tokens`` (at most the buffers' capacity): the padding rows get position and slot
+    -1, which the rotary/append kernel skips, and their attention output is left undefined.  The
+    longest query rounds up to a multiple of ``tokens`` too (it sizes the chunk tiles' query
+    blocks) and the longest contexts to a multiple of ``context`` (they size the grids and the
+    workspace); the kernels read each row's own lengths from the metadata, so larger bounds only
+    add tiles that exit at once and may choose other key splits.  The sequence and decode counts
+    stay exact: padding them would need dummy rows inside the metadata.
+    """
+
+    def __init__(self, tokens: int = 64, context: int = 4096):
+        self.tokens, self.context = tokens, context
+
+
 class MixedStepRunner:
     def __init__(self, *, Hq: int, Hkv: int, D: int, block_size: int, num_blocks: int,
                  dtype: torch.dtype, device, max_pos: int, cap_seqs: int, cap_tokens: int,
@@ -52,8 +74,10 @@ class MixedStepRunner:
         self.workspace = torch.empty(0, dtype=torch.uint8, device=self.device)
 
     # ---- host builder + metadata copy ----------------------------------------------------------
-    def build(self, sched: cb.Sched, budget: int) -> cb.StepMeta:
-        """cb_build_step into the next pinned buffer (after its previous copy has finished)."""
+    def build(self, sched: cb.Sched, budget: int, buckets: Buckets | None = None) -> cb.StepMeta:
+        """cb_build_step into the next pinned buffer (after its previous copy has finished).  With
+        ``buckets`` the launch shape is padded (``meta.launch_tokens`` rows and rounded-up maxima;
+        see ``Buckets``) before the decode split is planned for it."""
         i = self.ring
         self.ring ^= 1
         if self.copied[i] is not None:
@@ -61,6 +85,9 @@ class MixedStepRunner:
         meta = cb.cb_build_step(sched, budget, self.bufs[i])
         meta.buf_index = i
         meta.plan_waves = 0
+        meta.launch_tokens = meta.num_tokens
+        if buckets is not None:
+            self._pad(meta, buckets)
         nd = meta.num_decodes
         if nd > 0:
             S = meta.num_seqs
@@ -68,6 +95,19 @@ class MixedStepRunner:
                                                 nd, meta.max_q_len, meta.max_context_len, self.Hq, self.Hkv,
                                                 self.bufs[i].arrays["decode_plan"], self.device)
         return meta
+
+    def _pad(self, meta: cb.StepMeta, b: Buckets):
+        T = meta.num_tokens
+        cap = self.bufs[meta.buf_index].cap[1]
+        Tp = min(cap, round_up(T, b.tokens))
+        arrays = self.bufs[meta.buf_index].arrays
+        arrays["positions"][T:Tp] = -1              # padding rows: skipped by the append
+        arrays["slot_mapping"][T:Tp] = -1
+        meta.launch_tokens = Tp
+        meta.exact_max = (meta.max_q_len, meta.max_context_len, meta.max_decode_context_len)
+        meta.max_q_len = min(round_up(meta.max_q_len, b.tokens), Tp)
+        meta.max_context_len = round_up(meta.max_context_len, b.context)
+        meta.max_decode_context_len = round_up(meta.max_decode_context_len, b.context)
 
     def upload(self, meta: cb.StepMeta) -> dict:
         """cb_copy_host_to_device of the step's metadata on the current stream (a kernel, so the
@@ -106,7 +146,7 @@ class MixedStepRunner:
             self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
 
     def workspace_bytes(self, meta: cb.StepMeta) -> int:
-        return cb.cb_attn_workspace_bytes(meta.num_seqs, meta.num_decodes, meta.num_tokens,
+        return cb.cb_attn_workspace_bytes(meta.num_seqs, meta.num_decodes, meta.launch_tokens,
                                           meta.max_q_len, meta.max_decode_context_len,
                                           meta.max_context_len, self.Hq, self.Hkv, self.D)
 
@@ -145,7 +185,7 @@ class StepGraphs:
 
     @staticmethod
     def key(meta: cb.StepMeta) -> tuple:
-        return (meta.buf_index, meta.num_seqs, meta.num_decodes, meta.num_tokens, meta.max_q_len,
+        return (meta.buf_index, meta.num_seqs, meta.num_decodes, meta.launch_tokens, meta.max_q_len,
                 meta.max_context_len, meta.max_decode_context_len)
 
     def step(self, meta: cb.StepMeta, launch) -> str:

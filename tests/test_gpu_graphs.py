@@ -21,6 +21,17 @@ def dev():
     return torch.device("cuda:0")
 
 
+def _cycle_len(g, snap) -> int:
+    """Steps until the prompts are done (or the workload's step count), at most 40."""
+    w, cb = g.w, g.cb
+    probe, n = cb.cb_sched_clone(snap), 0
+    buf = cb.StepBuffers(*g.runner.bufs[0].cap)
+    while (w.steps is None and cb.cb_sched_pending_prompts(probe) > 0 or w.steps is not None and n < w.steps) and n < 40:
+        cb.cb_build_step(probe, w.budget, buf)
+        n += 1
+    return n
+
+
 @pytest.mark.parametrize("i", [2, 4])
 def test_graph_replay_equals_eager(dev, i):
     from chunked_prefill_mixed_decode_amd.runner import StepGraphs
@@ -28,12 +39,7 @@ def test_graph_replay_equals_eager(dev, i):
     g = DeviceRun(w, dev)
     cb = g.cb
     snap = cb.cb_sched_clone(g.sched)
-    # Cycle length: steps until the prompts are done, bounded.
-    probe, n = cb.cb_sched_clone(snap), 0
-    buf = cb.StepBuffers(*g.runner.bufs[0].cap)
-    while (w.steps is None and cb.cb_sched_pending_prompts(probe) > 0 or w.steps is not None and n < w.steps) and n < 40:
-        cb.cb_build_step(probe, w.budget, buf)
-        n += 1
+    n = _cycle_len(g, snap)
     # Eager reference: inputs and outputs per step (fixed addresses, reused by the graphs).
     metas, inputs, qrots, outs = [], [], [], []
     g.sched = cb.cb_sched_clone(snap)
@@ -67,5 +73,83 @@ def test_graph_replay_equals_eager(dev, i):
             assert torch.equal(got_o[k].view(torch.int16), outs[k].view(torch.int16)), (cycle, k)
             assert torch.equal(got_q[k].view(torch.int16), qrots[k].view(torch.int16)), (cycle, k)
     assert "replay" in modes and modes.count("captured") == len(graphs.graphs)
+    assert torch.equal(g.runner.k_cache.view(torch.int16), kc.view(torch.int16))
+    assert torch.equal(g.runner.v_cache.view(torch.int16), vc.view(torch.int16))
+
+
+@pytest.mark.parametrize("i", [2, 4])
+def test_bucketed_graph_replay(dev, i):
+    # Padded launch shapes (runner.Buckets): steps that round to the same shape share one graph
+    # (and one set of row buffers of the padded length).  Rows [0, T) of every replay equal an
+    # eager run of the same padded launch bit for bit, and the unpadded eager step within the
+    # output tolerance (a larger context bound may choose other key splits); the padding rows
+    # append nothing, so the cache ends bit-identical to the unpadded run's.
+    from chunked_prefill_mixed_decode_amd.runner import Buckets, StepGraphs
+    w = workloads.small(i)
+    g = DeviceRun(w, dev)
+    cb = g.cb
+    snap = cb.cb_sched_clone(g.sched)
+    n = _cycle_len(g, snap)
+    ref, inputs, exact = [], [], set()
+    for k in range(n):
+        meta, out, _ = g.step()
+        torch.cuda.synchronize()
+        inputs.append(g.step_inputs(meta))
+        ref.append(out.clone())
+        exact.add(StepGraphs.key(meta)[1:])          # launch shape without the pinned buffer
+    kc, vc = g.runner.k_cache.clone(), g.runner.v_cache.clone()
+    b = Buckets(tokens=64, context=256)
+    tol = dict(atol=2e-2, rtol=1e-2) if g.dtype == torch.bfloat16 else dict(atol=1e-4, rtol=0)
+
+    def padded_meta(sched):
+        meta = g.runner.build(sched, w.budget, buckets=b)
+        assert meta.launch_tokens % 64 == 0 or meta.launch_tokens == g.runner.bufs[0].cap[1]
+        assert meta.launch_tokens >= meta.num_tokens
+        return meta
+
+    # Eager runs of the padded launches (and the workspace they need).
+    g.sched = cb.cb_sched_clone(snap)
+    padded, metas = [], []
+    for k in range(n):
+        meta = padded_meta(g.sched)
+        T, Tp = meta.num_tokens, meta.launch_tokens
+        q, kk, vv = (torch.cat([x, x.new_zeros((Tp - T,) + x.shape[1:])]) for x in inputs[k])
+        q_rot, out = torch.empty_like(q), torch.empty_like(q)
+        dm = g.runner.upload(meta)
+        g.runner.append(dm, q, kk, vv, q_rot)
+        g.runner.attend(meta, dm, q_rot, out)
+        torch.cuda.synchronize()
+        padded.append(out[:T].clone())
+        metas.append(meta)
+        torch.testing.assert_close(out[:T].float(), ref[k].float(), **tol)
+    g.runner.ensure_workspace(max(g.runner.workspace_bytes(m) for m in metas))
+    graphs = StepGraphs(g.runner)
+    rows = {}                                       # graph key -> row buffers at fixed addresses
+    modes = []
+    for cycle in range(3):
+        g.sched = cb.cb_sched_clone(snap)
+        for k in range(n):
+            meta = padded_meta(g.sched)
+            T, Tp = meta.num_tokens, meta.launch_tokens
+            key = StepGraphs.key(meta)
+            if key not in rows:
+                rows[key] = [torch.zeros((Tp,) + x.shape[1:], dtype=x.dtype, device=dev) for x in inputs[k]]
+                rows[key] += [torch.empty_like(rows[key][0]), torch.empty_like(rows[key][0])]
+            q, kk, vv, q_rot, out = rows[key]
+            for dst, src in zip((q, kk, vv), inputs[k]):
+                dst[:T].copy_(src)
+            out.fill_(float("nan"))
+
+            def launch(dm, meta=meta, q=q, kk=kk, vv=vv, q_rot=q_rot, out=out):
+                g.runner.append(dm, q, kk, vv, q_rot)
+                g.runner.attend(meta, dm, q_rot, out)
+            modes.append(graphs.step(meta, launch))
+            torch.cuda.synchronize()
+            _ = (out[:T].float() * 2).sum().item()                  # eager work between replays
+            assert torch.equal(out[:T].view(torch.int16), padded[k].view(torch.int16)), (cycle, k)
+    # One graph per (pinned buffer, padded shape); no more padded shapes than exact ones.
+    shapes = {key[1:] for key in graphs.graphs}
+    assert "replay" in modes and modes.count("captured") == len(graphs.graphs)
+    assert len(shapes) <= len(exact) and len(graphs.graphs) <= 2 * len(shapes)
     assert torch.equal(g.runner.k_cache.view(torch.int16), kc.view(torch.int16))
     assert torch.equal(g.runner.v_cache.view(torch.int16), vc.view(torch.int16))
