@@ -1178,12 +1178,15 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a, int32_t n_dec_
     // Decode row: the partials of unit u sit in slots u + w for the waves w whose stage ranges
     // meet the unit's stages [a_u, a_u + n).
     row = ri;
-    const int32_t n = decode_stages(a.ctx_lens[row]);
     const int32_t g = h / a.G, hh = h - g * a.G;
     const int32_t r = g * a.head_blocks + (hh >> 4);
     const int32_t u = row * a.ups + r;
-    const int32_t w0 = n > 0 ? a.dec_unit[2 * u] : 0;
-    P = n > 0 ? a.dec_unit[2 * u + 1] - w0 + 1 : 0;
+    // The unit's two records in one load, beside the context length (they are meaningful only
+    // when the row has keys).
+    const int2 rec = reinterpret_cast<const int2*>(a.dec_unit)[u];
+    const int32_t n = decode_stages(a.ctx_lens[row]);
+    const int32_t w0 = n > 0 ? rec.x : 0;
+    P = n > 0 ? rec.y - w0 + 1 : 0;
     const int64_t base = static_cast<int64_t>(u + w0) * a.hw + (hh & 15);
     po = a.dec_o + base * D;
     pml = a.dec_ml + base * 2;
@@ -1198,6 +1201,13 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a, int32_t n_dec_
     so = D;
     sml = 2;
   }
+  // The first eight partials' o are loaded up front, beside their (m, l) pairs: the weights need
+  // the reductions below, the loads do not.
+  float x0[8][PER];
+#pragma unroll
+  for (int v = 0; v < 8; ++v)
+#pragma unroll
+    for (int j = 0; j < PER; ++j) x0[v][j] = v < P ? po[v * so + lane + 64 * j] : 0.f;
   // Lanes read the partials' (m, l) pairs side by side; butterfly reductions give every lane the
   // same maximum and total in the same order on every run.
   float m = kNegInf;
@@ -1218,6 +1228,18 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a, int32_t n_dec_
     const float wl = i < P ? exp2f(pml[i * sml] - m_use) * inv : 0.f;
     const int32_t n = min(64, P - base);
     int32_t k = 0;
+    if (base == 0) {                          // the prefetched partials, in the same order
+      const int32_t n8 = min(n, 8);
+#pragma unroll
+      for (int v = 0; v < 8; ++v) {
+        if (v < n8) {
+          const float wk = __shfl(wl, v, 64);
+#pragma unroll
+          for (int j = 0; j < PER; ++j) acc[j] += wk * x0[v][j];
+        }
+      }
+      k = n8;
+    }
     for (; k + 8 <= n; k += 8) {              // eight partials' loads in flight together
       float x[8][PER];
 #pragma unroll
