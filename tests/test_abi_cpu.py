@@ -388,3 +388,39 @@ def test_decode_plan_layout_and_rule():
     with pytest.raises(cb.CbError) as e:                  # chunk rows need cu_seqlens_q
         cb.cb_decode_plan(None, ctx, 4, 2, 4096, Hq, Hkv, torch.zeros(8192, dtype=torch.int32), None)
     assert e.value.status == cb.CB_ERR_INVALID
+
+
+def test_decode_plan_rule_random_steps():
+    # Seeded random steps (decode contexts, one to three chunks of random offsets and lengths, MHA
+    # and GQA groups): the library's plan equals the rule above, entry for entry.
+    import numpy as np
+    import torch
+    rng = np.random.Generator(np.random.PCG64(2024))
+    for case in range(40):
+        Hkv = int(rng.choice([1, 4, 8, 32]))
+        G = int(rng.choice([1, 2, 7, 8]))
+        Hq = Hkv * G
+        nd = int(rng.integers(1, 200))
+        dctx = rng.integers(0, 9000, size=nd)
+        dctx[0] = max(int(dctx[0]), 1)
+        n_chunk = int(rng.integers(0, 4))
+        d = rng.integers(1, 1500, size=n_chunk)
+        c = rng.integers(0, 20000, size=n_chunk)
+        ctx = [int(x) for x in dctx] + [int(a + b) for a, b in zip(c, d)]
+        cu = [0]
+        for L in [1] * nd + [int(x) for x in d]:
+            cu.append(cu[-1] + L)
+        mq = int(max(d)) if n_chunk else 1
+        mc = max(ctx)
+        chunks = n_chunk > 0
+        waves = cb.cb_attn_decode_waves(None, chunks)
+        out = torch.full((cb.cb_decode_plan_ints(nd, waves),), -7, dtype=torch.int32)
+        cu_t = torch.tensor(cu, dtype=torch.int32) if chunks else None
+        assert cb.cb_decode_plan(cu_t, torch.tensor(ctx, dtype=torch.int32), nd, mq, mc, Hq, Hkv, out, None) == waves
+        head, first, start = _expected_decode_plan(ctx, cu, nd, Hq, Hkv, waves, mq, mc)
+        W = head[2]
+        o = out.tolist()
+        assert o[:len(head)] == head, case
+        assert o[len(head):len(head) + W] == first, case
+        assert o[len(head) + waves:len(head) + waves + W + 1] == start, case
+        assert all(start[w + 1] > start[w] for w in range(W)), case
