@@ -507,13 +507,36 @@ def main():
         e2e.append((time.perf_counter() - t1) * 1e3)
 
     print("[bench] isolated launches (warm, then cold)...", file=sys.stderr, flush=True)
-    iso = summarize_isolated(*isolation_pass(g, metas, qrots, outs, w, reps=3), metas, w, elt)
+    dec_raw, chk_raw = isolation_pass(g, metas, qrots, outs, w, reps=3)
+    iso = summarize_isolated(dec_raw, chk_raw, metas, w, elt)
     iso["note"] = "decode-only and chunk-only launches of the same step metadata, 3 reps per step"
     flush = torch.zeros(128 << 20, dtype=torch.int32, device=dev)   # 512 MiB: L2 and MALL
     iso_cold = summarize_isolated(*isolation_pass(g, metas, qrots, outs, w, reps=2, flush=flush), metas, w, elt)
     iso_cold["note"] = "as isolated, with a 512 MiB device write before every launch (L2 and MALL cold)"
     del flush
     traffic = committed_traffic("attn_kernel", w.name)
+    # What the chunk rows add to a mixed step: the in-step attention + combine minus the warm
+    # decode-only launch of the same step's metadata, per sampled step with chunk rows.
+    iso_dec = {}
+    for k, t in dec_raw:
+        iso_dec.setdefault(k, []).append(t)
+    marg, mflops = [], []
+    for i, e8 in evs.items():
+        k = step_ids[i]
+        if k in iso_dec and chunk_flops(metas[k], w) > 0:
+            marg.append(e8[0].elapsed_time(e8[1]) + e8[4].elapsed_time(e8[5]) - sum(iso_dec[k]) / len(iso_dec[k]))
+            mflops.append(chunk_flops(metas[k], w))
+    chunk_marginal = None
+    if marg:
+        m_s = sum(marg) / len(marg) / 1e3
+        f = sum(mflops) / len(mflops)
+        chunk_marginal = {"us_per_step": m_s * 1e6, "chunk_flops_per_step": f,
+                          "TFLOPs": f / max(m_s, 1e-12) / 1e12,
+                          "frac_mfma": f / max(m_s, 1e-12) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                          "steps": len(marg),
+                          "note": "chunk FLOPs over the time they add to the mixed step (in-step attention "
+                                  "+ combine minus the warm decode-only launch of the same metadata); a step "
+                                  "cost, not the tiles' matrix-core utilisation (isolated.chunk_frac_mfma)"}
     lin = linear_pass(w, dev, {"decode_only": max(1, len(w.decode_ctx)),
                                "mixed_step": max(m.num_tokens for m in metas)}) if w.dtype == "bf16" else None
 
@@ -540,6 +563,7 @@ def main():
                      "bytes_per_launch": sum(abytes) / len(abytes), "avg_launch_us": attn_avg_s * 1e6},
         "isolated": iso,
         "isolated_cold": iso_cold,
+        "chunk_marginal": chunk_marginal,
         "linear_layers": lin,
         "combine_avg_us": sum(cmb_ms) / len(cmb_ms) * 1e3,
         "device_step_us": sum(dev_step_ms) / len(dev_step_ms) * 1e3,
