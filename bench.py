@@ -56,6 +56,12 @@ def parse():
                     help="also time the same steps replayed from HIP graphs (one graph per step of "
                          "the cycle, captured on its first occurrence) and report it beside the "
                          "eager figures")
+    ap.add_argument("--only", choices=("chunk", "decode"), default=None,
+                    help="after the warm-up, run only isolated launches of one kind (chunk-only or "
+                         "decode-only launches of every step's metadata, --reps each), print their "
+                         "summary and exit: a run whose attention dispatches are all of that kind, "
+                         "for profiler counters")
+    ap.add_argument("--reps", type=int, default=5, help="launches per step with --only")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one device copy of this many MiB before timing (a known-size kernel "
                          "for scaling profiler byte counters)")
@@ -108,7 +114,7 @@ def committed_traffic(kernel: str, workload: str):
     return rec["kernels"][kernel]["traffic_bytes"]
 
 
-def isolation_pass(g, metas, qrots, outs, w, reps: int, flush=None):
+def isolation_pass(g, metas, qrots, outs, w, reps: int, flush=None, kinds=("decode", "chunk")):
     """Decode-only and chunk-only launches of each step's metadata, timed with HIP events on the
     launch stream: per-kernel durations without the other kernel running beside it.  Decode
     launches report attention + combine time.  With ``flush`` (a device tensor), it is rewritten
@@ -133,7 +139,7 @@ def isolation_pass(g, metas, qrots, outs, w, reps: int, flush=None):
         for e in ev:
             e.record()
         for _ in range(reps):
-            if nd > 0:
+            if nd > 0 and "decode" in kinds:
                 if flush is not None:
                     flush.add_(1)
                 cb.cb_mixed_paged_attention(
@@ -144,7 +150,7 @@ def isolation_pass(g, metas, qrots, outs, w, reps: int, flush=None):
                     scale=g.runner.scale, events=[ev[0], ev[1], None, None, ev[4], ev[5]])
                 torch.cuda.synchronize()
                 dec.append((k, ev[0].elapsed_time(ev[1]) + ev[4].elapsed_time(ev[5])))
-            if T > nd:
+            if T > nd and "chunk" in kinds:
                 if flush is not None:
                     flush.add_(1)
                 cb.cb_mixed_paged_attention(
@@ -368,9 +374,16 @@ def main():
     # collector only the few objects each step creates.
     gc.collect()
     gc.freeze()
-    for _ in range(args.warmup):
+    for _ in range(max(args.warmup, cb_steps if args.only else 0)):
         one_step()
     torch.cuda.synchronize()
+    if args.only:
+        print(f"[bench] {args.only}-only launches, {args.reps} per step...", file=sys.stderr, flush=True)
+        dec_raw, chk_raw = isolation_pass(g, metas, qrots, outs, w, reps=args.reps, kinds=(args.only,))
+        res = summarize_isolated(dec_raw, chk_raw, metas, w, 2)
+        res.update({"only": args.only, "reps": args.reps, "workload": w.name})
+        print(json.dumps(res), flush=True)
+        return
 
     # Per-step phase events on a sample of the timed steps (created and touched once so the
     # runtime objects exist).

@@ -83,6 +83,10 @@ static_assert(CB_DECODE_MIN_STAGES *
               "non-empty waves");
 
 constexpr int kChunkRows = 128;   // rows per chunk tile: 4 waves x 32
+// Chunk tiles let a row's softmax reference lag its running maximum by up to this much (log2
+// units): weights 2^(s c - m_ref) stay below 2^8, and the accumulator is rescaled only when a
+// maximum jumps further.
+constexpr float kRescaleSlack = 8.f;
 constexpr int kChunkKeys = 32;    // keys per LDS stage of a chunk tile
 #ifndef CB_CHUNK_STAGES
 #define CB_CHUNK_STAGES 4             // chunk K/V stages in the LDS ring (copies run NS - 1 ahead)
@@ -230,6 +234,15 @@ __device__ __forceinline__ void lds_copy16_asm_s(const char* base, uint32_t voff
       : "=&s"(saved)
       : "v"(voff), "s"(base), "s"(dst));
 }
+// Scalar (SMEM) load of one int32 from a wave-uniform address, issued without waiting; the
+// value may be used only after sload_ready (s_waitcnt lgkmcnt(0), which the value passes
+// through, so no use can be scheduled before it).
+__device__ __forceinline__ int32_t sload_issue(const int32_t* p) {
+  int32_t v;
+  asm volatile("s_load_dword %0, %1, 0x0" : "=s"(v) : "s"(p) : "memory");
+  return v;
+}
+__device__ __forceinline__ void sload_ready(int32_t& v) { asm volatile("s_waitcnt lgkmcnt(0)" : "+s"(v)); }
 // Wait for this wave's LDS reads before a DMA overwrites the buffer they read
 // (s_waitcnt lgkmcnt(0), vmcnt and expcnt untouched).
 __device__ __forceinline__ void lds_reads_done() { __builtin_amdgcn_s_waitcnt(0xC07F); }
@@ -339,71 +352,118 @@ __device__ __forceinline__ void wait_vm_barrier() {
 }
 
 // The operands of one 32-key chunk stage (bf16): K rows (KS ds_read_b128) and V^T (two
-// ds_read_b64_tr_b16 per 32x16 piece, the second 16 keys further down), issued back to back
-// and waited for together inside one asm block.  ka[ks] / va[2 mt + h] are the LDS addresses
-// lds_row_frag / lds_vt_frag32 would read in ring buffer 0 (piece ps = 0); OFF selects the ring
-// buffer (an immediate offset), and ps = 1 is 16 rows further.
+// ds_read_b64_tr_b16 per 32x16 piece, the second 16 keys further down).  ka[ks] / va[2 mt + h]
+// are the LDS addresses lds_row_frag / lds_vt_frag32 would read in ring buffer 0 (piece ps = 0);
+// OFF selects the ring buffer (an immediate offset), and ps = 1 is 16 rows further.
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
-template <int D> struct StageRegs;
-template <> struct StageRegs<128> {
+// Two asm blocks issue them without waiting: K rows (KRegs) and V^T (VRegs), in the ring buffer
+// selected by OFF.  lds_operands_ready() waits for both (lgkmcnt(0)) and passes every destination register
+// through the wait, so no use of them can be scheduled before it.
+template <int D> struct KRegs;
+template <int D> struct VRegs;
+template <> struct KRegs<128> {
   u32x4 k[8];
+  template <int OFF>
+  __device__ __forceinline__ void read(const uint32_t (&ka)[8]) {
+    asm volatile(
+        "ds_read_b128 %0, %8 offset:%16\n\t"
+        "ds_read_b128 %1, %9 offset:%16\n\t"
+        "ds_read_b128 %2, %10 offset:%16\n\t"
+        "ds_read_b128 %3, %11 offset:%16\n\t"
+        "ds_read_b128 %4, %12 offset:%16\n\t"
+        "ds_read_b128 %5, %13 offset:%16\n\t"
+        "ds_read_b128 %6, %14 offset:%16\n\t"
+        "ds_read_b128 %7, %15 offset:%16"
+        : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(k[4]), "=&v"(k[5]), "=&v"(k[6]), "=&v"(k[7])
+        : "v"(ka[0]), "v"(ka[1]), "v"(ka[2]), "v"(ka[3]), "v"(ka[4]), "v"(ka[5]), "v"(ka[6]), "v"(ka[7]), "n"(OFF));
+  }
+};
+template <> struct KRegs<64> {
+  u32x4 k[4];
+  template <int OFF>
+  __device__ __forceinline__ void read(const uint32_t (&ka)[4]) {
+    asm volatile(
+        "ds_read_b128 %0, %4 offset:%8\n\t"
+        "ds_read_b128 %1, %5 offset:%8\n\t"
+        "ds_read_b128 %2, %6 offset:%8\n\t"
+        "ds_read_b128 %3, %7 offset:%8"
+        : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3])
+        : "v"(ka[0]), "v"(ka[1]), "v"(ka[2]), "v"(ka[3]), "n"(OFF));
+  }
+};
+template <> struct VRegs<128> {
   u32x2 v[2][8];   // [ps][2 mt + h]
   template <int OFF>
-  __device__ __forceinline__ void read(const uint32_t (&ka)[8], const uint32_t (&va)[8]) {
+  __device__ __forceinline__ void read(const uint32_t (&va)[8]) {
     asm volatile(
-        "ds_read_b128 %0, %24 offset:%40\n\t"
-        "ds_read_b128 %1, %25 offset:%40\n\t"
-        "ds_read_b128 %2, %26 offset:%40\n\t"
-        "ds_read_b128 %3, %27 offset:%40\n\t"
-        "ds_read_b128 %4, %28 offset:%40\n\t"
-        "ds_read_b128 %5, %29 offset:%40\n\t"
-        "ds_read_b128 %6, %30 offset:%40\n\t"
-        "ds_read_b128 %7, %31 offset:%40\n\t"
-        "ds_read_b64_tr_b16 %8, %32 offset:%40\n\t"
-        "ds_read_b64_tr_b16 %9, %33 offset:%40\n\t"
-        "ds_read_b64_tr_b16 %10, %34 offset:%40\n\t"
-        "ds_read_b64_tr_b16 %11, %35 offset:%40\n\t"
-        "ds_read_b64_tr_b16 %12, %36 offset:%40\n\t"
-        "ds_read_b64_tr_b16 %13, %37 offset:%40\n\t"
-        "ds_read_b64_tr_b16 %14, %38 offset:%40\n\t"
-        "ds_read_b64_tr_b16 %15, %39 offset:%40\n\t"
-        "ds_read_b64_tr_b16 %16, %32 offset:%41\n\t"
-        "ds_read_b64_tr_b16 %17, %33 offset:%41\n\t"
-        "ds_read_b64_tr_b16 %18, %34 offset:%41\n\t"
-        "ds_read_b64_tr_b16 %19, %35 offset:%41\n\t"
-        "ds_read_b64_tr_b16 %20, %36 offset:%41\n\t"
-        "ds_read_b64_tr_b16 %21, %37 offset:%41\n\t"
-        "ds_read_b64_tr_b16 %22, %38 offset:%41\n\t"
-        "ds_read_b64_tr_b16 %23, %39 offset:%41\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(k[4]), "=&v"(k[5]), "=&v"(k[6]), "=&v"(k[7]), "=&v"(v[0][0]), "=&v"(v[0][1]), "=&v"(v[0][2]), "=&v"(v[0][3]), "=&v"(v[0][4]), "=&v"(v[0][5]), "=&v"(v[0][6]), "=&v"(v[0][7]), "=&v"(v[1][0]), "=&v"(v[1][1]), "=&v"(v[1][2]), "=&v"(v[1][3]), "=&v"(v[1][4]), "=&v"(v[1][5]), "=&v"(v[1][6]), "=&v"(v[1][7])
-        : "v"(ka[0]), "v"(ka[1]), "v"(ka[2]), "v"(ka[3]), "v"(ka[4]), "v"(ka[5]), "v"(ka[6]), "v"(ka[7]), "v"(va[0]), "v"(va[1]), "v"(va[2]), "v"(va[3]), "v"(va[4]), "v"(va[5]), "v"(va[6]), "v"(va[7]), "n"(OFF), "n"(OFF + 4096));
+        "ds_read_b64_tr_b16 %0, %16 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %1, %17 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %2, %18 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %3, %19 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %4, %20 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %5, %21 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %6, %22 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %7, %23 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %8, %16 offset:%25\n\t"
+        "ds_read_b64_tr_b16 %9, %17 offset:%25\n\t"
+        "ds_read_b64_tr_b16 %10, %18 offset:%25\n\t"
+        "ds_read_b64_tr_b16 %11, %19 offset:%25\n\t"
+        "ds_read_b64_tr_b16 %12, %20 offset:%25\n\t"
+        "ds_read_b64_tr_b16 %13, %21 offset:%25\n\t"
+        "ds_read_b64_tr_b16 %14, %22 offset:%25\n\t"
+        "ds_read_b64_tr_b16 %15, %23 offset:%25"
+        : "=&v"(v[0][0]), "=&v"(v[0][1]), "=&v"(v[0][2]), "=&v"(v[0][3]), "=&v"(v[0][4]), "=&v"(v[0][5]), "=&v"(v[0][6]), "=&v"(v[0][7]),
+          "=&v"(v[1][0]), "=&v"(v[1][1]), "=&v"(v[1][2]), "=&v"(v[1][3]), "=&v"(v[1][4]), "=&v"(v[1][5]), "=&v"(v[1][6]), "=&v"(v[1][7])
+        : "v"(va[0]), "v"(va[1]), "v"(va[2]), "v"(va[3]), "v"(va[4]), "v"(va[5]), "v"(va[6]), "v"(va[7]), "n"(OFF), "n"(OFF + 4096));
   }
 };
-template <> struct StageRegs<64> {
-  u32x4 k[4];
+template <> struct VRegs<64> {
   u32x2 v[2][4];   // [ps][2 mt + h]
   template <int OFF>
-  __device__ __forceinline__ void read(const uint32_t (&ka)[4], const uint32_t (&va)[4]) {
+  __device__ __forceinline__ void read(const uint32_t (&va)[4]) {
     asm volatile(
-        "ds_read_b128 %0, %12 offset:%20\n\t"
-        "ds_read_b128 %1, %13 offset:%20\n\t"
-        "ds_read_b128 %2, %14 offset:%20\n\t"
-        "ds_read_b128 %3, %15 offset:%20\n\t"
-        "ds_read_b64_tr_b16 %4, %16 offset:%20\n\t"
-        "ds_read_b64_tr_b16 %5, %17 offset:%20\n\t"
-        "ds_read_b64_tr_b16 %6, %18 offset:%20\n\t"
-        "ds_read_b64_tr_b16 %7, %19 offset:%20\n\t"
-        "ds_read_b64_tr_b16 %8, %16 offset:%21\n\t"
-        "ds_read_b64_tr_b16 %9, %17 offset:%21\n\t"
-        "ds_read_b64_tr_b16 %10, %18 offset:%21\n\t"
-        "ds_read_b64_tr_b16 %11, %19 offset:%21\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(v[0][0]), "=&v"(v[0][1]), "=&v"(v[0][2]), "=&v"(v[0][3]), "=&v"(v[1][0]), "=&v"(v[1][1]), "=&v"(v[1][2]), "=&v"(v[1][3])
-        : "v"(ka[0]), "v"(ka[1]), "v"(ka[2]), "v"(ka[3]), "v"(va[0]), "v"(va[1]), "v"(va[2]), "v"(va[3]), "n"(OFF), "n"(OFF + 2048));
+        "ds_read_b64_tr_b16 %0, %8 offset:%12\n\t"
+        "ds_read_b64_tr_b16 %1, %9 offset:%12\n\t"
+        "ds_read_b64_tr_b16 %2, %10 offset:%12\n\t"
+        "ds_read_b64_tr_b16 %3, %11 offset:%12\n\t"
+        "ds_read_b64_tr_b16 %4, %8 offset:%13\n\t"
+        "ds_read_b64_tr_b16 %5, %9 offset:%13\n\t"
+        "ds_read_b64_tr_b16 %6, %10 offset:%13\n\t"
+        "ds_read_b64_tr_b16 %7, %11 offset:%13"
+        : "=&v"(v[0][0]), "=&v"(v[0][1]), "=&v"(v[0][2]), "=&v"(v[0][3]), "=&v"(v[1][0]), "=&v"(v[1][1]), "=&v"(v[1][2]), "=&v"(v[1][3])
+        : "v"(va[0]), "v"(va[1]), "v"(va[2]), "v"(va[3]), "n"(OFF), "n"(OFF + 2048));
   }
 };
+// Wait for this wave's LDS reads; the registers pass through the wait (data dependence).
+__device__ __forceinline__ void lds_operands_ready(KRegs<128>& kr, VRegs<128>& vr) {
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(kr.k[0]), "+v"(kr.k[1]), "+v"(kr.k[2]), "+v"(kr.k[3]), "+v"(kr.k[4]), "+v"(kr.k[5]), "+v"(kr.k[6]), "+v"(kr.k[7]),
+                 "+v"(vr.v[0][0]), "+v"(vr.v[0][1]), "+v"(vr.v[0][2]), "+v"(vr.v[0][3]), "+v"(vr.v[0][4]), "+v"(vr.v[0][5]), "+v"(vr.v[0][6]), "+v"(vr.v[0][7]),
+                 "+v"(vr.v[1][0]), "+v"(vr.v[1][1]), "+v"(vr.v[1][2]), "+v"(vr.v[1][3]), "+v"(vr.v[1][4]), "+v"(vr.v[1][5]), "+v"(vr.v[1][6]), "+v"(vr.v[1][7]));
+}
+__device__ __forceinline__ void lds_operands_ready(KRegs<64>& kr, VRegs<64>& vr) {
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(kr.k[0]), "+v"(kr.k[1]), "+v"(kr.k[2]), "+v"(kr.k[3]),
+                 "+v"(vr.v[0][0]), "+v"(vr.v[0][1]), "+v"(vr.v[0][2]), "+v"(vr.v[0][3]), "+v"(vr.v[1][0]), "+v"(vr.v[1][1]), "+v"(vr.v[1][2]), "+v"(vr.v[1][3]));
+}
+template <int D>
+__device__ __forceinline__ void lds_operands_ready(KRegs<D>& kr) {
+  if constexpr (D == 128)
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(kr.k[0]), "+v"(kr.k[1]), "+v"(kr.k[2]), "+v"(kr.k[3]), "+v"(kr.k[4]), "+v"(kr.k[5]), "+v"(kr.k[6]), "+v"(kr.k[7]));
+  else
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(kr.k[0]), "+v"(kr.k[1]), "+v"(kr.k[2]), "+v"(kr.k[3]));
+}
+template <int D>
+__device__ __forceinline__ void lds_operands_ready(VRegs<D>& vr) {
+  if constexpr (D == 128)
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(vr.v[0][0]), "+v"(vr.v[0][1]), "+v"(vr.v[0][2]), "+v"(vr.v[0][3]), "+v"(vr.v[0][4]), "+v"(vr.v[0][5]), "+v"(vr.v[0][6]), "+v"(vr.v[0][7]),
+                   "+v"(vr.v[1][0]), "+v"(vr.v[1][1]), "+v"(vr.v[1][2]), "+v"(vr.v[1][3]), "+v"(vr.v[1][4]), "+v"(vr.v[1][5]), "+v"(vr.v[1][6]), "+v"(vr.v[1][7]));
+  else
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(vr.v[0][0]), "+v"(vr.v[0][1]), "+v"(vr.v[0][2]), "+v"(vr.v[0][3]), "+v"(vr.v[1][0]), "+v"(vr.v[1][1]), "+v"(vr.v[1][2]), "+v"(vr.v[1][3]));
+}
 
 // ---------------------------------------------------------------------------------------------
 // Decode rows.
@@ -1002,101 +1062,258 @@ __device__ __forceinline__ void chunk_tile(const AttnArgs& a, int32_t tile, char
   // the compiler adds no waits there.
   const int32_t n_st = kt_hi - kt_lo;
   int32_t j = 0;
-  while (j < n_st) {
-    fill_window(((kt_lo + j) * kChunkKeys) >> bsh);   // ends with vmcnt(0): nothing left pending
-    __syncthreads();                                   // also: every wave is done with the ring
-    // Stages whose keys all lie in blocks [win_lo, win_lo + kBlockWindow) (a multiple of 32 keys).
-    const int64_t key_end = static_cast<int64_t>(win_lo + kBlockWindow) << bsh;
-    const int32_t j_end = kv_end <= key_end ? n_st : static_cast<int32_t>(min<int64_t>(n_st, key_end / kChunkKeys - kt_lo));
-    // The ring restarts at buffer 0 in every window; unrolled by NS, each stage's buffer is a
-    // compile-time constant (immediate LDS offsets).
-    const int32_t j0 = j;
-    auto stage = [&](int32_t jj, auto B) {
-      constexpr int buf = decltype(B)::value;
-      constexpr int next_buf = (buf + NS - 1) % NS;
-      const int32_t kt = kt_lo + jj;
-      wait_stage(min(NS - 2, j_end - 1 - jj));   // every wave's copy of stage jj has landed
-      if (jj + NS - 1 < j_end) issue(kt + NS - 1, next_buf);
+  if constexpr (sizeof(T) == 2) {
+    // Software-pipelined stages: iteration jj reads V of stage jj and K of stage jj + 1, then
+    // issues stage jj + 1's score products (matrix cores) while the softmax of stage jj (vector
+    // ALU) runs, then stage jj's P V products.  So each wave keeps the matrix cores fed while
+    // its own exponentials run, instead of alternating the two.  Buffer of stage jj - 1 is
+    // free once every wave has passed iteration jj's barrier (it read V of jj - 1 and K of jj in
+    // iteration jj - 1), so stage jj + NS - 1's copy goes there: NS - 2 stages of work cover it.
+    //
+    // Each wave copies 8 consecutive key rows of a stage (8 <= block size, 8-aligned), so they
+    // lie in one cache block: one block id per wave and stage, read by a scalar load one
+    // iteration before its copy is issued.  Rows past kv_end repeat kv_end - 1, which lies in the
+    // same block as the wave's first real row.
+    static_assert(NS >= 3, "pipelined ring needs three buffers");
+    static_assert(NCPW * RPI == 8, "each wave copies 8 rows of a stage");
+    if (n_st > 0) {
+      const int32_t row_w = 8 * wave;
+      int32_t cub = sload_issue(a.cu_blocks + s);
+      sload_ready(cub);
+      const int32_t* bt = a.block_table + cub;
+      auto blk_ptr = [&](int32_t jj) { return bt + (min((kt_lo + jj) * kChunkKeys + row_w, k_last) >> bsh); };
+      auto issue_s = [&](int32_t jj, int buf, int32_t blk) {
+        const int32_t k0 = (kt_lo + jj) * kChunkKeys;
+        const char* kb = kc + (static_cast<int64_t>(blk) * blk_bytes + head_bytes);
+        const char* vb = vc + (static_cast<int64_t>(blk) * blk_bytes + head_bytes);
+        if (k0 + row_w + 7 <= k_last) {               // the wave's rows are all real keys
+#pragma unroll
+          for (int jc = 0; jc < NCPW; ++jc) {
+            const int i = wave * NCPW + jc;
+            const int64_t roff = static_cast<int64_t>((k0 + i * RPI) & bmask) * ROW;
+            lds_copy16_asm_s(kb + roff, lane_off[jc], sK + buf * STAGE + i * 1024);
+            lds_copy16_asm_s(vb + roff, lane_off[jc], sV + buf * STAGE + i * 1024);
+          }
+        } else {                                      // keys past kv_end repeat the last one
+#pragma unroll
+          for (int jc = 0; jc < NCPW; ++jc) {
+            const int i = wave * NCPW + jc;
+            const int r = i * RPI + cp_row;
+            const int32_t key = min(k0 + r, k_last);
+            const uint32_t voff = static_cast<uint32_t>((key & bmask) * ROW + 16 * lds_chunk(cp_pos, r, ROW));
+            lds_copy16_asm_s(kb, voff, sK + buf * STAGE + i * 1024);
+            lds_copy16_asm_s(vb, voff, sV + buf * STAGE + i * 1024);
+          }
+        }
+      };
+      // Prologue: block ids and copies of the first NS - 1 stages, the next id, then the first
+      // stage's scores.
+      int32_t blk0[NS - 1];
+#pragma unroll
+      for (int p = 0; p < NS - 1; ++p) blk0[p] = sload_issue(blk_ptr(p));
+#pragma unroll
+      for (int p = 0; p < NS - 1; ++p) sload_ready(blk0[p]);
+#pragma unroll
+      for (int p = 0; p < NS - 1; ++p)
+        if (p < n_st) issue_s(p, p, blk0[p]);
+      int32_t blk_nx = sload_issue(blk_ptr(NS - 1));
+      wait_stage(min(NS - 2, n_st - 1));
+      f32x16 s_cur = f32x16{};
+      {
+        KRegs<D> kr;
+        kr.template read<0>(ka);
+        lds_operands_ready<D>(kr);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          Frag<T> kf;
+          kf.u = make_uint4(kr.k[ks].x, kr.k[ks].y, kr.k[ks].z, kr.k[ks].w);
+          mma32_k16(s_cur, kf, qf[ks]);
+        }
+      }
+      auto step = [&](int32_t jj, auto B) {
+        constexpr int buf = decltype(B)::value;
+        constexpr int nbuf = (buf + 1) % NS;
+        constexpr int pbuf = (buf + NS - 1) % NS;
+        if (jj + 1 < n_st) wait_stage(min(NS - 3, n_st - jj - 2));   // stage jj + 1 landed everywhere
+        if (jj + NS - 1 < n_st) {
+          sload_ready(blk_nx);
+          issue_s(jj + NS - 1, pbuf, blk_nx);
+        }
+        // K of stage jj + 1 is read even on the last stage (stale ring data, its products
+        // unused), so the score products and the softmax share one basic block and can be
+        // interleaved.
+        VRegs<D> vr;
+        KRegs<D> kr;
+        vr.template read<buf * STAGE>(va);
+        kr.template read<nbuf * STAGE>(ka);
 
-      Frag<T> kf[KS];
-      Frag<T> vt[2][MT];
-      if constexpr (sizeof(T) == 2) {
-        StageRegs<D> sr;
-        sr.template read<buf * STAGE>(ka, va);
+        // Mask and row maximum of stage jj (while the operand reads are in flight).
+        const int32_t k0 = (kt_lo + jj) * kChunkKeys;
+        f32x16 st = s_cur;
+        if (k0 + kChunkKeys - 1 > c + qb * a.bmq) {   // some key of the stage may pass a row
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) kf[ks].u = make_uint4(sr.k[ks].x, sr.k[ks].y, sr.k[ks].z, sr.k[ks].w);
+          for (int r = 0; r < 16; ++r)
+            if (k0 + acc32_row(lane, r) > qpos) st[r] = kNegInf;
+        }
+        float mx = st[0];
 #pragma unroll
-        for (int ps = 0; ps < 2; ++ps)
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, st[r]);
+        mx = half_xor_max(mx);
+        // Lazy rescale: the weights are 2^(s c - m_ref) with m_ref a running maximum allowed to
+        // lag the true one by up to kRescaleSlack (weights stay below 2^kRescaleSlack), so the
+        // accumulator rescale and its exponential run only when some row's maximum jumps past it.
+        const float m_cand = mx * a.scale_log2;
+        if (__builtin_amdgcn_ballot_w64(m_cand > m_run + kRescaleSlack)) {
+          const float m_new = fmaxf(m_run, m_cand);
+          const float alpha = m_new == kNegInf ? 1.f : fast_exp2(m_run - m_new);
+          l_run *= alpha;
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt)
-            vt[ps][mt].u = make_uint4(sr.v[ps][2 * mt].x, sr.v[ps][2 * mt].y, sr.v[ps][2 * mt + 1].x,
-                                      sr.v[ps][2 * mt + 1].y);
-      } else {
+          for (int mt = 0; mt < MT; ++mt) o[mt] *= alpha;
+          m_run = m_new;
+        }
+        const float m_use = m_run == kNegInf ? 0.f : m_run;
+
+        lds_operands_ready(kr, vr);
+        blk_nx = sload_issue(blk_ptr(jj + NS));        // for the next iteration's copy
+        s_cur = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          Frag<T> kf;
+          kf.u = make_uint4(kr.k[ks].x, kr.k[ks].y, kr.k[ks].z, kr.k[ks].w);
+          mma32_k16(s_cur, kf, qf[ks]);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) st[r] = fast_exp2(fmaf(st[r], a.scale_log2, -m_use));
+        float s4[4];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) s4[q4] = (st[4 * q4] + st[4 * q4 + 1]) + (st[4 * q4 + 2] + st[4 * q4 + 3]);
+        l_run += (s4[0] + s4[1]) + (s4[2] + s4[3]);
+#pragma unroll
+        for (int ps = 0; ps < 2; ++ps) {          // 16-key contraction steps
+          float pv[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pv[e] = st[8 * ps + e];
+          Frag<T> pf;
+          pf.set_all(pv);
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            Frag<T> vt;
+            vt.u = make_uint4(vr.v[ps][2 * mt].x, vr.v[ps][2 * mt].y, vr.v[ps][2 * mt + 1].x, vr.v[ps][2 * mt + 1].y);
+            mma32_k16(o[mt], vt, pf);
+          }
+        }
+        // Issue order: each score product followed by a share of the softmax arithmetic, then
+        // each P V product followed by the rest, so the matrix cores and the vector ALU work side
+        // by side within the wave.
+#pragma unroll
+        for (int i = 0; i < KS; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x402, 40 / KS, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 2 * MT; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x402, 2, 0);
+        }
+      };
+      while (j < n_st) {
+        step(j, std::integral_constant<int, 0>{});
+        if (++j == n_st) break;
+        step(j, std::integral_constant<int, 1>{});
+        if (++j == n_st) break;
+        step(j, std::integral_constant<int, 2 % NS>{});
+        if (++j == n_st) break;
+        if constexpr (NS > 3) {
+          step(j, std::integral_constant<int, 3 % NS>{});
+          if (++j == n_st) break;
+        }
+      }
+      sload_ready(blk_nx);                             // nothing left in flight
+    }
+  } else {
+    while (j < n_st) {
+      fill_window(((kt_lo + j) * kChunkKeys) >> bsh);   // ends with vmcnt(0): nothing left pending
+      __syncthreads();                                   // also: every wave is done with the ring
+      // Stages whose keys all lie in blocks [win_lo, win_lo + kBlockWindow) (a multiple of 32 keys).
+      const int64_t key_end = static_cast<int64_t>(win_lo + kBlockWindow) << bsh;
+      const int32_t j_end = kv_end <= key_end ? n_st : static_cast<int32_t>(min<int64_t>(n_st, key_end / kChunkKeys - kt_lo));
+      // The ring restarts at buffer 0 in every window; unrolled by NS, each stage's buffer is a
+      // compile-time constant (immediate LDS offsets).
+      const int32_t j0 = j;
+      auto stage = [&](int32_t jj, auto B) {
+        constexpr int buf = decltype(B)::value;
+        constexpr int next_buf = (buf + NS - 1) % NS;
+        const int32_t kt = kt_lo + jj;
+        wait_stage(min(NS - 2, j_end - 1 - jj));   // every wave's copy of stage jj has landed
+        if (jj + NS - 1 < j_end) issue(kt + NS - 1, next_buf);
+
+        Frag<T> kf[KS];
+        Frag<T> vt[2][MT];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) kf[ks] = lds_row_frag<T>(sK + buf * STAGE, col, 16 * ks + 8 * half, ROW);
 #pragma unroll
         for (int ps = 0; ps < 2; ++ps)
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt) vt[ps][mt] = lds_vt_frag32<T>(sV + buf * STAGE, mt, ps, lane, ROW);
-      }
 
-      const int32_t k0 = kt * kChunkKeys;
-      f32x16 st = f32x16{};
+        const int32_t k0 = kt * kChunkKeys;
+        f32x16 st = f32x16{};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) mma32_k16(st, kf[ks], qf[ks]);
-      if (k0 + kChunkKeys - 1 > c + qb * a.bmq) {   // some key of the stage may pass a row
+        for (int ks = 0; ks < KS; ++ks) mma32_k16(st, kf[ks], qf[ks]);
+        if (k0 + kChunkKeys - 1 > c + qb * a.bmq) {   // some key of the stage may pass a row
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (k0 + acc32_row(lane, r) > qpos) st[r] = kNegInf;
-      }
-      // Raw scores: the maximum is taken before scaling (scale > 0 keeps the order) and the scale
-      // is folded into the exponent, 2^(s c - m).
-      float mx = st[0];
+          for (int r = 0; r < 16; ++r)
+            if (k0 + acc32_row(lane, r) > qpos) st[r] = kNegInf;
+        }
+        // Raw scores: the maximum is taken before scaling (scale > 0 keeps the order) and the scale
+        // is folded into the exponent, 2^(s c - m).
+        float mx = st[0];
 #pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, st[r]);
-      mx = half_xor_max(mx);
-      const float m_new = fmaxf(m_run, mx * a.scale_log2);
-      const float m_use = m_new == kNegInf ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - m_use);
-      float psum = 0.f;
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, st[r]);
+        mx = half_xor_max(mx);
+        const float m_new = fmaxf(m_run, mx * a.scale_log2);
+        const float m_use = m_new == kNegInf ? 0.f : m_new;
+        const float alpha = fast_exp2(m_run - m_use);
+        float psum = 0.f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float e = fast_exp2(fmaf(st[r], a.scale_log2, -m_use));
-        st[r] = e;
-        psum += e;
-      }
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-      if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {   // some row's maximum moved
+        for (int r = 0; r < 16; ++r) {
+          const float e = fast_exp2(fmaf(st[r], a.scale_log2, -m_use));
+          st[r] = e;
+          psum += e;
+        }
+        l_run = l_run * alpha + psum;
+        m_run = m_new;
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {   // some row's maximum moved
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) o[mt] *= alpha;
-      }
+          for (int mt = 0; mt < MT; ++mt) o[mt] *= alpha;
+        }
 #pragma unroll
-      for (int ps = 0; ps < 2; ++ps) {          // 16-key contraction steps
-        float pv[8];
+        for (int ps = 0; ps < 2; ++ps) {          // 16-key contraction steps
+          float pv[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pv[e] = st[8 * ps + e];
-        Frag<T> pf;
-        pf.set_all(pv);
+          for (int e = 0; e < 8; ++e) pv[e] = st[8 * ps + e];
+          Frag<T> pf;
+          pf.set_all(pv);
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) mma32_k16(o[mt], vt[ps][mt], pf);
-      }
-    };
+          for (int mt = 0; mt < MT; ++mt) mma32_k16(o[mt], vt[ps][mt], pf);
+        }
+      };
 #pragma unroll
-    for (int p = 0; p < NS - 1; ++p)
-      if (j0 + p < j_end) issue(kt_lo + j0 + p, p);
-    while (j < j_end) {
-      stage(j, std::integral_constant<int, 0>{});
-      if (++j == j_end) break;
-      stage(j, std::integral_constant<int, 1>{});
-      if (++j == j_end) break;
-      if constexpr (NS > 2) {
-        stage(j, std::integral_constant<int, 2 % NS>{});
+      for (int p = 0; p < NS - 1; ++p)
+        if (j0 + p < j_end) issue(kt_lo + j0 + p, p);
+      while (j < j_end) {
+        stage(j, std::integral_constant<int, 0>{});
         if (++j == j_end) break;
-      }
-      if constexpr (NS > 3) {
-        stage(j, std::integral_constant<int, 3 % NS>{});
+        stage(j, std::integral_constant<int, 1>{});
         if (++j == j_end) break;
+        if constexpr (NS > 2) {
+          stage(j, std::integral_constant<int, 2 % NS>{});
+          if (++j == j_end) break;
+        }
+        if constexpr (NS > 3) {
+          stage(j, std::integral_constant<int, 3 % NS>{});
+          if (++j == j_end) break;
+        }
       }
     }
   }
