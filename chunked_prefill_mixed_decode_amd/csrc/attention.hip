@@ -511,23 +511,33 @@ struct TileGrid {
   int32_t nd, Hkv, q_blocks, nsplit, bmq;
   int64_t n_tiles, per_xcd;     // tiles; chunk workgroups per XCD (launch order below)
 };
-__host__ __device__ __forceinline__ bool chunk_tile_span(int32_t tile, const TileGrid& tg, const int32_t* cu_q,
-                                                         const int32_t* ctx_lens, TileSpan& t) {
+// The tile's chunk, KV head, query block and split from its number alone.
+__host__ __device__ __forceinline__ void chunk_tile_index(int32_t tile, const TileGrid& tg, TileSpan& t) {
   int32_t x = tile;
   t.sp = x % tg.nsplit; x /= tg.nsplit;
   t.qb = tg.q_blocks - 1 - x % tg.q_blocks; x /= tg.q_blocks;
   t.g = x % tg.Hkv;
   t.s = tg.nd + x / tg.Hkv;
-  t.row0 = cu_q[t.s];
-  t.d = cu_q[t.s + 1] - t.row0;
+}
+// The rest of the span from the chunk's row offsets q0 = cu_q[s], q1 = cu_q[s + 1] and its
+// context length ctx = ctx_lens[s].
+__host__ __device__ __forceinline__ bool chunk_tile_rows(const TileGrid& tg, int32_t q0, int32_t q1, int32_t ctx,
+                                                         TileSpan& t) {
+  t.row0 = q0;
+  t.d = q1 - q0;
   if (t.qb * tg.bmq >= t.d) return false;
-  t.c = ctx_lens[t.s] - t.d;
+  t.c = ctx - t.d;
   const int32_t rows = (t.qb + 1) * tg.bmq < t.d ? (t.qb + 1) * tg.bmq : t.d;
   const int32_t total = (t.c + rows + kChunkKeys - 1) / kChunkKeys;   // stages up to the block's last key
   const int32_t per = (total + tg.nsplit - 1) / tg.nsplit;
   t.kt_lo = t.sp * per;
   t.kt_hi = total < t.kt_lo + per ? total : t.kt_lo + per;
   return true;
+}
+__host__ __device__ __forceinline__ bool chunk_tile_span(int32_t tile, const TileGrid& tg, const int32_t* cu_q,
+                                                         const int32_t* ctx_lens, TileSpan& t) {
+  chunk_tile_index(tile, tg, t);
+  return chunk_tile_rows(tg, cu_q[t.s], cu_q[t.s + 1], ctx_lens[t.s], t);
 }
 // Chunk workgroup cb of a launch runs tile (cb mod 8) per_xcd + cb / 8 (XCD-aware order).
 __host__ __device__ __forceinline__ int64_t chunk_wg_tile(int64_t cb, int64_t per_xcd) {
@@ -933,8 +943,17 @@ __device__ __forceinline__ void chunk_tile(const AttnArgs& a, int32_t tile, char
   char* sV = lds + ChunkLds<T, D>::V;
   int32_t* sBlk = reinterpret_cast<int32_t*>(lds + ChunkLds<T, D>::BLK);   // block-table window
 
+  // The chunk's metadata by scalar loads, all four in flight together.
   TileSpan ts;
-  if (!chunk_tile_span(tile, TileGrid{a.nd, a.Hkv, a.q_blocks, a.nsplit, a.bmq, 0, 0}, a.cu_q, a.ctx_lens, ts)) return;
+  const TileGrid tg{a.nd, a.Hkv, a.q_blocks, a.nsplit, a.bmq, 0, 0};
+  chunk_tile_index(tile, tg, ts);
+  int32_t m_q0 = sload_issue(a.cu_q + ts.s), m_q1 = sload_issue(a.cu_q + ts.s + 1);
+  int32_t m_ctx = sload_issue(a.ctx_lens + ts.s), cub = sload_issue(a.cu_blocks + ts.s);
+  sload_ready(m_q0);
+  sload_ready(m_q1);
+  sload_ready(m_ctx);
+  sload_ready(cub);
+  if (!chunk_tile_rows(tg, m_q0, m_q1, m_ctx, ts)) return;
   const int32_t sp = ts.sp, qb = ts.qb, g = ts.g, s = ts.s, row0 = ts.row0, d = ts.d, c = ts.c;
   const int32_t kt_lo = ts.kt_lo, kt_hi = ts.kt_hi;
   const int32_t kv_end = c + min(d, (qb + 1) * a.bmq);        // past the block's last position
@@ -953,7 +972,7 @@ __device__ __forceinline__ void chunk_tile(const AttnArgs& a, int32_t tile, char
   const T* q = static_cast<const T*>(a.q);
   const char* kc = static_cast<const char*>(a.k_cache);
   const char* vc = static_cast<const char*>(a.v_cache);
-  const int32_t* btab = a.block_table + a.cu_blocks[s];
+  const int32_t* btab = a.block_table + cub;
   const int bsh = a.bs_shift;
   const int32_t bmask = (1 << bsh) - 1;
 
@@ -1078,9 +1097,7 @@ __device__ __forceinline__ void chunk_tile(const AttnArgs& a, int32_t tile, char
     static_assert(NCPW * RPI == 8, "each wave copies 8 rows of a stage");
     if (n_st > 0) {
       const int32_t row_w = 8 * wave;
-      int32_t cub = sload_issue(a.cu_blocks + s);
-      sload_ready(cub);
-      const int32_t* bt = a.block_table + cub;
+      const int32_t* bt = btab;
       auto blk_ptr = [&](int32_t jj) { return bt + (min((kt_lo + jj) * kChunkKeys + row_w, k_last) >> bsh); };
       auto issue_s = [&](int32_t jj, int buf, int32_t blk) {
         const int32_t k0 = (kt_lo + jj) * kChunkKeys;
