@@ -52,6 +52,17 @@ class OracleRun:
         v = self.raw("v", rid, pos)
         return k, v
 
+    def expected_kv_rows(self, reqs: np.ndarray, pos: np.ndarray):
+        """(k^, v) in the storage type (as float32), [n, Hkv, D], for rows given by (request,
+        position) pairs, all at once."""
+        w = self.w
+        dt = TORCH_DTYPE[w.dtype]
+        rq = torch.as_tensor(np.asarray(reqs, dtype=np.int64), device=self.value_device)
+        ps = torch.as_tensor(np.asarray(pos, dtype=np.int64), device=self.value_device)
+        k = values.rows_values(w.seed, "k", rq, ps, w.Hkv, w.D, dt, self.value_device).float().cpu().numpy()
+        v = values.rows_values(w.seed, "v", rq, ps, w.Hkv, w.D, dt, self.value_device).float().cpu().numpy()
+        return orope.rotate_stored(k, np.asarray(pos), self.table, w.dtype), v
+
     def expected_rows(self, plan: dict, rows=None) -> dict:
         """fp64 attention for rows of a step (all rows if ``rows`` is None): {row: [Hq, D]}."""
         cu = plan["cu_seqlens_q"]

@@ -13,7 +13,7 @@ import torch
 from oracle import attention as oattn
 from oracle import rope as orope
 from synth import workloads
-from tests.harness import DeviceRun, OracleRun, bits_of, compare, plan_of_meta
+from tests.harness import DeviceRun, OracleRun, bits_of, cached_tokens, compare, plan_of_meta
 
 pytestmark = pytest.mark.gpu
 
@@ -56,6 +56,49 @@ def check_step_kv(gpu: DeviceRun, ora: OracleRun, plan, rows):
                 say(f"  {name} mismatch request {rid}: {len(bad)} of {got.size} elements; first at "
                     f"(row {i[0]} pos {pos[i[0]]}, head {i[1]}, dim {i[2]}): got {got[i]} want {want[i]}")
             assert not len(bad), f"{name} slots of request {rid}"
+
+
+def check_kv_rows(gpu: DeviceRun, ora: OracleRun, reqs, pos, slots, tag):
+    """K and V at ``slots`` equal the oracle's rotated keys and raw values of (reqs, pos), bit for
+    bit ("Chunked Prefill 的 Token 预算" §06: slot_mapping names where each token's K/V lands)."""
+    kw, vw = ora.expected_kv_rows(reqs, pos)
+    _, _, kb, vb = gpu.cache_rows(np.asarray(slots))
+    for name, got, want in (("K", kb, bits_of(kw, gpu.w.dtype)), ("V", vb, bits_of(vw, gpu.w.dtype))):
+        bad = np.argwhere(got != want)
+        if len(bad):
+            i = tuple(bad[0])
+            say(f"  {tag}: {name} mismatch at {len(bad)} of {got.size} elements; first at request "
+                f"{reqs[i[0]]} pos {pos[i[0]]}, head {i[1]}, dim {i[2]}: got {got[i]} want {want[i]}")
+        assert not len(bad), f"{tag}: {name} slots"
+
+
+def check_step_kv_all(gpu: DeviceRun, ora: OracleRun, plan, tag):
+    """Every slot the step wrote (all its rows) is bit-exact."""
+    T = plan["num_tokens"]
+    if T == 0:
+        return
+    cu = plan["cu_seqlens_q"]
+    reqs = np.repeat(np.array(plan["seq_ids"][:plan["num_seqs"]]), np.diff(np.array(cu[:plan["num_seqs"] + 1])))
+    check_kv_rows(gpu, ora, reqs, np.array(plan["positions"][:T]), np.array(plan["slot_mapping"][:T]), tag)
+
+
+def check_setup_sample(gpu: DeviceRun, ora: OracleRun, w, frac: float, seed: int):
+    """A seeded sample (at least ``frac`` of them, and the first and last of each request) of the
+    slots written at set-up (the cached contexts) is bit-exact."""
+    rng = np.random.default_rng(seed)
+    reqs, pos, slots = [], [], []
+    for rid, n in cached_tokens(w):
+        blocks = np.array(gpu.cb.cb_sched_get_blocks(gpu.sched, rid))
+        take = max(2, int(np.ceil(frac * n)))
+        p = np.unique(np.concatenate([[0, n - 1], rng.choice(n, size=min(n, take), replace=False)]))
+        reqs.append(np.full(len(p), rid))
+        pos.append(p)
+        slots.append(blocks[p // w.block_size] * w.block_size + p % w.block_size)
+    reqs, pos, slots = np.concatenate(reqs), np.concatenate(pos), np.concatenate(slots)
+    say(f"  set-up sample: {len(pos)} slots")
+    for a in range(0, len(pos), 1 << 16):
+        b = min(len(pos), a + (1 << 16))
+        check_kv_rows(gpu, ora, reqs[a:b], pos[a:b], slots[a:b], "set-up")
 
 
 def check_q_rot(gpu: DeviceRun, ora: OracleRun, plan, q_rot, rows):
@@ -134,7 +177,19 @@ def test_small_workload_every_row_every_step(dev, i):
 # ---------------------------------------------------------------------------------------------
 # Full-size workloads: sampled rows and slots at the benchmark's launch configuration.
 # ---------------------------------------------------------------------------------------------
-FULL_SAMPLE = {1: (8, 8, 1), 2: (8, 24, 1), 3: (8, 24, 1), 4: (4, 12, 4), 5: (16, 12, 1)}
+FULL_SAMPLE = {1: (8, 8, 1), 2: (8, 24, 1), 3: (8, 24, 1), 4: (4, 12, 1), 5: (None, None, 1)}
+
+
+def stratified_rows(plan, seed):
+    """All decode rows; of the chunk rows the first 64, the last 64 and 128 seeded random others."""
+    rng = np.random.default_rng(seed)
+    nd, T = plan["num_decodes"], plan["num_tokens"]
+    chunk = np.arange(nd, T)
+    rows = set(range(nd)) | set(chunk[:64].tolist()) | set(chunk[-64:].tolist())
+    rest = chunk[64:-64]
+    if len(rest):
+        rows |= set(rng.choice(rest, size=min(128, len(rest)), replace=False).tolist())
+    return rows
 
 
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
@@ -144,16 +199,17 @@ def test_full_workload_sampled(dev, cfg):
     say(f"[{w.name}] set-up: {len(w.decode_ctx)} decodes, {w.num_blocks} blocks")
     gpu = DeviceRun(w, dev)
     ora = OracleRun(w, value_device=dev)
+    check_setup_sample(gpu, ora, w, 0.01, seed=cfg)
     step = 0
     while (w.steps is None and ora.b.pending_prompts() > 0) or (w.steps is not None and step < w.steps):
         plan = ora.build()
         meta, out, q_rot = gpu.step()
         torch.cuda.synchronize()
         check_metadata(meta, plan)
+        check_step_kv_all(gpu, ora, plan, f"step {step}")
         if step % every == 0 or step == (w.steps or 0) - 1:
             say(f"[{w.name}] step {step}: T={plan['num_tokens']} nd={plan['num_decodes']}")
-            rows = sample_rows(plan, n_dec, n_chunk, seed=step)
-            check_step_kv(gpu, ora, plan, rows)
+            rows = stratified_rows(plan, seed=step) if n_dec is None else sample_rows(plan, n_dec, n_chunk, seed=step)
             check_q_rot(gpu, ora, plan, q_rot, rows)
             check_outputs(gpu, ora, plan, out, rows, f"step {step}")
         step += 1

@@ -40,7 +40,22 @@ def test_stream_draws_are_seeded_and_valid():
     assert [r.arrival for r in a] == sorted(r.arrival for r in a) and a[0].arrival >= 1
 
 
-def test_exercise_one_first_token_delay():
+def _run(impl, stream, budget, steps, **kw):
+    """(ttft, tbt, finished) of the product's simulator or of the oracle's."""
+    if impl == "product":
+        if kw.get("policy") == PREFILL_FIRST:
+            kw["policy"] = cb.CB_POLICY_PREFILL_FIRST
+        r = sim.simulate(stream, budget, steps, **kw)
+        return r.ttft, r.tbt, r.finished
+    r = osim.simulate(stream, budget, steps, **kw)
+    return r["ttft"], r["tbt"], r["finished"]
+
+
+IMPLS = ["oracle", "product"]
+
+
+@pytest.mark.parametrize("impl", IMPLS)
+def test_exercise_one_first_token_delay(impl):
     # "Chunked Prefill 的 Token 预算" §16, first exercise: budget 16, six decodes, prompts with 18 and
     # 5 tokens.  Decode-first (by hand): round 1 gives A 10; round 2 A 8 (done) and B 2; round 3
     # B 3 (done) -- the 5-token prompt waits three rounds behind the long one.  Prefill-first:
@@ -48,20 +63,49 @@ def test_exercise_one_first_token_delay():
     # so each decode's gap is two steps there.
     stream = [Request(1, 18, 0, 10 ** 6), Request(1, 5, 0, 10 ** 6)]
     running = [(20, 10 ** 6)] * 6
-    df = sim.simulate(stream, 16, 3, running=running)
-    assert df.ttft == {0: 2, 1: 3}
-    pf = sim.simulate(stream, 16, 2, running=running, policy=cb.CB_POLICY_PREFILL_FIRST)
-    assert pf.ttft == {0: 2, 1: 2}
-    assert pf.tbt == [2] * 6
+    ttft, _, _ = _run(impl, stream, 16, 3, running=running)
+    assert ttft == {0: 2, 1: 3}
+    ttft, tbt, _ = _run(impl, stream, 16, 2, running=running, policy=PREFILL_FIRST)
+    assert ttft == {0: 2, 1: 2}
+    assert tbt == [2] * 6
 
 
-def test_quota_ends_starvation_and_bounds_the_gap():
+@pytest.mark.parametrize("impl", IMPLS)
+def test_quota_ends_starvation_and_bounds_the_gap(impl):
     # §08 and §16 (third exercise): 16 decodes that never finish fill a budget of 16; decode-first
     # never gives the 40-token prompt a token; with a 25% quota it gets 4 per round (first token at
     # round 10) while 12 of the 16 decodes run each round, so no decode waits more than 2 steps.
     stream = [Request(1, 40, 0, 1)]
     running = [(10, 10 ** 6)] * 16
-    df = sim.simulate(stream, 16, 30, running=running)
-    assert df.ttft == {} and max(df.tbt) == 1
-    q = sim.simulate(stream, 16, 30, running=running, prefill_quota_pct=25)
-    assert q.ttft == {0: 10} and max(q.tbt) == 2 and q.finished == 1
+    ttft, tbt, _ = _run(impl, stream, 16, 30, running=running)
+    assert ttft == {} and max(tbt) == 1
+    ttft, tbt, finished = _run(impl, stream, 16, 30, running=running, prefill_quota_pct=25)
+    assert ttft == {0: 10} and max(tbt) == 2 and finished == 1
+
+
+@pytest.mark.parametrize("impl", IMPLS)
+def test_budget8_worked_example_as_a_simulation(impl):
+    # "Chunked Prefill 的 Token 预算" §03: budget 8, three running decodes, one 12-token prompt:
+    # chunks 5, 5, 2, so the prompt's first token comes from round 3 (TTFT 3 steps); every decode
+    # runs every round (gap 1).  A 2-token output finishes in round 4 (its one decode row).
+    stream = [Request(1, 12, 0, 2)]
+    running = [(16, 10 ** 6), (20, 10 ** 6), (24, 10 ** 6)]
+    ttft, tbt, finished = _run(impl, stream, 8, 4, running=running)
+    assert ttft == {0: 3}
+    assert finished == 1
+    # decode gaps: three decodes x 4 rounds, then the prompt's own decode in round 4 (gap 1 after
+    # its first token in round 3)
+    assert sorted(tbt) == [1] * 13
+
+
+@pytest.mark.parametrize("impl", IMPLS)
+def test_retired_request_frees_its_blocks(impl):
+    # A request that has produced all its tokens leaves the batch and its blocks return to the pool
+    # (the state the builder keeps between steps).  A 4-block pool (block size 8) holds one 24-token
+    # prompt plus its growth; the second prompt can only be admitted once the first has finished.
+    stream = [Request(1, 24, 0, 2), Request(1, 24, 0, 1)]
+    ttft, _, finished = _run(impl, stream, 64, 10, block_size=8, num_blocks=4)
+    assert ttft[0] == 1          # 24 tokens in round 1; first token then
+    # round 2: its one decode row (needs position 24 -> a 4th block) finishes it; round 3 the
+    # second prompt (3 blocks) is admitted and done at once.
+    assert ttft[1] == 3 and finished == 2
