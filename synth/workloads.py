@@ -33,6 +33,8 @@ class Workload:
     steps: int | None           # None: run until every prompt has had its last chunk
     seed: int
     max_steps: int = 64
+    arrivals: tuple = ()        # (step, prompt_len, cached_len): prompts joining the queue before
+                                # that step's build (0-based), after the ones listed in ``prompts``
 
     @property
     def group(self) -> int:
@@ -50,8 +52,13 @@ class Workload:
     def max_position(self) -> int:
         """An upper bound on any absolute position the run can touch."""
         s = self.max_steps if self.steps is None else self.steps
-        m = max([c + s for c in self.decode_ctx] + [L + s for L, _ in self.prompts] + [1])
+        m = max([c + s for c in self.decode_ctx] + [L + s for L, _ in self.prompts] +
+                [L + s for _, L, _ in self.arrivals] + [1])
         return m + 1
+
+    def arriving(self, step: int):
+        """(prompt_len, cached_len) of the prompts that join the queue before ``step``'s build."""
+        return [(L, c) for t, L, c in self.arrivals if t == step]
 
 
 def _pool_size(decode_ctx, prompts, bs, steps) -> int:
@@ -115,6 +122,23 @@ def config5() -> Workload:
 BUILDERS = {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}
 
 
+def stream_b512() -> Workload:
+    """Serving-like traffic on the budget-512 layer's geometry (32/32 heads, D 128, block 16): 64
+    decodes U{512..4096} and 16 prompts arriving over a 48-step cycle (exponential gaps of mean 2.5
+    steps, log-normal lengths of median 300, sigma 0.8, cap 1500, nothing cached), so the token
+    count and the decode count change from step to step."""
+    from synth.streams import mixed_stream
+    rng = np.random.Generator(np.random.PCG64(1012))
+    ctx = rng.integers(512, 4096, size=64, endpoint=True)
+    reqs = mixed_stream(1012, 16, mean_gap=2.5, median_prompt=300, sigma=0.8, max_prompt=1500)
+    arrivals = tuple((r.arrival - 1, r.prompt_len, 0) for r in reqs)
+    steps = 48
+    nb = _pool_size(ctx, [(L, 0) for _, L, _ in arrivals], 16, steps)
+    free = tuple(int(b) for b in rng.permutation(nb))
+    return Workload("stream_b512_bf16", "bf16", 32, 32, 128, 16, 512, tuple(int(c) for c in ctx), (), nb,
+                    free, steps, 1012, steps, arrivals)
+
+
 def get(i: int) -> Workload:
     return BUILDERS[i]()
 
@@ -148,6 +172,13 @@ def small(i: int) -> Workload:
     if i == 7:   # float32 at head dim 128
         ctx = rng.integers(20, 300, size=4, endpoint=True)
         return _make("small7_d128_f32", "f32", 4, 4, 128, 16, 160, ctx, ((400, 0),), 3, 2007, rng)
+    if i == 9:   # arrivals: 4 decodes, prompts joining at steps 0, 1, 3 and 4 (the token and
+        # decode counts change from step to step)
+        ctx = rng.integers(100, 600, size=4, endpoint=True)
+        nb = _pool_size(ctx, [(300, 0), (90, 0), (170, 40), (60, 0)], 16, 8)
+        return Workload("small9_arrivals_bf16", "bf16", 8, 2, 128, 16, 128, tuple(int(c) for c in ctx), (),
+                        nb, tuple(int(b) for b in rng.permutation(nb)), 8, 2009, 8,
+                        ((0, 300, 0), (1, 90, 0), (3, 170, 40), (4, 60, 0)))
     if i == 8:   # decode-heavy: 24 decodes U{1500..3000} x 16 heads, ~27K 32-key decode stages,
         # so the stage split spreads each unit over several waves and the combine merges several
         # partials per row and head
@@ -157,4 +188,4 @@ def small(i: int) -> Workload:
     raise KeyError(i)
 
 
-SMALL = (1, 2, 3, 4, 5, 6, 7, 8)
+SMALL = (1, 2, 3, 4, 5, 6, 7, 8, 9)

@@ -21,10 +21,11 @@ def cached_tokens(w: workloads.Workload):
 
 def step_caps(w: workloads.Workload, budget: int | None = None):
     """Capacities for one step's metadata arrays (for budgets up to ``budget``)."""
-    n_req = len(w.decode_ctx) + len(w.prompts)
+    prompts = list(w.prompts) + [(L, c) for _, L, c in w.arrivals]
+    n_req = len(w.decode_ctx) + len(prompts)
     tokens = max(w.budget, budget or 0)
     blocks = sum(-(-(c + (w.steps or w.max_steps) + 1) // w.block_size) for c in w.decode_ctx)
-    blocks += sum(-(-(L + (w.steps or w.max_steps) + 1) // w.block_size) for L, _ in w.prompts)
+    blocks += sum(-(-(L + (w.steps or w.max_steps) + 1) // w.block_size) for L, _ in prompts)
     return n_req, tokens, blocks
 
 
@@ -33,14 +34,14 @@ def step_caps(w: workloads.Workload, budget: int | None = None):
 # ---------------------------------------------------------------------------------------------
 class DeviceRun:
     def __init__(self, w: workloads.Workload, device="cuda", sentinel=True, populate=True,
-                 max_budget: int | None = None):
+                 max_budget: int | None = None, sched_cfg: dict | None = None):
         from chunked_prefill_mixed_decode_amd import binding as cb
         from chunked_prefill_mixed_decode_amd.runner import MixedStepRunner
         self.cb = cb
         self.w = w
         self.device = torch.device(device)
         self.dtype = TORCH_DTYPE[w.dtype]
-        self.sched = cb.cb_sched_create(w.block_size, w.num_blocks, w.free_list)
+        self.sched = cb.cb_sched_create(w.block_size, w.num_blocks, w.free_list, **(sched_cfg or {}))
         for c in w.decode_ctx:
             cb.cb_sched_add_running(self.sched, c)
         for L, cached in w.prompts:
@@ -51,8 +52,28 @@ class DeviceRun:
                                       max_pos=w.max_position(), cap_seqs=ns, cap_tokens=nt,
                                       cap_blocks=nb, sentinel=sentinel)
         self.written = 0                       # slots written so far
+        self.step_index = 0                    # steps run by step()
         if populate:
             self.populate()
+
+    def arrive(self, step: int, sched=None):
+        """Queue the prompts that arrive before ``step``'s build (into ``sched``, default this run's)
+        and write the K/V of their cached prefixes."""
+        sched = self.sched if sched is None else sched
+        for L, cached in self.w.arriving(step):
+            rid = self.cb.cb_sched_add_prompt(sched, L, cached)
+            if cached:
+                self._write_cached(rid, cached, sched)
+
+    def _write_cached(self, rid: int, n: int, sched):
+        w, bs = self.w, self.w.block_size
+        blocks = torch.tensor(self.cb.cb_sched_get_blocks(sched, rid), dtype=torch.int64, device=self.device)
+        pos = torch.arange(n, dtype=torch.int64, device=self.device)
+        slots = (blocks[pos // bs] * bs + pos % bs).to(torch.int32)
+        k = values.token_values(w.seed, "k", rid, pos, w.Hkv, w.D, self.dtype, self.device)
+        v = values.token_values(w.seed, "v", rid, pos, w.Hkv, w.D, self.dtype, self.device)
+        self.runner.append_rows(pos.to(torch.int32), slots, k, v)
+        self.written += n
 
     def populate(self, rows_per_batch: int = 1 << 16):
         """Write K/V of every token that is already cached at set-up into its slots."""
@@ -82,7 +103,9 @@ class DeviceRun:
         return q, k, v
 
     def step(self, budget=None, inputs=None):
-        """Build, copy, rope + append, attention.  Returns (meta, out [T, Hq, D], q_rot)."""
+        """Arrivals, build, copy, rope + append, attention.  Returns (meta, out [T, Hq, D], q_rot)."""
+        self.arrive(self.step_index)
+        self.step_index += 1
         meta = self.runner.build(self.sched, self.w.budget if budget is None else budget)
         dev = self.runner.upload(meta)
         q, k, v = self.step_inputs(meta) if inputs is None else inputs

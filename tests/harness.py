@@ -26,9 +26,9 @@ TOL = {"f32": (1e-4, 0.0), "bf16": (2e-2, 1e-2)}        # (atol, rtol)
 # Oracle side
 # ---------------------------------------------------------------------------------------------
 class OracleRun:
-    def __init__(self, w: workloads.Workload, value_device="cpu"):
+    def __init__(self, w: workloads.Workload, value_device="cpu", sched_cfg: dict | None = None):
         self.w = w
-        self.b = RefBuilder(w.block_size, w.num_blocks, w.free_list)
+        self.b = RefBuilder(w.block_size, w.num_blocks, w.free_list, **(sched_cfg or {}))
         for c in w.decode_ctx:
             self.b.add_running(c)
         for L, cached in w.prompts:
@@ -36,6 +36,7 @@ class OracleRun:
         self.table = orope.cos_sin_table(w.max_position(), w.D)
         self.scale = 1.0 / math.sqrt(w.D)
         self.value_device = value_device
+        self.build_index = 0
 
     def raw(self, tensor: str, rid: int, pos) -> np.ndarray:
         n_heads = self.w.Hq if tensor == "q" else self.w.Hkv
@@ -44,6 +45,9 @@ class OracleRun:
         return x.float().cpu().numpy()
 
     def build(self, budget=None) -> dict:
+        for L, cached in self.w.arriving(self.build_index):
+            self.b.add_prompt(L, cached)
+        self.build_index += 1
         return self.b.build(self.w.budget if budget is None else budget)
 
     def expected_kv(self, rid: int, pos: np.ndarray):

@@ -98,6 +98,26 @@ def test_builder_matches_oracle_over_full_runs(cfg):
         assert steps == 9
 
 
+@pytest.mark.parametrize("name", ["small9", "stream_b512"])
+def test_builder_matches_oracle_with_arrivals(name):
+    # Prompts joining the queue between steps (one with a cached prefix): the token and decode
+    # counts change from step to step.
+    w = workloads.small(9) if name == "small9" else workloads.stream_b512()
+    ref, s = _pair(w)
+    buf = cb.StepBuffers(*step_caps(w), pin=False)
+    counts = set()
+    for step in range(w.steps):
+        for L, cached in w.arriving(step):
+            assert ref.add_prompt(L, cached) == cb.cb_sched_add_prompt(s, L, cached)
+        plan = ref.build(w.budget)
+        meta = cb.cb_build_step(s, w.budget, buf)
+        _same_plan(plan, meta)
+        counts.add((plan["num_tokens"], plan["num_decodes"]))
+    assert len(counts) >= 4
+    for rid in range(len(w.decode_ctx) + len(w.arrivals)):
+        assert cb.cb_sched_get_blocks(s, rid) == ref.blocks_of(rid)
+
+
 def test_worked_example_metadata_rounds():
     # Derived from the budget-8 example of the zwjcode page, §03, with the identity free list.
     w = workloads.get(1)

@@ -1,16 +1,36 @@
-"""HIP-graph replay of whole steps (runner.StepGraphs) against the eager path, on the GPU.
+"""HIP-graph replay of whole steps (runner.StepGraphs) on the GPU, against the oracle and the
+eager path.
 
 Each step of a scaled-down workload's cycle runs eagerly, is then captured, and is replayed on
 later cycles (from the same builder snapshot, so every step recurs with identical launch
-parameters); every replay's attention output and rotated queries must equal the eager run's bit
-for bit, with eager torch work and host synchronisations between the replays, and the cache must
-hold the same bits afterwards.
+parameters); every replay's attention output must agree with the oracle's (fp64, non-chunked) at
+the parity bar and equal the eager run's bit for bit, its rotated queries likewise, with eager
+torch work and host synchronisations between the replays, and the cache must hold the same bits
+afterwards.
 """
+import numpy as np
 import pytest
 import torch
 
 from synth import workloads
 from tests.gpu_harness import DeviceRun
+from tests.harness import OracleRun, compare
+
+
+def oracle_cycle(w, dev, n):
+    """The oracle's outputs for every row of the cycle's first n steps: [T, Hq, D] per step."""
+    ora = OracleRun(w, value_device=dev)
+    outs = []
+    for _ in range(n):
+        plan = ora.build()
+        want = ora.expected_rows(plan)
+        outs.append(np.stack([want[r] for r in range(plan["num_tokens"])]))
+    return outs
+
+
+def check_oracle(got, want, dtype, tag):
+    ok, mabs, mrel = compare(got.float().cpu().numpy(), want, dtype)
+    assert ok, f"{tag}: max abs {mabs}, max rel {mrel}"
 
 pytestmark = pytest.mark.gpu
 
@@ -32,7 +52,7 @@ def _cycle_len(g, snap) -> int:
     return n
 
 
-@pytest.mark.parametrize("i", [2, 4])
+@pytest.mark.parametrize("i", [2, 4, 9])
 def test_graph_replay_equals_eager(dev, i):
     from chunked_prefill_mixed_decode_amd.runner import StepGraphs
     w = workloads.small(i)
@@ -53,6 +73,7 @@ def test_graph_replay_equals_eager(dev, i):
     ws = max(g.runner.workspace_bytes(m) for m in metas)
     g.runner.ensure_workspace(ws)
     kc, vc = g.runner.k_cache.clone(), g.runner.v_cache.clone()
+    want = oracle_cycle(w, dev, n)
     graphs = StepGraphs(g.runner)
     got_q = [torch.empty_like(q) for q in qrots]
     got_o = [torch.empty_like(o) for o in outs]
@@ -60,6 +81,7 @@ def test_graph_replay_equals_eager(dev, i):
     for cycle in range(3):
         g.sched = cb.cb_sched_clone(snap)
         for k in range(n):
+            g.arrive(k)
             meta = g.runner.build(g.sched, w.budget)
             q, kk, vv = inputs[k]
 
@@ -70,6 +92,7 @@ def test_graph_replay_equals_eager(dev, i):
             modes.append(graphs.step(meta, launch))
             torch.cuda.synchronize()
             _ = (got_o[k].float() * 2).sum().item()            # eager work between replays
+            check_oracle(got_o[k], want[k], w.dtype, f"cycle {cycle} step {k}")
             assert torch.equal(got_o[k].view(torch.int16), outs[k].view(torch.int16)), (cycle, k)
             assert torch.equal(got_q[k].view(torch.int16), qrots[k].view(torch.int16)), (cycle, k)
     assert "replay" in modes and modes.count("captured") == len(graphs.graphs)
@@ -77,7 +100,7 @@ def test_graph_replay_equals_eager(dev, i):
     assert torch.equal(g.runner.v_cache.view(torch.int16), vc.view(torch.int16))
 
 
-@pytest.mark.parametrize("i", [2, 4])
+@pytest.mark.parametrize("i", [2, 4, 9])
 def test_bucketed_graph_replay(dev, i):
     # Padded launch shapes (runner.Buckets): steps that round to the same shape share one graph
     # (and one set of row buffers of the padded length).  Rows [0, T) of every replay equal an
@@ -98,6 +121,7 @@ def test_bucketed_graph_replay(dev, i):
         ref.append(out.clone())
         exact.add(StepGraphs.key(meta)[1:])          # launch shape without the pinned buffer
     kc, vc = g.runner.k_cache.clone(), g.runner.v_cache.clone()
+    want = oracle_cycle(w, dev, n)
     b = Buckets(tokens=64, context=256)
     tol = dict(atol=2e-2, rtol=1e-2) if g.dtype == torch.bfloat16 else dict(atol=1e-4, rtol=0)
 
@@ -111,6 +135,7 @@ def test_bucketed_graph_replay(dev, i):
     g.sched = cb.cb_sched_clone(snap)
     padded, metas = [], []
     for k in range(n):
+        g.arrive(k)
         meta = padded_meta(g.sched)
         T, Tp = meta.num_tokens, meta.launch_tokens
         q, kk, vv = (torch.cat([x, x.new_zeros((Tp - T,) + x.shape[1:])]) for x in inputs[k])
@@ -129,6 +154,7 @@ def test_bucketed_graph_replay(dev, i):
     for cycle in range(3):
         g.sched = cb.cb_sched_clone(snap)
         for k in range(n):
+            g.arrive(k)
             meta = padded_meta(g.sched)
             T, Tp = meta.num_tokens, meta.launch_tokens
             key = StepGraphs.key(meta)
@@ -146,6 +172,7 @@ def test_bucketed_graph_replay(dev, i):
             modes.append(graphs.step(meta, launch))
             torch.cuda.synchronize()
             _ = (out[:T].float() * 2).sum().item()                  # eager work between replays
+            check_oracle(out[:T], want[k], w.dtype, f"bucketed cycle {cycle} step {k}")
             assert torch.equal(out[:T].view(torch.int16), padded[k].view(torch.int16)), (cycle, k)
     # One graph per (pinned buffer, padded shape); no more padded shapes than exact ones.
     shapes = {key[1:] for key in graphs.graphs}

@@ -449,3 +449,52 @@ def test_host_decode_plan_matches_device_split(dev, case):
                                         g.runner.workspace, decode_plan=dm["decode_plan"],
                                         plan_waves=meta.plan_waves + 4, **kw)
         assert e.value.status == cb.CB_ERR_INVALID
+
+
+# ---------------------------------------------------------------------------------------------
+# Builder policies and caps other than the default, through the kernels.
+# ---------------------------------------------------------------------------------------------
+POLICY_CASES = [
+    # "Splitting Prefill From Decode Inside a Step", "Choosing the priority order": prefill-first
+    # gives the prompts the whole budget; the decodes run only in what is left (here: not until
+    # the prompts are through, then all of them).
+    ("prefill_first", dict(policy=1), (900, 40, 2000, 333, 17), ((300, 0), (100, 60)), 128),
+    # the same paper's fair share: decodes get up to 30% of the budget, the prompts the rest
+    ("fair_share", dict(policy=2, decode_share_pct=30), (500, 70, 1200, 2048, 9, 64), ((400, 0), (90, 0)), 96),
+    # the sference post's proposed floor: each admitted prompt gets up to 24 tokens first, the rest
+    # is shared, so several prompts are partly prefilled in one step
+    ("prefill_floor", dict(prefill_floor=24, max_chunk=80), (300, 700), ((150, 0), (260, 100), (90, 0)), 160),
+    # "Chunked Prefill 的 Token 预算" §08/§16: a 25% prefill quota under decode-first, with more
+    # decodes than fit beside it, so some decodes wait
+    ("quota", dict(prefill_quota_pct=25), tuple(range(100, 3100, 100)), ((500, 0),), 32),
+]
+
+
+@pytest.mark.parametrize("case", POLICY_CASES, ids=[c[0] for c in POLICY_CASES])
+def test_policies_every_row_every_step(dev, case):
+    """Every row of every step and every written slot against the oracle builder run with the same
+    policy; steps with deferred decodes and with several partial prefills."""
+    from synth.workloads import _make
+    name, cfg, ctx, prompts, budget = case
+    w = _make(f"policy_{name}", "bf16", 16, 4, 128, 16, budget, ctx, prompts, 12, 3200 + len(name),
+              np.random.default_rng(len(name)))
+    gpu = DeviceRun(w, dev, sched_cfg=cfg)
+    ora = OracleRun(w, value_device=dev, sched_cfg=cfg)
+    seen_partial, seen_deferred = 0, 0
+    for step in range(w.steps):
+        plan = ora.build()
+        meta, out, q_rot = gpu.step()
+        torch.cuda.synchronize()
+        check_metadata(meta, plan)
+        n_prompts = plan["num_seqs"] - plan["num_decodes"]
+        seen_partial = max(seen_partial, n_prompts)
+        seen_deferred = max(seen_deferred, len(ctx) - plan["num_decodes"])
+        say(f"[{w.name}] step {step}: T={plan['num_tokens']} nd={plan['num_decodes']} prompts={n_prompts}")
+        if plan["num_tokens"] == 0:
+            continue
+        check_step_kv_all(gpu, ora, plan, f"step {step}")
+        check_outputs(gpu, ora, plan, out, None, f"step {step}")
+    if name in ("prefill_floor", "fair_share"):
+        assert seen_partial >= 2, "expected several prompts in one step"
+    if name in ("prefill_first", "quota"):
+        assert seen_deferred > 0, "expected deferred decodes"
