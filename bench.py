@@ -14,12 +14,15 @@ HBM before the timed region.
 
 Prints one JSON line.  ``roofline`` reports the dominant kernel (the attention kernel, whose decode
 waves stream the cache, bound by HBM): algorithmic bytes per launch (K and V of every decode
-context and of every chunk's visible keys, plus q and out) divided by its average duration
-measured with HIP events on the launch stream over the timed steps.  ``isolated`` times
-decode-only and chunk-only launches of the same metadata.
-``cpu_baseline`` times the CPU oracle (reference builder + fp64 full-prefill attention with
-rotary embedding) on the workload's steps in order, whole steps until ``--cpu-budget-s`` seconds
-of oracle time (default 25) have been spent.
+context and of every chunk's visible keys, plus q and out) divided by its average duration,
+measured with HIP events on the launch stream over every launch of a dedicated pass of whole
+cycles after the timed loop (at least 20 launches).  ``isolated`` times decode-only and
+chunk-only launches of the same metadata, warm and with L2 and MALL evicted by a read-only sweep.
+``graph_replay`` times the same steps replayed from HIP graphs (one per step shape, and with
+padded token buckets), on this workload and on a serving-like stream whose token count changes
+every step.  ``cpu_baseline`` times the CPU oracle (reference builder + rotary embedding + fp64
+full-prefill attention) on every step of the cycle: all decode rows and a fixed subset of each
+step's chunk rows, extrapolated to whole steps.
 """
 from __future__ import annotations
 
@@ -45,17 +48,18 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=2, help="workload index (default: the budget-512 layer)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget-s", type=float, default=25.0,
-                    help="oracle seconds the CPU baseline may spend (whole steps, at least one)")
     ap.add_argument("--json-out", default=None)
     ap.add_argument("--event-every", type=int, default=7,
                     help="record the per-kernel and per-step HIP events on every n-th timed step "
                          "(each event record costs the GPU a few microseconds; 7 is coprime with "
                          "the ten-step cycle, so every step kind is sampled)")
-    ap.add_argument("--graphs", action="store_true",
-                    help="also time the same steps replayed from HIP graphs (one graph per step of "
-                         "the cycle, captured on its first occurrence) and report it beside the "
-                         "eager figures")
+    ap.add_argument("--no-graphs", action="store_true",
+                    help="skip the HIP-graph legs (replays of the same steps, exact shapes and "
+                         "padded buckets, on this workload and on the serving-like stream)")
+    ap.add_argument("--cpu-chunk-rows", type=int, default=32,
+                    help="chunk rows per step the CPU baseline computes")
+    ap.add_argument("--cpu-decode-rows", type=int, default=16,
+                    help="decode rows per step the CPU baseline computes")
     ap.add_argument("--only", choices=("chunk", "decode"), default=None,
                     help="after the warm-up, run only isolated launches of one kind (chunk-only or "
                          "decode-only launches of every step's metadata, --reps each), print their "
@@ -117,8 +121,9 @@ def committed_traffic(kernel: str, workload: str):
 def isolation_pass(g, metas, qrots, outs, w, reps: int, flush=None, kinds=("decode", "chunk")):
     """Decode-only and chunk-only launches of each step's metadata, timed with HIP events on the
     launch stream: per-kernel durations without the other kernel running beside it.  Decode
-    launches report attention + combine time.  With ``flush`` (a device tensor), it is rewritten
-    before every launch so that L2 and the MALL hold none of the step's data (cold cache)."""
+    launches report attention + combine time.  With ``flush`` (a device tensor larger than L2 and
+    the MALL together), it is read in full (a sum) and the stream synchronised before every launch,
+    so that the caches hold none of the step's data and no dirty lines (cold cache)."""
     import torch
     cb = g.cb
     dec, chk = [], []
@@ -141,7 +146,8 @@ def isolation_pass(g, metas, qrots, outs, w, reps: int, flush=None, kinds=("deco
         for _ in range(reps):
             if nd > 0 and "decode" in kinds:
                 if flush is not None:
-                    flush.add_(1)
+                    flush.sum()
+                    torch.cuda.synchronize()
                 cb.cb_mixed_paged_attention(
                     qrots[k][:nd], g.runner.k_cache, g.runner.v_cache, dev["cu_seqlens_q"],
                     dev["context_lens"], dev["cu_blocks"], dev["block_table"], outs[k][:nd],
@@ -152,7 +158,8 @@ def isolation_pass(g, metas, qrots, outs, w, reps: int, flush=None, kinds=("deco
                 dec.append((k, ev[0].elapsed_time(ev[1]) + ev[4].elapsed_time(ev[5])))
             if T > nd and "chunk" in kinds:
                 if flush is not None:
-                    flush.add_(1)
+                    flush.sum()
+                    torch.cuda.synchronize()
                 cb.cb_mixed_paged_attention(
                     qrots[k][nd:], g.runner.k_cache, g.runner.v_cache, cu_chunk,
                     dev["context_lens"][nd:], dev["cu_blocks"][nd:], dev["block_table"], outs[k][nd:],
@@ -229,10 +236,14 @@ def summarize_isolated(dec, chk, metas, w, elt):
     return out
 
 
-def cpu_baseline(w, n_steps: int, budget_s: float):
-    """The oracle on the cycle's steps in order (Python reference builder, then fp64 attention with
-    the rotary embedding of all of a step's rows), until budget_s seconds of oracle time have been
-    spent (at least one step).  Each step's raw inputs are generated before its timed part."""
+def cpu_baseline(w, n_steps: int, chunk_rows: int, decode_rows: int):
+    """The oracle on every step of the cycle, in order: the Python reference builder, then for a
+    fixed subset of each step's rows (``decode_rows`` of the decode rows and ``chunk_rows`` of the
+    chunk rows: the first and last quarter of each kind, the rest seeded random) the rotary
+    embedding of the row's sequence's keys and of its query, and fp64 attention.  Each part is
+    timed; a step's oracle time is extrapolated to all of its rows (decode sequences by count,
+    chunk-row attention by rows; a chunk's keys are rotated in full either way).  Raw inputs are
+    generated before each step's timed part."""
     import numpy as np
 
     from oracle import attention as oattn
@@ -253,42 +264,215 @@ def cpu_baseline(w, n_steps: int, budget_s: float):
         b.add_prompt(L, cached)
     dt = TORCH_DTYPE[w.dtype]
     table = orope.cos_sin_table(w.max_position(), w.D)
-    rows = 0
-    el = 0.0
-    done = 0
+    scale = 1.0 / np.sqrt(w.D)
+    rng = np.random.default_rng(0)
+
+    def subset(rows, n):
+        rows = np.asarray(rows)
+        if len(rows) <= n:
+            return set(rows.tolist())
+        q = n // 4
+        out = set(rows[:q].tolist()) | set(rows[-q:].tolist())
+        return out | set(rng.choice(rows[q:-q], size=n - 2 * q, replace=False).tolist())
+
+    per_step, rows_done, tokens, est = [], 0, 0, 0.0
     for step in range(n_steps):
-        # inputs of the step (untimed): raw q/k/v of every sequence up to its last row
         probe = b.clone().build(w.budget)
-        raw = {}
+        nd, T = probe["num_decodes"], probe["num_tokens"]
         cu = probe["cu_seqlens_q"]
+        pick = subset(range(nd), decode_rows) | subset(range(nd, T), chunk_rows)
+        raw = {}
         for s in range(probe["num_seqs"]):
+            rows = [r for r in range(cu[s], cu[s + 1]) if r in pick]
+            if not rows:
+                continue
             rid = probe["seq_ids"][s]
+            pos = [probe["positions"][r] for r in rows]
             last = probe["context_lens"][s]
-            pos = list(range(probe["positions"][cu[s]], probe["positions"][cu[s + 1] - 1] + 1))
             raw[rid] = (values.range_values(w.seed, "k", rid, 0, last, w.Hkv, w.D, dt).float().numpy(),
                         values.range_values(w.seed, "v", rid, 0, last, w.Hkv, w.D, dt).float().numpy(),
-                        values.token_values(w.seed, "q", rid, pos, w.Hq, w.D, dt).float().numpy())
+                        values.token_values(w.seed, "q", rid, pos, w.Hq, w.D, dt).float().numpy(),
+                        np.array(pos))
         t0 = time.perf_counter()
         plan = b.build(w.budget)
-        cu = plan["cu_seqlens_q"]
+        t_build = time.perf_counter() - t0
+        t_dec = t_chk_rot = t_chk_att = 0.0
+        n_dec = n_chk = 0
         for s in range(plan["num_seqs"]):
             rid = plan["seq_ids"][s]
-            k, v, q = raw[rid]
-            pos = np.array(plan["positions"][cu[s]:cu[s + 1]])
+            if rid not in raw:
+                continue
+            k, v, q, pos = raw[rid]
+            t1 = time.perf_counter()
             kh = orope.rotate_stored(k, np.arange(k.shape[0]), table, w.dtype)
             qh = orope.rotate_stored(q, pos, table, w.dtype)
-            oattn.attend(qh, kh, v, pos, 1.0 / np.sqrt(w.D))
-            rows += len(pos)
-        el += time.perf_counter() - t0
-        done += 1
+            t2 = time.perf_counter()
+            oattn.attend(qh, kh, v, pos, scale)
+            t3 = time.perf_counter()
+            if s < nd:
+                t_dec += t3 - t1
+                n_dec += 1
+            else:
+                t_chk_rot += t2 - t1
+                t_chk_att += t3 - t2
+                n_chk += len(pos)
+        rows_done += n_dec + n_chk
+        full = (t_build + (t_dec * nd / n_dec if n_dec else 0.0) + t_chk_rot +
+                (t_chk_att * (T - nd) / n_chk if n_chk else 0.0))
+        est += full
+        tokens += T
+        per_step.append({"step": step, "tokens": T, "rows_computed": n_dec + n_chk,
+                         "seconds": t_build + t_dec + t_chk_rot + t_chk_att, "seconds_full_step": full})
         del raw
-        if el >= budget_s:
-            break
-    return {"value": rows / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "seconds": el,
-            "sample": f"steps 0-{done - 1} of the {n_steps}-step cycle ({rows} rows x {w.Hq} heads): "
-                      f"reference builder + rotary + fp64 causal attention (raw inputs pre-generated), "
-                      f"stopped after {budget_s:.0f} s of oracle time"}
+    measured = sum(p["seconds"] for p in per_step)
+    return {"value": tokens / est, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "seconds": measured, "per_step": per_step,
+            "sample": f"every step of the {n_steps}-step cycle: reference builder, then rotary embedding and "
+                      f"fp64 causal attention of {decode_rows} decode rows and {chunk_rows} chunk rows per step "
+                      f"(first and last quarter of each kind, the rest seeded random; {rows_done} rows x "
+                      f"{w.Hq} heads in {measured:.1f} s); value = the cycle's tokens over the oracle time "
+                      f"extrapolated to every row of every step ({est:.1f} s)"}
+
+
+def graph_legs(g, w, snap, inputs, cycle: int, steps: int, arrivals: bool = False):
+    """The cycle's steps eagerly, replayed from one HIP graph per step shape (runner.StepGraphs,
+    captured on first occurrence), and replayed from one graph per padded shape (runner.Buckets:
+    token count and longest query to a multiple of 64, longest contexts to a multiple of 4096,
+    padding rows skipped by the append).  ``steps`` timed steps each; host wall time with a device
+    sync on both sides.  Row buffers of a padded shape keep the inputs of the first step that used
+    it (timing only)."""
+    import torch
+
+    from chunked_prefill_mixed_decode_amd.runner import Buckets, StepGraphs
+    cb = g.cb
+    r = g.runner
+    bk = Buckets(tokens=64, context=4096)
+    st = {"sched": cb.cb_sched_clone(snap), "k": 0}
+
+    def restart():
+        st["sched"], st["k"] = cb.cb_sched_clone(snap), 0
+
+    def build(buckets=None):
+        k = st["k"]
+        if arrivals:
+            g.arrive(k, st["sched"])
+        return k, r.build(st["sched"], w.budget, buckets=buckets)
+
+    def advance():
+        st["k"] += 1
+        if st["k"] == cycle:
+            restart()
+
+    # Workspace for every exact and padded shape of the cycle (a reallocation drops the graphs).
+    need = 0
+    for buckets in (None, bk):
+        restart()
+        for _ in range(cycle):
+            _, meta = build(buckets)
+            need = max(need, r.workspace_bytes(meta))
+            advance()
+    r.ensure_workspace(need)
+    q_rot = [torch.empty_like(x[0]) for x in inputs]
+    out = [torch.empty_like(x[0]) for x in inputs]
+
+    def timed(step_fn):
+        restart()
+        for _ in range(2 * cycle):             # warm-up; captures every shape (both pinned buffers)
+            step_fn(False)
+        torch.cuda.synchronize()
+        restart()
+        tok = 0
+        t1 = time.perf_counter()
+        for _ in range(steps):
+            tok += step_fn(True)
+        torch.cuda.synchronize()
+        return tok, time.perf_counter() - t1
+
+    def eager(count):
+        k, meta = build()
+        dm = r.upload(meta)
+        q, kk, vv = inputs[k]
+        r.append(dm, q, kk, vv, q_rot[k])
+        r.attend(meta, dm, q_rot[k], out[k])
+        advance()
+        return meta.num_tokens
+
+    graphs, modes = StepGraphs(r), set()
+
+    def replay(count):
+        k, meta = build()
+        q, kk, vv = inputs[k]
+
+        def launch(dm):
+            r.append(dm, q, kk, vv, q_rot[k])
+            r.attend(meta, dm, q_rot[k], out[k])
+        m = graphs.step(meta, launch)
+        if count:
+            modes.add(m)
+        advance()
+        return meta.num_tokens
+
+    bgraphs, bmodes, rows, pad = StepGraphs(r), set(), {}, {"rows": 0, "real": 0}
+
+    def bucketed(count):
+        k, meta = build(bk)
+        key = StepGraphs.key(meta)
+        if key not in rows:
+            T, Tp = meta.num_tokens, meta.launch_tokens
+            rows[key] = [torch.cat([x, x.new_zeros((Tp - T,) + x.shape[1:])]) for x in inputs[k]]
+            rows[key] += [torch.empty_like(rows[key][0]), torch.empty_like(rows[key][0])]
+        q, kk, vv, qr, o = rows[key]
+
+        def launch(dm):
+            r.append(dm, q, kk, vv, qr)
+            r.attend(meta, dm, qr, o)
+        m = bgraphs.step(meta, launch)
+        if count:
+            bmodes.add(m)
+            pad["rows"] += meta.launch_tokens
+            pad["real"] += meta.num_tokens
+        advance()
+        return meta.num_tokens
+
+    etok, eel = timed(eager)
+    gtok, gel = timed(replay)
+    btok, bel = timed(bucketed)
+    restart()
+    return {
+        "workload": w.name, "steps": steps, "cycle": cycle,
+        "eager_ms_per_step": eel / steps * 1e3, "eager_tokens_per_s": etok / eel,
+        "ms_per_step": gel / steps * 1e3, "value": gtok / gel, "unit": "tokens/s",
+        "graphs": len(graphs.graphs), "all_replayed": modes == {"replay"},
+        "bucketed": {"ms_per_step": bel / steps * 1e3, "value": btok / bel, "unit": "tokens/s",
+                     "graphs": len(bgraphs.graphs), "all_replayed": bmodes == {"replay"},
+                     "token_bucket": bk.tokens, "context_bucket": bk.context,
+                     "padded_rows_frac": pad["rows"] / max(1, pad["real"]) - 1.0,
+                     "us_saved_per_step_vs_eager": (eel - bel) / steps * 1e6},
+        "us_saved_per_step_vs_eager": (eel - gel) / steps * 1e6,
+        "note": "the cycle's steps eager, replayed from one HIP graph per exact step shape (and pinned "
+                "buffer), and from one graph per padded shape; host wall time per step"}
+
+
+def stream_graph_leg(dev, steps: int):
+    """graph_legs on the serving-like stream (synth.workloads.stream_b512): the budget-512 layer's
+    geometry with 64 decodes and prompts arriving over a 48-step cycle, so the token count (64 to
+    512) and the decode count change from step to step and padding really occurs."""
+    from synth import workloads
+    from tests.gpu_harness import DeviceRun
+    w = workloads.stream_b512()
+    g = DeviceRun(w, dev, sentinel=False)
+    cb = g.cb
+    snap = cb.cb_sched_clone(g.sched)
+    probe = cb.cb_sched_clone(snap)
+    bufs = cb.StepBuffers(*g.runner.bufs[0].cap)
+    inputs = []
+    for k in range(w.steps):
+        g.arrive(k, probe)
+        meta = cb.cb_build_step(probe, w.budget, bufs)
+        inputs.append(g.step_inputs(meta))
+    res = graph_legs(g, w, snap, inputs, w.steps, max(steps, 2 * w.steps), arrivals=True)
+    res["tokens_per_step_range"] = [min(x[0].shape[0] for x in inputs), max(x[0].shape[0] for x in inputs)]
+    return res
 
 
 def main():
@@ -408,106 +592,34 @@ def main():
     el = time.perf_counter() - t0
 
     dev_step_ms = [e8[6].elapsed_time(e8[7]) for e8 in evs.values()]
-    dec_ms, cmb_ms = [], []
-    for e8 in evs.values():
-        dec_ms.append(e8[0].elapsed_time(e8[1]))      # the attention kernel (events 2, 3: the same)
-        cmb_ms.append(e8[4].elapsed_time(e8[5]))
     elt = 2
-    abytes = [decode_bytes(metas[step_ids[i]], w, elt) + chunk_bytes(metas[step_ids[i]], w, elt) for i in sampled]
+
+    # Roofline pass: whole cycles (at least 20 steps) with HIP events around every attention
+    # launch and its combine, after the timed loop, so the timed figures carry no extra records.
+    n_ev = cb_steps * max(2, -(-20 // cb_steps))
+    ev_pass = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(n_ev)]
+    for e6 in ev_pass:
+        for e in e6:
+            e.record()
+    torch.cuda.synchronize()
+    state["sched"], state["k"] = cb.cb_sched_clone(snapshot), 0
+    ev_steps = []
+    for e6 in ev_pass:
+        _, k = one_step(e6)
+        ev_steps.append(k)
+    torch.cuda.synchronize()
+    dec_ms = [e6[0].elapsed_time(e6[1]) for e6 in ev_pass]      # the attention kernel
+    cmb_ms = [e6[4].elapsed_time(e6[5]) for e6 in ev_pass]
+    abytes = [decode_bytes(metas[k], w, elt) + chunk_bytes(metas[k], w, elt) for k in ev_steps]
     attn_avg_s = sum(dec_ms) / len(dec_ms) / 1e3
     achieved = sum(abytes) / len(abytes) / attn_avg_s / 1e9
+    state["sched"], state["k"] = cb.cb_sched_clone(snapshot), 0
 
     graph_rep = None
-    if args.graphs:
-        from chunked_prefill_mixed_decode_amd.runner import StepGraphs
-        graphs = StepGraphs(g.runner)
-        state["sched"], state["k"] = cb.cb_sched_clone(snapshot), 0
-
-        def graph_step():
-            k = state["k"]
-            meta = g.runner.build(state["sched"], w.budget)
-            q, kk, vv = inputs[k]
-
-            def launch(dev_meta):
-                g.runner.append(dev_meta, q, kk, vv, qrots[k])
-                g.runner.attend(meta, dev_meta, qrots[k], outs[k])
-            mode = graphs.step(meta, launch)
-            state["k"] = k + 1
-            if state["k"] == cb_steps:
-                state["k"] = 0
-                state["sched"] = cb.cb_sched_clone(snapshot)
-            return meta.num_tokens, mode
-        for _ in range(2 * cb_steps):                  # capture every step of the cycle
-            graph_step()
-        torch.cuda.synchronize()
-        gtok, modes = 0, set()
-        t1 = time.perf_counter()
-        for _ in range(args.steps):
-            n, mode = graph_step()
-            gtok += n
-            modes.add(mode)
-        torch.cuda.synchronize()
-        gel = time.perf_counter() - t1
-        graph_rep = {"value": gtok / gel, "unit": "tokens/s", "ms_per_step": gel / args.steps * 1e3,
-                     "eager_ms_per_step": el / args.steps * 1e3, "graphs": len(graphs.graphs),
-                     "all_replayed": modes == {"replay"},
-                     "note": "the same steps replayed from one HIP graph per step of the cycle"}
-        state["sched"], state["k"] = cb.cb_sched_clone(snapshot), 0
-
-        # Padded token buckets: launch shapes rounded up (runner.Buckets), one graph per padded
-        # shape, row buffers of the padded length per graph.  Timing only: a shape's buffers keep
-        # the inputs of the first step that used it.
-        from chunked_prefill_mixed_decode_amd.runner import Buckets
-        bk = Buckets(tokens=64, context=4096)
-        bgraphs, rows = StepGraphs(g.runner), {}
-        bmetas = []
-        for k in range(cb_steps):
-            bmetas.append(g.runner.build(state["sched"], w.budget, buckets=bk))
-        g.runner.ensure_workspace(max(g.runner.workspace_bytes(m) for m in bmetas))
-        state["sched"], state["k"] = cb.cb_sched_clone(snapshot), 0
-        pad = {"rows": 0, "real": 0}
-
-        def bucket_step(count=False):
-            k = state["k"]
-            meta = g.runner.build(state["sched"], w.budget, buckets=bk)
-            key = StepGraphs.key(meta)
-            if key not in rows:
-                T, Tp = meta.num_tokens, meta.launch_tokens
-                src = inputs[k]
-                rows[key] = [torch.cat([x, x.new_zeros((Tp - T,) + x.shape[1:])]) for x in src]
-                rows[key] += [torch.empty_like(rows[key][0]), torch.empty_like(rows[key][0])]
-            q, kk, vv, q_rot, out = rows[key]
-
-            def launch(dev_meta):
-                g.runner.append(dev_meta, q, kk, vv, q_rot)
-                g.runner.attend(meta, dev_meta, q_rot, out)
-            mode = bgraphs.step(meta, launch)
-            if count:
-                pad["rows"] += meta.launch_tokens
-                pad["real"] += meta.num_tokens
-            state["k"] = k + 1
-            if state["k"] == cb_steps:
-                state["k"] = 0
-                state["sched"] = cb.cb_sched_clone(snapshot)
-            return meta.num_tokens, mode
-        for _ in range(2 * cb_steps):
-            bucket_step()
-        torch.cuda.synchronize()
-        btok, bmodes = 0, set()
-        t1 = time.perf_counter()
-        for _ in range(args.steps):
-            n, mode = bucket_step(count=True)
-            btok += n
-            bmodes.add(mode)
-        torch.cuda.synchronize()
-        bel = time.perf_counter() - t1
-        graph_rep["bucketed"] = {
-            "value": btok / bel, "unit": "tokens/s", "ms_per_step": bel / args.steps * 1e3,
-            "graphs": len(bgraphs.graphs), "all_replayed": bmodes == {"replay"},
-            "token_bucket": bk.tokens, "context_bucket": bk.context,
-            "padded_rows_frac": pad["rows"] / pad["real"] - 1.0,
-            "note": "one HIP graph per padded launch shape (token count to a multiple of 64, "
-                    "longest query likewise, longest contexts to a multiple of 4096)"}
+    if not args.no_graphs:
+        print("[bench] graph replay legs...", file=sys.stderr, flush=True)
+        graph_rep = graph_legs(g, w, snapshot, inputs, cb_steps, args.steps)
+        graph_rep["varying"] = stream_graph_leg(dev, args.steps)
         state["sched"], state["k"] = cb.cb_sched_clone(snapshot), 0
 
     # End-to-end latency: host wall time from cb_build_step to stream sync after attention.
@@ -523,9 +635,11 @@ def main():
     dec_raw, chk_raw = isolation_pass(g, metas, qrots, outs, w, reps=3)
     iso = summarize_isolated(dec_raw, chk_raw, metas, w, elt)
     iso["note"] = "decode-only and chunk-only launches of the same step metadata, 3 reps per step"
-    flush = torch.zeros(128 << 20, dtype=torch.int32, device=dev)   # 512 MiB: L2 and MALL
+    flush = torch.ones(256 << 20, dtype=torch.int32, device=dev)    # 1 GiB, written once here
+    torch.cuda.synchronize()
     iso_cold = summarize_isolated(*isolation_pass(g, metas, qrots, outs, w, reps=2, flush=flush), metas, w, elt)
-    iso_cold["note"] = "as isolated, with a 512 MiB device write before every launch (L2 and MALL cold)"
+    iso_cold["note"] = ("as isolated, after a read-only sweep of 1 GiB and a synchronisation before every "
+                        "launch (L2 and MALL hold none of the step's data and no dirty lines)")
     del flush
     traffic = committed_traffic("attn_kernel", w.name)
     # What the chunk rows add to a mixed step: the in-step attention + combine minus the warm
@@ -534,10 +648,9 @@ def main():
     for k, t in dec_raw:
         iso_dec.setdefault(k, []).append(t)
     marg, mflops = [], []
-    for i, e8 in evs.items():
-        k = step_ids[i]
+    for e6, k in zip(ev_pass, ev_steps):
         if k in iso_dec and chunk_flops(metas[k], w) > 0:
-            marg.append(e8[0].elapsed_time(e8[1]) + e8[4].elapsed_time(e8[5]) - sum(iso_dec[k]) / len(iso_dec[k]))
+            marg.append(e6[0].elapsed_time(e6[1]) + e6[4].elapsed_time(e6[5]) - sum(iso_dec[k]) / len(iso_dec[k]))
             mflops.append(chunk_flops(metas[k], w))
     chunk_marginal = None
     if marg:
@@ -573,7 +686,8 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "attn_kernel (decode waves + chunk tiles, one launch)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "bytes_per_launch": sum(abytes) / len(abytes), "avg_launch_us": attn_avg_s * 1e6},
+                     "bytes_per_launch": sum(abytes) / len(abytes), "avg_launch_us": attn_avg_s * 1e6,
+                     "launches_timed": len(dec_ms)},
         "isolated": iso,
         "isolated_cold": iso_cold,
         "chunk_marginal": chunk_marginal,
@@ -583,11 +697,12 @@ def main():
         "device_step_us_p10_p50_p90": [pct(dev_step_ms, q) * 1e3 for q in (0.1, 0.5, 0.9)],
         "end_to_end_ms_p10_p50_p90": [pct(e2e, q) for q in (0.1, 0.5, 0.9)],
         "event_sampled_steps": len(sampled),
+        "roofline_pass_launches": len(dec_ms),
         "graph_replay": graph_rep,
     }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)...", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(w, cb_steps, args.cpu_budget_s)
+        res["cpu_baseline"] = cpu_baseline(w, cb_steps, args.cpu_chunk_rows, args.cpu_decode_rows)
     line = json.dumps(res)
     print(line, flush=True)
     if args.json_out:
