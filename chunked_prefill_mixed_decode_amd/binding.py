@@ -75,6 +75,9 @@ EXPORTS = {
     "cb_mixed_paged_attention": (ctypes.c_int, [_vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                                 _i32, _i32, _i32, _i32, _f32, _vp, _vp, _vp, _vp,
                                                 _vp, _vp, _vp, _vp, _vp, _sz]),
+    "cb_mixed_paged_attention_noalloc": (ctypes.c_int, [_vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                                        _i32, _i32, _i32, _i32, _f32, _vp, _vp, _vp,
+                                                        _vp, _vp, _vp, _vp, _vp]),
     "cb_mixed_paged_attention_timed": (ctypes.c_int, [_vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                                       _i32, _i32, _i32, _i32, _i32, _f32, _vp,
                                                       _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
@@ -391,3 +394,15 @@ def cb_mixed_paged_attention(q, k_cache, v_cache, cu_seqlens_q, context_lens, cu
             ev = (_vp * 6)(*[ctypes.c_void_p(e.cuda_event) if e is not None else None for e in events])
         _check(_lib().cb_mixed_paged_attention_timed(*args, _ptr(decode_plan), plan_waves, ev),
                "cb_mixed_paged_attention_timed")
+
+
+def cb_mixed_paged_attention_noalloc(q, k_cache, v_cache, cu_seqlens_q, context_lens, cu_blocks,
+                                     block_table, out, *, num_seqs, num_decodes, max_q_len,
+                                     max_decode_ctx, max_ctx, scale, stream=None):
+    """cb_mixed_paged_attention without a workspace (the library's per-GPU scratch array)."""
+    T, Hq, D = q.shape
+    _, Hkv, bs, _ = k_cache.shape
+    _check(_lib().cb_mixed_paged_attention_noalloc(
+        _stream(q, stream), dtype_code(q.dtype), num_seqs, num_decodes, T, max_q_len, max_decode_ctx,
+        max_ctx, Hq, Hkv, D, bs, scale, _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cu_seqlens_q),
+        _ptr(context_lens), _ptr(cu_blocks), _ptr(block_table), _ptr(out)), "cb_mixed_paged_attention_noalloc")

@@ -24,6 +24,7 @@
 // Softmax runs in base 2: weights are 2^(s c - m) with c = scale * log2(e) and m the running
 // maximum of s c.
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "cb.h"
@@ -1761,4 +1762,61 @@ extern "C" int cb_mixed_paged_attention(
                                         k_cache, v_cache, cu_seqlens_q, context_lens, cu_blocks,
                                         block_table, out, workspace, workspace_bytes, nullptr, 0,
                                         nullptr);
+}
+
+// ---------------------------------------------------------------------------------------------
+// The same call for callers that cannot allocate (graph capture, tight serving loops): its
+// workspace is a file-scope device array of kScratchBytes.  Each GPU holds its own copy at its own
+// address, found once per device with hipGetSymbolAddress (with that device current) and kept;
+// host code passes only that address, never the array's name.  Nothing in it must start at zero:
+// every word the kernels read is written earlier in the same call.  Calls that overlap in time on
+// one GPU share the array and race.
+// ---------------------------------------------------------------------------------------------
+namespace cb {
+namespace {
+constexpr size_t kScratchBytes = static_cast<size_t>(64) << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) char scratch[kScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices] = {};
+
+int scratch_address(hipStream_t st, void** addr) {
+  int dev = -1;
+  if (hipStreamGetDevice(st, &dev) != hipSuccess && hipGetDevice(&dev) != hipSuccess) return CB_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return CB_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_addr[dev] == nullptr) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return CB_ERR_HIP;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return CB_ERR_HIP;
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (cur != dev && hipSetDevice(cur) != hipSuccess) return CB_ERR_HIP;
+    if (e != hipSuccess || ptr == nullptr) return CB_ERR_HIP;
+    g_scratch_addr[dev] = ptr;
+  }
+  *addr = g_scratch_addr[dev];
+  return CB_OK;
+}
+}  // namespace
+}  // namespace cb
+
+extern "C" int cb_mixed_paged_attention_noalloc(
+    void* stream, int32_t dtype, int32_t num_seqs, int32_t num_decodes, int32_t T,
+    int32_t max_q_len, int32_t max_decode_ctx, int32_t max_ctx, int32_t Hq, int32_t Hkv,
+    int32_t D, int32_t block_size, float scale, const void* q, const void* k_cache,
+    const void* v_cache, const int32_t* cu_seqlens_q, const int32_t* context_lens,
+    const int32_t* cu_blocks, const int32_t* block_table, void* out) {
+  using namespace cb;
+  if (!valid_shape(num_seqs, num_decodes, T, max_q_len, max_decode_ctx, max_ctx, Hq, Hkv, D))
+    return CB_ERR_INVALID;
+  if (make_plan(num_seqs, num_decodes, T, max_q_len, max_ctx, Hq, Hkv, D).total > kScratchBytes)
+    return CB_ERR_CAPACITY;
+  void* ws = nullptr;
+  const int rc = scratch_address(static_cast<hipStream_t>(stream), &ws);
+  if (rc != CB_OK) return rc;
+  return cb_mixed_paged_attention(stream, dtype, num_seqs, num_decodes, T, max_q_len, max_decode_ctx,
+                                  max_ctx, Hq, Hkv, D, block_size, scale, q, k_cache, v_cache,
+                                  cu_seqlens_q, context_lens, cu_blocks, block_table, out, ws,
+                                  kScratchBytes);
 }

@@ -316,6 +316,27 @@ int cb_mixed_paged_attention_timed(void* stream, int32_t dtype, int32_t num_seqs
                                    const int32_t* decode_plan, int32_t plan_waves,
                                    void* const* events);
 
+/* cb_mixed_paged_attention for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same arguments and result,
+ * without a workspace argument.  The workspace is a device array inside the library of
+ * CB_ATTN_NOALLOC_SCRATCH_BYTES (64 MiB) per GPU, held until the process ends; calls whose
+ * cb_attn_workspace_bytes(...) exceeds it return CB_ERR_CAPACITY (every workload here needs at
+ * most ~44 MiB).  The call allocates nothing and makes no allocating library call; the first call
+ * on a device looks the array's address up once (hipGetSymbolAddress, with that device made
+ * current for the lookup).  Every call on one GPU shares the array: calls that overlap in time on
+ * the same GPU (different streams, or other host threads) race and must be serialised by the
+ * caller.  Errors: CB_ERR_INVALID on bad shapes or pointers (as cb_mixed_paged_attention),
+ * CB_ERR_CAPACITY as above, CB_ERR_HIP if the address lookup or a launch fails. */
+#define CB_ATTN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int cb_mixed_paged_attention_noalloc(void* stream, int32_t dtype, int32_t num_seqs,
+                                     int32_t num_decodes, int32_t T, int32_t max_q_len,
+                                     int32_t max_decode_ctx, int32_t max_ctx, int32_t Hq,
+                                     int32_t Hkv, int32_t D, int32_t block_size, float scale,
+                                     const void* q, const void* k_cache, const void* v_cache,
+                                     const int32_t* cu_seqlens_q, const int32_t* context_lens,
+                                     const int32_t* cu_blocks, const int32_t* block_table,
+                                     void* out);
+
 #ifdef __cplusplus
 }
 #endif
