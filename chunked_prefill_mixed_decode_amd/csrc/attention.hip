@@ -24,6 +24,7 @@
 // Softmax runs in base 2: weights are 2^(s c - m) with c = scale * log2(e) and m the running
 // maximum of s c.
 #include <algorithm>
+#include <atomic>
 #include <mutex>
 #include <type_traits>
 
@@ -305,29 +306,12 @@ __device__ __forceinline__ Frag<float> lds_vt_frag16<float>(const char* base, in
 
 // The V^T operand of a 32x32x16 step over keys [16 ps, 16 ps + 16) of a stage: lane l gets
 // dimension 32 mt + l % 32 of the keys in slot order 8 (l / 32) + jj <-> key
-// 16 ps + 8 (jj / 4) + 4 (l / 32) + jj % 4 (the key order of the S^T accumulator).
+// 16 ps + 8 (jj / 4) + 4 (l / 32) + jj % 4 (the key order of the S^T accumulator).  bf16: two
+// ds_read_b64_tr_b16 (VRegs below), lane 16 grp + 4 j + qd addressing row
+// 16 ps + 8 h + 4 (grp / 2) + j at dimensions 32 mt + 16 (grp % 2) + 4 qd .. + 3 for h = 0, 1;
+// float: eight 4-byte reads.
 template <typename T>
 __device__ __forceinline__ Frag<T> lds_vt_frag32(const char* base, int mt, int ps, int lane, int row_bytes);
-template <>
-__device__ __forceinline__ Frag<bf16_t> lds_vt_frag32<bf16_t>(const char* base, int mt, int ps, int lane, int row_bytes) {
-  typedef __attribute__((ext_vector_type(4))) short s4;
-  Frag<bf16_t> f;
-  const int grp = lane >> 4, i = lane & 15;
-  const int j = i >> 2, qd = i & 3;
-  const int e = 32 * mt + 16 * (grp & 1) + 4 * qd;
-  uint32_t w[4];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int r = 16 * ps + 8 * h + 4 * (grp >> 1) + j;
-    const char* addr = base + r * row_bytes + 16 * lds_chunk((2 * e) >> 4, r, row_bytes) + ((2 * e) & 15);
-    const s4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (s4 __attribute__((address_space(3)))*)(const_cast<char*>(addr)));
-    w[2 * h] = static_cast<uint16_t>(v[0]) | (static_cast<uint32_t>(static_cast<uint16_t>(v[1])) << 16);
-    w[2 * h + 1] = static_cast<uint16_t>(v[2]) | (static_cast<uint32_t>(static_cast<uint16_t>(v[3])) << 16);
-  }
-  f.u = make_uint4(w[0], w[1], w[2], w[3]);
-  return f;
-}
 template <>
 __device__ __forceinline__ Frag<float> lds_vt_frag32<float>(const char* base, int mt, int ps, int lane, int row_bytes) {
   Frag<float> f;
@@ -340,11 +324,6 @@ __device__ __forceinline__ Frag<float> lds_vt_frag32<float>(const char* base, in
   return f;
 }
 
-// Wait until this wave's LDS copies have landed (s_waitcnt vmcnt(0); lgkmcnt, expcnt untouched).
-// Other waves' copies are visible after the workgroup barrier that follows.
-__device__ __forceinline__ void lds_copies_done() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-
-
 // Wait until at most N of this wave's vector-memory operations are outstanding (memory returns
 // in issue order, so every older LDS copy has landed), then the workgroup barrier.
 template <int N>
@@ -354,8 +333,8 @@ __device__ __forceinline__ void wait_vm_barrier() {
 
 // The operands of one 32-key chunk stage (bf16): K rows (KS ds_read_b128) and V^T (two
 // ds_read_b64_tr_b16 per 32x16 piece, the second 16 keys further down).  ka[ks] / va[2 mt + h]
-// are the LDS addresses lds_row_frag / lds_vt_frag32 would read in ring buffer 0 (piece ps = 0);
-// OFF selects the ring buffer (an immediate offset), and ps = 1 is 16 rows further.
+// are the LDS addresses lds_row_frag and the V^T layout above read in ring buffer 0 (piece
+// ps = 0); OFF selects the ring buffer (an immediate offset), and ps = 1 is 16 rows further.
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 // Two asm blocks issue them without waiting: K rows (KRegs) and V^T (VRegs), in the ring buffer
@@ -955,7 +934,7 @@ __device__ __forceinline__ void chunk_tile(const AttnArgs& a, int32_t tile, char
   sload_ready(m_ctx);
   sload_ready(cub);
   if (!chunk_tile_rows(tg, m_q0, m_q1, m_ctx, ts)) return;
-  const int32_t sp = ts.sp, qb = ts.qb, g = ts.g, s = ts.s, row0 = ts.row0, d = ts.d, c = ts.c;
+  const int32_t sp = ts.sp, qb = ts.qb, g = ts.g, row0 = ts.row0, d = ts.d, c = ts.c;
   const int32_t kt_lo = ts.kt_lo, kt_hi = ts.kt_hi;
   const int32_t kv_end = c + min(d, (qb + 1) * a.bmq);        // past the block's last position
 
@@ -1508,16 +1487,16 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a, int32_t n_dec_
 
 // Compute units of the device that owns the stream (cached per device).
 int compute_units(hipStream_t st) {
-  static int cached[64] = {0};
+  static std::atomic<int> cached[64] = {};      // 0 = not looked up yet; any thread may fill it
   int dev = 0;
   if (hipStreamGetDevice(st, &dev) != hipSuccess && hipGetDevice(&dev) != hipSuccess) return 256;
   if (dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev] = n;
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return n;
 }
 
 // Decode waves of an attention launch on the stream's device: four per decode workgroup, one

@@ -83,6 +83,13 @@ class MixedStepRunner:
         if self.copied[i] is not None:
             self.copied[i].synchronize()
         meta = cb.cb_build_step(sched, budget, self.bufs[i])
+        if meta.max_context_len > self.cos_sin.shape[0]:
+            # cb_rope_kv_append skips rows beyond the rotary table (its padding convention), which
+            # would leave their K/V unwritten and their queries unrotated: stop instead.  The
+            # builder has already committed the step, so this is fatal for the serving loop (it
+            # was configured with too small a max_pos).
+            raise ValueError(f"step reaches position {meta.max_context_len - 1}, beyond the rotary table's "
+                             f"{self.cos_sin.shape[0]} rows (max_pos)")
         meta.buf_index = i
         meta.plan_waves = 0
         meta.launch_tokens = meta.num_tokens

@@ -1,4 +1,5 @@
 """Padded launch shapes (runner.Buckets) on the host: what build() writes and plans, no GPU."""
+import pytest
 import torch
 
 from chunked_prefill_mixed_decode_amd import binding as cb
@@ -58,3 +59,16 @@ def test_bucket_never_exceeds_capacity():
     r = _runner(cap_tokens=100)
     m = r.build(_sched(), 100, buckets=Buckets(tokens=64, context=1024))
     assert m.num_tokens == 100 and m.launch_tokens == 100
+
+
+def test_runner_refuses_a_step_beyond_the_rotary_table():
+    # The rotary/append kernel skips rows whose position lies past its table (the padding rows'
+    # convention), so a serving loop that outgrows max_pos must be stopped on the host.
+    import types
+    from chunked_prefill_mixed_decode_amd import runner as rn
+    r = types.SimpleNamespace(ring=0, copied=[None, None], bufs=[cb.StepBuffers(4, 16, 16, pin=False)] * 2,
+                              cos_sin=torch.zeros((20, 64)), Hq=2, Hkv=2, device=torch.device("cpu"))
+    s = cb.cb_sched_create(16, 8)
+    cb.cb_sched_add_running(s, 19)          # its query sits at position 19: row 20 of the table
+    with pytest.raises(ValueError, match="rotary table"):
+        rn.MixedStepRunner.build(r, s, 8)
