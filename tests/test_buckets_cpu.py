@@ -67,8 +67,8 @@ def test_runner_refuses_a_step_beyond_the_rotary_table():
     import types
     from chunked_prefill_mixed_decode_amd import runner as rn
     r = types.SimpleNamespace(ring=0, copied=[None, None], bufs=[cb.StepBuffers(4, 16, 16, pin=False)] * 2,
-                              cos_sin=torch.zeros((20, 64)), Hq=2, Hkv=2, device=torch.device("cpu"))
+                              cos_sin=torch.zeros((19, 64)), Hq=2, Hkv=2, device=torch.device("cpu"))
     s = cb.cb_sched_create(16, 8)
-    cb.cb_sched_add_running(s, 19)          # its query sits at position 19: row 20 of the table
+    cb.cb_sched_add_running(s, 19)          # its query sits at position 19, past a 19-row table
     with pytest.raises(ValueError, match="rotary table"):
         rn.MixedStepRunner.build(r, s, 8)
