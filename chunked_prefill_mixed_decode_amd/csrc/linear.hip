@@ -9,7 +9,7 @@
 // in it, so T tokens give about T FLOP per weight byte (bf16) -- weight-bandwidth bound for a
 // decode-only step, compute bound once a prefill chunk joins.
 //
-// One 256-thread workgroup per BM x 128 output tile and K split, 64-deep K stages: the x and w
+// One 256-thread workgroup per BM x BN output tile and K split, 64-deep K stages: the x and w
 // tiles of a stage are copied HBM -> LDS with the gfx950 16-byte LDS DMA into a ring of stage
 // buffers, rows chunk-swizzled (16-byte chunk c of row r at c ^ (r mod 8), so the 32 rows an
 // operand read touches at one chunk spread over all 16-byte bank groups); each wave computes a
@@ -50,8 +50,21 @@ constexpr int64_t kMinWorkgroups = CB_LINEAR_MIN_WG;
 constexpr int kMaxSplit = 16;
 constexpr int kMinStagesPerSplit = 4;
 
-int32_t tile_rows(int32_t M) { return M <= CB_LINEAR_SKINNY_M ? 64 : 128; }
-int32_t tile_cols(int32_t M) { return M <= CB_LINEAR_SKINNY_M ? CB_LINEAR_SKINNY_BN : 128; }
+// Tile shape of a layer.  Few rows (a decode-only step): 64 x BN_skinny tiles, a deeper ring, K
+// split until the weight stream has enough workgroups.  More rows: 128 x 192 tiles (three 40 KB
+// stage buffers, one workgroup per compute unit) when N allows and that gives at least
+// kMinWorkgroups * 3 / 4 tiles (the budget-512 layer's QKV projection: 256 tiles, 70 against
+// 72 us with 128 x 128), else 128 x 128 (two 32 KB buffers, two workgroups per unit) with K split
+// as needed (its output projection: 128 x 64 tiles without a split measured 35.8 against 32.7 us).
+struct TileShape {
+  int32_t bm, bn, ns;
+};
+TileShape tile_shape(int32_t M, int32_t N) {
+  if (M <= CB_LINEAR_SKINNY_M) return {64, CB_LINEAR_SKINNY_BN, CB_LINEAR_SKINNY_STAGES};
+  const int64_t mt = (static_cast<int64_t>(M) + 127) / 128;
+  if (N % 192 == 0 && mt * (N / 192) >= kMinWorkgroups * 3 / 4) return {128, 192, 3};
+  return {128, 128, 2};
+}
 
 // K splits for a shape: the smallest power of two giving kMinWorkgroups workgroups, at most
 // kMaxSplit, dividing the K stages evenly and keeping kMinStagesPerSplit stages per split.
@@ -98,7 +111,8 @@ __global__ __launch_bounds__(256) void linear_kernel(const bf16_t* __restrict__ 
                                                      bf16_t* __restrict__ y, float* __restrict__ part,
                                                      int32_t M, int32_t N, int32_t K, int32_t m_tiles,
                                                      int32_t splits, int32_t items, int32_t per_xcd) {
-  static_assert((BM == 64 || BM == 128) && (BN == 64 || BN == 128) && NS >= 2 && NS <= 4, "tile shape and ring depth");
+  static_assert((BM == 64 || BM == 128) && (BN == 64 || BN == 128 || BN == 192) && NS >= 2 && NS <= 4,
+                "tile shape and ring depth");
   constexpr int XC = BM / 32;                        // x copies per wave per stage (8 rows each)
   constexpr int WC = BN / 32;                        // w copies per wave per stage
   constexpr int CPS = XC + WC;                       // copies per wave per stage
@@ -220,8 +234,8 @@ __global__ __launch_bounds__(256) void linear_reduce_kernel(const float* __restr
 extern "C" size_t cb_linear_workspace_bytes(int32_t M, int32_t N, int32_t K) {
   using namespace cb;
   if (M < 1 || N < 1 || K < 1 || N % kNAlign || K % kBK) return 0;
-  const int32_t bm = tile_rows(M), bn = tile_cols(M);
-  const int64_t tiles = ((static_cast<int64_t>(M) + bm - 1) / bm) * (N / bn);
+  const TileShape ts = tile_shape(M, N);
+  const int64_t tiles = ((static_cast<int64_t>(M) + ts.bm - 1) / ts.bm) * (N / ts.bn);
   const int32_t s = k_splits(tiles, K);
   return s > 1 ? static_cast<size_t>(s) * M * N * sizeof(float) : 0;
 }
@@ -235,9 +249,9 @@ extern "C" int cb_linear(void* stream, int32_t dtype, int32_t M, int32_t N, int3
   if (!x || !w || !y) return CB_ERR_INVALID;
   for (const void* p : {x, w, static_cast<const void*>(y)})
     if (reinterpret_cast<uintptr_t>(p) & 15u) return CB_ERR_INVALID;
-  const int32_t bm = tile_rows(M), bn = tile_cols(M);
-  const int64_t m_tiles = (static_cast<int64_t>(M) + bm - 1) / bm;
-  const int64_t tiles = m_tiles * (N / bn);
+  const TileShape ts = tile_shape(M, N);
+  const int64_t m_tiles = (static_cast<int64_t>(M) + ts.bm - 1) / ts.bm;
+  const int64_t tiles = m_tiles * (N / ts.bn);
   const int32_t splits = k_splits(tiles, K);
   if (splits > 1) {
     if (workspace_bytes < cb_linear_workspace_bytes(M, N, K)) return CB_ERR_CAPACITY;
@@ -248,7 +262,9 @@ extern "C" int cb_linear(void* stream, int32_t dtype, int32_t M, int32_t N, int3
   if (per_xcd * 8 > 0x7fffffff) return CB_ERR_INVALID;
   hipStream_t st = static_cast<hipStream_t>(stream);
   float* part = static_cast<float*>(workspace);
-  auto kernel = bm == 64 ? linear_kernel<64, CB_LINEAR_SKINNY_BN, CB_LINEAR_SKINNY_STAGES> : linear_kernel<128, 128, 2>;
+  auto kernel = ts.bm == 64  ? linear_kernel<64, CB_LINEAR_SKINNY_BN, CB_LINEAR_SKINNY_STAGES>
+                : ts.bn == 192 ? linear_kernel<128, 192, 3>
+                               : linear_kernel<128, 128, 2>;
   kernel<<<dim3(static_cast<uint32_t>(per_xcd * 8)), dim3(256), 0, st>>>(
       static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(w), static_cast<bf16_t*>(y), part, M, N, K,
       static_cast<int32_t>(m_tiles), splits, static_cast<int32_t>(items), static_cast<int32_t>(per_xcd));
