@@ -13,12 +13,13 @@
 // tiles of a stage are copied HBM -> LDS with the gfx950 16-byte LDS DMA into a ring of stage
 // buffers, rows chunk-swizzled (16-byte chunk c of row r at c ^ (r mod 8), so the 32 rows an
 // operand read touches at one chunk spread over all 16-byte bank groups); each wave computes a
-// BM/2 x 64 quarter with v_mfma_f32_32x32x16_bf16.  Two shapes: BM = 128 with two stage buffers
-// (the next stage's copy in flight behind the one being multiplied; 64 KB, two workgroups per
-// compute unit -- measured faster than three buffers and one workgroup) for the compute-bound
-// mixed step, and BM = 64 with three (72 KB, still two workgroups per unit, two stages of weights
-// in flight) for a decode-only step's few rows, where the weight stream is the whole cost and the
-// bytes in flight set its rate.  Tiles are ordered so that the workgroups sharing one weight tile
+// BM/2 x BN/2 quarter with v_mfma_f32_32x32x16_bf16.  Three shapes: 128 x 128 with two stage
+// buffers (the next stage's copy in flight behind the one being multiplied; 64 KB, two workgroups
+// per compute unit -- measured faster than three buffers and one workgroup) and 128 x 192 with
+// three (120 KB, one workgroup per unit, for wide layers whose tiles then fill the chip once) for
+// the compute-bound mixed step, and 64 x 64 with three (48 KB, two stages of weights in flight)
+// for a decode-only step's few rows, where the weight stream is the whole cost and the bytes in
+// flight set its rate.  Tiles are ordered so that the workgroups sharing one weight tile
 // run on one XCD (workgroup b runs on XCD b mod 8) and read it through that XCD's L2.  A layer
 // with few tiles (a decode-only step's rows) splits K so that at least 256 workgroups stream the
 // weights: each split writes float32 partials and a second kernel sums them in split order (the
