@@ -236,6 +236,67 @@ __device__ __forceinline__ void lds_copy16_asm_s(const char* base, uint32_t voff
       : "=&s"(saved)
       : "v"(voff), "s"(base), "s"(dst));
 }
+// K and V copies of one wave's rows of a stage in one asm block: for each of its NC copy
+// instructions j, K then V, from the wave-uniform bases kb[j] / vb[j] plus the lane's 32-bit
+// offset voff[j], into the LDS spans dk[j] / dv[j] (wave-uniform).  No immediate offset: the
+// LDS DMA adds it to the LDS address as well.  M0 is saved once, set before each copy (one wait
+// state before the copy reads it) and restored.
+template <int NC>
+__device__ __forceinline__ void dma_kv(const char* const (&kb)[NC], const char* const (&vb)[NC], const uint32_t (&voff)[NC],
+                                       const uint32_t (&dk)[NC], const uint32_t (&dv)[NC]) {
+  static_assert(NC == 1 || NC == 2, "one or two copies per tensor");
+  uint32_t saved;
+  if constexpr (NC == 1) {
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %4\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %2\n\t"
+        "s_mov_b32 m0, %5\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %3\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(voff[0]), "s"(kb[0]), "s"(vb[0]), "s"(dk[0]), "s"(dv[0]));
+  } else {
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %7\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %3\n\t"
+        "s_mov_b32 m0, %8\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %4\n\t"
+        "s_mov_b32 m0, %9\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %2, %5\n\t"
+        "s_mov_b32 m0, %10\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %2, %6\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(voff[0]), "v"(voff[1]), "s"(kb[0]), "s"(vb[0]), "s"(kb[1]), "s"(vb[1]), "s"(dk[0]), "s"(dv[0]),
+          "s"(dk[1]), "s"(dv[1]));
+  }
+}
+// Maximum of a lane's 16 scores in eight v_max3_f32 of one asm block (no canonicalising moves
+// around each fmaxf, no wait states between the steps; the operands are matrix-core results or
+// -inf, never signalling NaNs).
+__device__ __forceinline__ float max16_raw(const f32x16& v) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3\n\t"
+      "v_max3_f32 %0, %0, %4, %5\n\t"
+      "v_max3_f32 %0, %0, %6, %7\n\t"
+      "v_max3_f32 %0, %0, %8, %9\n\t"
+      "v_max3_f32 %0, %0, %10, %11\n\t"
+      "v_max3_f32 %0, %0, %12, %13\n\t"
+      "v_max3_f32 %0, %0, %14, %15\n\t"
+      "v_max_f32 %0, %0, %16"
+      : "=&v"(r)
+      : "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "v"(v[4]), "v"(v[5]), "v"(v[6]), "v"(v[7]), "v"(v[8]),
+        "v"(v[9]), "v"(v[10]), "v"(v[11]), "v"(v[12]), "v"(v[13]), "v"(v[14]), "v"(v[15]));
+  return r;
+}
 // Scalar (SMEM) load of one int32 from a wave-uniform address, issued without waiting; the
 // value may be used only after sload_ready (s_waitcnt lgkmcnt(0), which the value passes
 // through, so no use can be scheduled before it).
@@ -1079,28 +1140,43 @@ __device__ __forceinline__ void chunk_tile(const AttnArgs& a, int32_t tile, char
       const int32_t row_w = 8 * wave;
       const int32_t* bt = btab;
       auto blk_ptr = [&](int32_t jj) { return bt + (min((kt_lo + jj) * kChunkKeys + row_w, k_last) >> bsh); };
-      auto issue_s = [&](int32_t jj, int buf, int32_t blk) {
+      // LDS spans of this wave's copies in ring buffer 0 (wave-uniform integers).
+      const uint32_t dk0 = __builtin_amdgcn_readfirstlane(lds_addr(sK)) + wave * NCPW * 1024;
+      const uint32_t dv0 = __builtin_amdgcn_readfirstlane(lds_addr(sV)) + wave * NCPW * 1024;
+      auto issue_s = [&](int32_t jj, auto B, int32_t blk) {
+        constexpr int buf = decltype(B)::value;
         const int32_t k0 = (kt_lo + jj) * kChunkKeys;
-        const char* kb = kc + (static_cast<int64_t>(blk) * blk_bytes + head_bytes);
-        const char* vb = vc + (static_cast<int64_t>(blk) * blk_bytes + head_bytes);
+        const int64_t bb = static_cast<int64_t>(blk) * blk_bytes + head_bytes;
+        uint32_t dk[NCPW], dv[NCPW];
+#pragma unroll
+        for (int jc = 0; jc < NCPW; ++jc) {
+          dk[jc] = dk0 + buf * STAGE + jc * 1024;
+          dv[jc] = dv0 + buf * STAGE + jc * 1024;
+        }
         if (k0 + row_w + 7 <= k_last) {               // the wave's rows are all real keys
+          // Its 8 rows are 8-aligned in one block: copy jc starts RPI jc rows further.
+          const int64_t roff = static_cast<int64_t>((k0 + row_w) & bmask) * ROW;
+          const char* kb[NCPW];
+          const char* vb[NCPW];
 #pragma unroll
           for (int jc = 0; jc < NCPW; ++jc) {
-            const int i = wave * NCPW + jc;
-            const int64_t roff = static_cast<int64_t>((k0 + i * RPI) & bmask) * ROW;
-            lds_copy16_asm_s(kb + roff, lane_off[jc], sK + buf * STAGE + i * 1024);
-            lds_copy16_asm_s(vb + roff, lane_off[jc], sV + buf * STAGE + i * 1024);
+            kb[jc] = kc + bb + roff + jc * RPI * ROW;
+            vb[jc] = vc + bb + roff + jc * RPI * ROW;
           }
+          dma_kv<NCPW>(kb, vb, lane_off, dk, dv);
         } else {                                      // keys past kv_end repeat the last one
+          uint32_t voff[NCPW];
+          const char* kb[NCPW];
+          const char* vb[NCPW];
 #pragma unroll
           for (int jc = 0; jc < NCPW; ++jc) {
-            const int i = wave * NCPW + jc;
-            const int r = i * RPI + cp_row;
+            const int r = (wave * NCPW + jc) * RPI + cp_row;
             const int32_t key = min(k0 + r, k_last);
-            const uint32_t voff = static_cast<uint32_t>((key & bmask) * ROW + 16 * lds_chunk(cp_pos, r, ROW));
-            lds_copy16_asm_s(kb, voff, sK + buf * STAGE + i * 1024);
-            lds_copy16_asm_s(vb, voff, sV + buf * STAGE + i * 1024);
+            voff[jc] = static_cast<uint32_t>((key & bmask) * ROW + 16 * lds_chunk(cp_pos, r, ROW));
+            kb[jc] = kc + bb;
+            vb[jc] = vc + bb;
           }
+          dma_kv<NCPW>(kb, vb, voff, dk, dv);
         }
       };
       // Prologue: block ids and copies of the first NS - 1 stages, the next id, then the first
@@ -1110,9 +1186,11 @@ __device__ __forceinline__ void chunk_tile(const AttnArgs& a, int32_t tile, char
       for (int p = 0; p < NS - 1; ++p) blk0[p] = sload_issue(blk_ptr(p));
 #pragma unroll
       for (int p = 0; p < NS - 1; ++p) sload_ready(blk0[p]);
-#pragma unroll
-      for (int p = 0; p < NS - 1; ++p)
-        if (p < n_st) issue_s(p, p, blk0[p]);
+      if (0 < n_st) issue_s(0, std::integral_constant<int, 0>{}, blk0[0]);
+      if (1 < n_st) issue_s(1, std::integral_constant<int, 1>{}, blk0[1]);
+      if constexpr (NS > 3) {
+        if (2 < n_st) issue_s(2, std::integral_constant<int, 2>{}, blk0[2]);
+      }
       int32_t blk_nx = sload_issue(blk_ptr(NS - 1));
       wait_stage(min(NS - 2, n_st - 1));
       f32x16 s_cur = f32x16{};
@@ -1134,7 +1212,7 @@ __device__ __forceinline__ void chunk_tile(const AttnArgs& a, int32_t tile, char
         if (jj + 1 < n_st) wait_stage(min(NS - 3, n_st - jj - 2));   // stage jj + 1 landed everywhere
         if (jj + NS - 1 < n_st) {
           sload_ready(blk_nx);
-          issue_s(jj + NS - 1, pbuf, blk_nx);
+          issue_s(jj + NS - 1, std::integral_constant<int, pbuf>{}, blk_nx);
         }
         // K of stage jj + 1 is read even on the last stage (stale ring data, its products
         // unused), so the score products and the softmax share one basic block and can be
@@ -1152,9 +1230,7 @@ __device__ __forceinline__ void chunk_tile(const AttnArgs& a, int32_t tile, char
           for (int r = 0; r < 16; ++r)
             if (k0 + acc32_row(lane, r) > qpos) st[r] = kNegInf;
         }
-        float mx = st[0];
-#pragma unroll
-        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, st[r]);
+        float mx = max16_raw(st);
         mx = half_xor_max(mx);
         // Lazy rescale: the weights are 2^(s c - m_ref) with m_ref a running maximum allowed to
         // lag the true one by up to kRescaleSlack (weights stay below 2^kRescaleSlack), so the
@@ -1185,13 +1261,17 @@ __device__ __forceinline__ void chunk_tile(const AttnArgs& a, int32_t tile, char
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) s4[q4] = (st[4 * q4] + st[4 * q4 + 1]) + (st[4 * q4 + 2] + st[4 * q4 + 3]);
         l_run += (s4[0] + s4[1]) + (s4[2] + s4[3]);
+        Frag<T> pfs[2];
 #pragma unroll
-        for (int ps = 0; ps < 2; ++ps) {          // 16-key contraction steps
+        for (int ps = 0; ps < 2; ++ps) {
           float pv[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) pv[e] = st[8 * ps + e];
-          Frag<T> pf;
-          pf.set_all(pv);
+          pfs[ps].set_all(pv);
+        }
+#pragma unroll
+        for (int ps = 0; ps < 2; ++ps) {          // 16-key contraction steps
+          const Frag<T>& pf = pfs[ps];
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt) {
             Frag<T> vt;
