@@ -488,6 +488,15 @@ __device__ __forceinline__ void lds_operands_ready(KRegs<64>& kr, VRegs<64>& vr)
                : "+v"(kr.k[0]), "+v"(kr.k[1]), "+v"(kr.k[2]), "+v"(kr.k[3]),
                  "+v"(vr.v[0][0]), "+v"(vr.v[0][1]), "+v"(vr.v[0][2]), "+v"(vr.v[0][3]), "+v"(vr.v[1][0]), "+v"(vr.v[1][1]), "+v"(vr.v[1][2]), "+v"(vr.v[1][3]));
 }
+// Wait for the K reads of a stage issued before its V reads (LDS reads of a wave complete in
+// order, so at most the V reads may still be outstanding; the counter holds at most 15).
+template <int D>
+__device__ __forceinline__ void lds_k_ready(KRegs<D>& kr) {
+  if constexpr (D == 128)
+    asm volatile("s_waitcnt lgkmcnt(15)" : "+v"(kr.k[0]), "+v"(kr.k[1]), "+v"(kr.k[2]), "+v"(kr.k[3]), "+v"(kr.k[4]), "+v"(kr.k[5]), "+v"(kr.k[6]), "+v"(kr.k[7]));
+  else
+    asm volatile("s_waitcnt lgkmcnt(8)" : "+v"(kr.k[0]), "+v"(kr.k[1]), "+v"(kr.k[2]), "+v"(kr.k[3]));
+}
 template <int D>
 __device__ __forceinline__ void lds_operands_ready(KRegs<D>& kr) {
   if constexpr (D == 128)
@@ -1219,8 +1228,8 @@ __device__ __forceinline__ void chunk_tile(const AttnArgs& a, int32_t tile, char
         // interleaved.
         VRegs<D> vr;
         KRegs<D> kr;
-        vr.template read<buf * STAGE>(va);
         kr.template read<nbuf * STAGE>(ka);
+        vr.template read<buf * STAGE>(va);
 
         // Mask and row maximum of stage jj (while the operand reads are in flight).
         const int32_t k0 = (kt_lo + jj) * kChunkKeys;
@@ -1246,8 +1255,7 @@ __device__ __forceinline__ void chunk_tile(const AttnArgs& a, int32_t tile, char
         }
         const float m_use = m_run == kNegInf ? 0.f : m_run;
 
-        lds_operands_ready(kr, vr);
-        blk_nx = sload_issue(blk_ptr(jj + NS));        // for the next iteration's copy
+        lds_k_ready<D>(kr);                            // K landed; V may still be in flight
         s_cur = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
@@ -1269,6 +1277,8 @@ __device__ __forceinline__ void chunk_tile(const AttnArgs& a, int32_t tile, char
           for (int e = 0; e < 8; ++e) pv[e] = st[8 * ps + e];
           pfs[ps].set_all(pv);
         }
+        lds_operands_ready<D>(vr);
+        blk_nx = sload_issue(blk_ptr(jj + NS));        // for the next iteration's copy
 #pragma unroll
         for (int ps = 0; ps < 2; ++ps) {          // 16-key contraction steps
           const Frag<T>& pf = pfs[ps];
