@@ -1,4 +1,5 @@
-"""Thin ctypes binding of libcb.so (include/cb.h).  Argument marshalling only.
+"""Thin ctypes binding of libcb.so (include/cb.h and its optional extensions include/cb_ext.h).
+Argument marshalling only.
 
 Every function here has the name of the C entry point it calls and forwards to it: torch tensors
 become raw pointers (host or device), the HIP stream defaults to torch's current stream on the

@@ -29,6 +29,7 @@
 #include <type_traits>
 
 #include "cb.h"
+#include "cb_ext.h"
 #include "common.h"
 
 namespace cb {

@@ -19,7 +19,7 @@ from tests.harness import step_caps
 
 from chunked_prefill_mixed_decode_amd import binding as cb
 
-HEADER = os.path.join(ROOT, "include", "cb.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("cb.h", "cb_ext.h")]
 
 REASON = {cb.CB_ERR_INVALID: "invalid", cb.CB_ERR_DECODE_OVER_BUDGET: "decode_over_budget",
           cb.CB_ERR_OUT_OF_BLOCKS: "out_of_blocks"}
@@ -34,7 +34,7 @@ def built_library():
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    text = "".join(open(h).read() for h in HEADERS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(cb_[a-z0-9_]+)\s*\(", text)))
 
