@@ -136,9 +136,13 @@ def isolation_pass(g, metas, qrots, outs, w, reps: int, flush=None, kinds=("deco
         Hq, Hkv, D = g.runner.Hq, g.runner.Hkv, g.runner.D
         need = [cb.cb_attn_workspace_bytes(nd, nd, nd, 1, meta.max_decode_context_len,
                                            meta.max_decode_context_len, Hq, Hkv, D)]
+        # A chunk-only launch sizes its key split by its own rows' longest context.
+        chunk_ctx = int(h["context_lens"][nd:meta.num_seqs].max()) if T > nd else 0
+        need_chunk = 0
         if T > nd:
-            need.append(cb.cb_attn_workspace_bytes(meta.num_seqs - nd, 0, T - nd, meta.max_q_len, 0,
-                                                   meta.max_context_len, Hq, Hkv, D))
+            need_chunk = cb.cb_attn_workspace_bytes(meta.num_seqs - nd, 0, T - nd, meta.max_q_len, 0,
+                                                    chunk_ctx, Hq, Hkv, D)
+            need.append(need_chunk)
         g.runner.ensure_workspace(max(need))
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
         for e in ev:
@@ -157,17 +161,29 @@ def isolation_pass(g, metas, qrots, outs, w, reps: int, flush=None, kinds=("deco
                 torch.cuda.synchronize()
                 dec.append((k, ev[0].elapsed_time(ev[1]) + ev[4].elapsed_time(ev[5])))
             if T > nd and "chunk" in kinds:
-                if flush is not None:
-                    flush.sum()
+                # Two launches: one timed from the attention kernel's start to the combine's end
+                # (the launch splits keys, and so has a combine, exactly when it needs a
+                # workspace), one around the attention kernel alone.
+                split = need_chunk > 0
+                times = []
+                for slots in ((2, 5 if split else 3), (2, 3)):
+                    if flush is not None:
+                        flush.sum()
+                        torch.cuda.synchronize()
+                    ce = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+                    for e in ce:
+                        e.record()                         # torch's record flag; the call re-records
+                    evs6 = [None] * 6
+                    evs6[slots[0]], evs6[slots[1]] = ce
+                    cb.cb_mixed_paged_attention(
+                        qrots[k][nd:], g.runner.k_cache, g.runner.v_cache, cu_chunk,
+                        dev["context_lens"][nd:], dev["cu_blocks"][nd:], dev["block_table"], outs[k][nd:],
+                        g.runner.workspace, num_seqs=meta.num_seqs - nd, num_decodes=0,
+                        max_q_len=meta.max_q_len, max_decode_ctx=0, max_ctx=chunk_ctx,
+                        scale=g.runner.scale, events=evs6)
                     torch.cuda.synchronize()
-                cb.cb_mixed_paged_attention(
-                    qrots[k][nd:], g.runner.k_cache, g.runner.v_cache, cu_chunk,
-                    dev["context_lens"][nd:], dev["cu_blocks"][nd:], dev["block_table"], outs[k][nd:],
-                    g.runner.workspace, num_seqs=meta.num_seqs - nd, num_decodes=0,
-                    max_q_len=meta.max_q_len, max_decode_ctx=0, max_ctx=meta.max_context_len,
-                    scale=g.runner.scale, events=[None, None, ev[2], ev[3], None, None])
-                torch.cuda.synchronize()
-                chk.append((k, ev[2].elapsed_time(ev[3])))
+                    times.append(ce[0].elapsed_time(ce[1]))
+                chk.append((k, times[0], times[1]))
     return dec, chk
 
 
@@ -216,13 +232,15 @@ def linear_pass(w, dev, tokens: dict, reps: int = 20):
 
 def summarize_isolated(dec, chk, metas, w, elt):
     """Roofline fractions of isolated launches: decode rows (bytes over attention + combine time)
-    against HBM, chunk rows (FLOPs over chunk time) against bf16 MFMA, totals and per step."""
+    against HBM, chunk rows (FLOPs over attention + combine time when the launch splits keys; the
+    attention kernel alone beside it) against bf16 MFMA, totals and per step."""
     dec_s = sum(t for _, t in dec) / 1e3
-    chk_s = sum(t for _, t in chk) / 1e3
+    chk_s = sum(t for _, t, _ in chk) / 1e3
+    chk_attn_s = sum(t for _, _, t in chk) / 1e3
     dbytes = sum(decode_bytes(metas[k], w, elt) for k, _ in dec)
-    cflops = sum(chunk_flops(metas[k], w) for k, _ in chk)
+    cflops = sum(chunk_flops(metas[k], w) for k, _, _ in chk)
     per_step = {}
-    for k, t in chk:
+    for k, t, _ in chk:
         per_step.setdefault(k, []).append(t)
     out = {"decode_avg_us": dec_s / max(1, len(dec)) * 1e6,
            "decode_GBps": dbytes / max(dec_s, 1e-12) / 1e9,
@@ -230,6 +248,8 @@ def summarize_isolated(dec, chk, metas, w, elt):
            "chunk_avg_us": chk_s / max(1, len(chk)) * 1e6,
            "chunk_TFLOPs": cflops / max(chk_s, 1e-12) / 1e12,
            "chunk_frac_mfma": cflops / max(chk_s, 1e-12) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+           "chunk_attn_kernel_avg_us": chk_attn_s / max(1, len(chk)) * 1e6,
+           "chunk_attn_kernel_frac_mfma": cflops / max(chk_attn_s, 1e-12) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
            "chunk_flops_per_step": cflops / max(1, len(chk)),
            "chunk_TFLOPs_per_step": {str(k): chunk_flops(metas[k], w) / (sum(v) / len(v) / 1e3) / 1e12
                                      for k, v in sorted(per_step.items())}}

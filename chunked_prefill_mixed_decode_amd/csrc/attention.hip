@@ -45,6 +45,12 @@ namespace {
 #ifndef CB_CHUNK_MIN_TILES_MIXED
 #define CB_CHUNK_MIN_TILES_MIXED 128  // the same beside decode rows, whose streaming covers long tiles
 #endif
+#ifndef CB_CHUNK_SPLIT_KEYS
+#define CB_CHUNK_SPLIT_KEYS 512       // fewest keys of the longest context per split (no decodes):
+#endif                                // each split adds a float32 partial and its merge
+#ifndef CB_CHUNK_SPLIT_KEYS_MIXED
+#define CB_CHUNK_SPLIT_KEYS_MIXED 64  // the same beside decode rows
+#endif
 #ifndef CB_DECODE_WG_PER_CU
 #define CB_DECODE_WG_PER_CU 2         // four-wave decode workgroups per CU without chunk tiles
 #endif
@@ -132,8 +138,8 @@ Plan make_plan(int32_t num_seqs, int32_t nd, int32_t T, int32_t max_q_len, int32
     p.q_blocks = (std::max(max_q_len, 1) + p.bmq - 1) / p.bmq;
     const int64_t tiles = static_cast<int64_t>(p.n_chunk) * p.q_blocks * Hkv;
     const int64_t min_tiles = nd > 0 ? CB_CHUNK_MIN_TILES_MIXED : CB_CHUNK_MIN_TILES;
-    while (p.nsplit < kMaxSplit && tiles * p.nsplit < min_tiles &&
-           max_ctx / (2 * p.nsplit) >= 2 * kChunkKeys)
+    const int32_t min_keys = nd > 0 ? CB_CHUNK_SPLIT_KEYS_MIXED : CB_CHUNK_SPLIT_KEYS;
+    while (p.nsplit < kMaxSplit && tiles * p.nsplit < min_tiles && max_ctx / (2 * p.nsplit) >= min_keys)
       p.nsplit *= 2;
   }
   size_t off = 0;
@@ -397,8 +403,8 @@ __device__ __forceinline__ void wait_vm_barrier() {
 // ds_read_b64_tr_b16 per 32x16 piece, the second 16 keys further down).  ka[ks] / va[2 mt + h]
 // are the LDS addresses lds_row_frag and the V^T layout above read in ring buffer 0 (piece
 // ps = 0); OFF selects the ring buffer (an immediate offset), and ps = 1 is 16 rows further.
-typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 // Two asm blocks issue them without waiting: K rows (KRegs) and V^T (VRegs), in the ring buffer
 // selected by OFF.  lds_operands_ready() waits for both (lgkmcnt(0)) and passes every destination register
 // through the wait, so no use of them can be scheduled before it.
@@ -514,6 +520,21 @@ __device__ __forceinline__ void lds_operands_ready(VRegs<D>& vr) {
   else
     asm volatile("s_waitcnt lgkmcnt(0)"
                  : "+v"(vr.v[0][0]), "+v"(vr.v[0][1]), "+v"(vr.v[0][2]), "+v"(vr.v[0][3]), "+v"(vr.v[1][0]), "+v"(vr.v[1][1]), "+v"(vr.v[1][2]), "+v"(vr.v[1][3]));
+}
+// The same wait for V, ordered after the packed weights P of the stage (they pass through it
+// too): the scheduler may otherwise hoist the wait above the score products, so that these
+// would also wait for the V reads.
+template <int D>
+__device__ __forceinline__ void lds_v_ready_after(VRegs<D>& vr, u32x4& p0, u32x4& p1) {
+  if constexpr (D == 128)
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(vr.v[0][0]), "+v"(vr.v[0][1]), "+v"(vr.v[0][2]), "+v"(vr.v[0][3]), "+v"(vr.v[0][4]), "+v"(vr.v[0][5]), "+v"(vr.v[0][6]), "+v"(vr.v[0][7]),
+                   "+v"(vr.v[1][0]), "+v"(vr.v[1][1]), "+v"(vr.v[1][2]), "+v"(vr.v[1][3]), "+v"(vr.v[1][4]), "+v"(vr.v[1][5]), "+v"(vr.v[1][6]), "+v"(vr.v[1][7]),
+                   "+v"(p0), "+v"(p1));
+  else
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(vr.v[0][0]), "+v"(vr.v[0][1]), "+v"(vr.v[0][2]), "+v"(vr.v[0][3]), "+v"(vr.v[1][0]), "+v"(vr.v[1][1]), "+v"(vr.v[1][2]), "+v"(vr.v[1][3]),
+                   "+v"(p0), "+v"(p1));
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -1153,17 +1174,20 @@ __device__ __forceinline__ void chunk_tile(const AttnArgs& a, int32_t tile, char
       // LDS spans of this wave's copies in ring buffer 0 (wave-uniform integers).
       const uint32_t dk0 = __builtin_amdgcn_readfirstlane(lds_addr(sK)) + wave * NCPW * 1024;
       const uint32_t dv0 = __builtin_amdgcn_readfirstlane(lds_addr(sV)) + wave * NCPW * 1024;
-      auto issue_s = [&](int32_t jj, auto B, int32_t blk) {
+      auto issue_s = [&](int32_t jj, auto B, int32_t blk, auto FULL) {
         constexpr int buf = decltype(B)::value;
         const int32_t k0 = (kt_lo + jj) * kChunkKeys;
-        const int64_t bb = static_cast<int64_t>(blk) * blk_bytes + head_bytes;
+        // Block ids are >= 0 and a block's bytes fit 32 bits (the launch checks), so the offset
+        // is one 32 x 32 -> 64-bit product.
+        const int64_t bb = static_cast<int64_t>(static_cast<uint64_t>(static_cast<uint32_t>(blk)) *
+                                                static_cast<uint32_t>(blk_bytes)) + head_bytes;
         uint32_t dk[NCPW], dv[NCPW];
 #pragma unroll
         for (int jc = 0; jc < NCPW; ++jc) {
           dk[jc] = dk0 + buf * STAGE + jc * 1024;
           dv[jc] = dv0 + buf * STAGE + jc * 1024;
         }
-        if (k0 + row_w + 7 <= k_last) {               // the wave's rows are all real keys
+        if (decltype(FULL)::value || k0 + row_w + 7 <= k_last) {   // the wave's rows are all real keys
           // Its 8 rows are 8-aligned in one block: copy jc starts RPI jc rows further.
           const int64_t roff = static_cast<int64_t>((k0 + row_w) & bmask) * ROW;
           const char* kb[NCPW];
@@ -1196,10 +1220,12 @@ __device__ __forceinline__ void chunk_tile(const AttnArgs& a, int32_t tile, char
       for (int p = 0; p < NS - 1; ++p) blk0[p] = sload_issue(blk_ptr(p));
 #pragma unroll
       for (int p = 0; p < NS - 1; ++p) sload_ready(blk0[p]);
-      if (0 < n_st) issue_s(0, std::integral_constant<int, 0>{}, blk0[0]);
-      if (1 < n_st) issue_s(1, std::integral_constant<int, 1>{}, blk0[1]);
+      constexpr std::false_type kAny{};
+      constexpr std::true_type kSteady{};
+      if (0 < n_st) issue_s(0, std::integral_constant<int, 0>{}, blk0[0], kAny);
+      if (1 < n_st) issue_s(1, std::integral_constant<int, 1>{}, blk0[1], kAny);
       if constexpr (NS > 3) {
-        if (2 < n_st) issue_s(2, std::integral_constant<int, 2>{}, blk0[2]);
+        if (2 < n_st) issue_s(2, std::integral_constant<int, 2>{}, blk0[2], kAny);
       }
       int32_t blk_nx = sload_issue(blk_ptr(NS - 1));
       wait_stage(min(NS - 2, n_st - 1));
@@ -1215,14 +1241,18 @@ __device__ __forceinline__ void chunk_tile(const AttnArgs& a, int32_t tile, char
           mma32_k16(s_cur, kf, qf[ks]);
         }
       }
-      auto step = [&](int32_t jj, auto B) {
+      // Steady iterations (the bulk of a long tile) know that stages jj .. jj + NS hold only real
+      // keys and that stage jj needs no causal mask, so they test nothing at run time.
+      auto step = [&](int32_t jj, auto B, auto STEADY) {
         constexpr int buf = decltype(B)::value;
         constexpr int nbuf = (buf + 1) % NS;
         constexpr int pbuf = (buf + NS - 1) % NS;
-        if (jj + 1 < n_st) wait_stage(min(NS - 3, n_st - jj - 2));   // stage jj + 1 landed everywhere
-        if (jj + NS - 1 < n_st) {
-          sload_ready(blk_nx);
-          issue_s(jj + NS - 1, std::integral_constant<int, pbuf>{}, blk_nx);
+        constexpr bool steady = decltype(STEADY)::value;
+        if (steady || jj + NS - 1 < n_st) sload_ready(blk_nx);   // ahead of the LDS reads, or it waits for them too
+        if constexpr (steady) {
+          wait_vm_barrier<(NS - 3 >= 2 ? 2 : NS - 3) * CPW>();    // stage jj + 1 landed everywhere
+        } else if (jj + 1 < n_st) {
+          wait_stage(min(NS - 3, n_st - jj - 2));
         }
         // K of stage jj + 1 is read even on the last stage (stale ring data, its products
         // unused), so the score products and the softmax share one basic block and can be
@@ -1231,11 +1261,14 @@ __device__ __forceinline__ void chunk_tile(const AttnArgs& a, int32_t tile, char
         KRegs<D> kr;
         kr.template read<nbuf * STAGE>(ka);
         vr.template read<buf * STAGE>(va);
+        // The copy of stage jj + NS - 1 (address arithmetic and DMA) goes behind the operand
+        // reads, so they start right after the barrier.
+        if (steady || jj + NS - 1 < n_st) issue_s(jj + NS - 1, std::integral_constant<int, pbuf>{}, blk_nx, STEADY);
 
         // Mask and row maximum of stage jj (while the operand reads are in flight).
         const int32_t k0 = (kt_lo + jj) * kChunkKeys;
         f32x16 st = s_cur;
-        if (k0 + kChunkKeys - 1 > c + qb * a.bmq) {   // some key of the stage may pass a row
+        if (!steady && k0 + kChunkKeys - 1 > c + qb * a.bmq) {   // some key of the stage may pass a row
 #pragma unroll
           for (int r = 0; r < 16; ++r)
             if (k0 + acc32_row(lane, r) > qpos) st[r] = kNegInf;
@@ -1278,8 +1311,14 @@ __device__ __forceinline__ void chunk_tile(const AttnArgs& a, int32_t tile, char
           for (int e = 0; e < 8; ++e) pv[e] = st[8 * ps + e];
           pfs[ps].set_all(pv);
         }
-        lds_operands_ready<D>(vr);
-        blk_nx = sload_issue(blk_ptr(jj + NS));        // for the next iteration's copy
+        {
+          u32x4 p0 = __builtin_bit_cast(u32x4, pfs[0].u), p1 = __builtin_bit_cast(u32x4, pfs[1].u);
+          lds_v_ready_after<D>(vr, p0, p1);
+          pfs[0].u = __builtin_bit_cast(uint4, p0);
+          pfs[1].u = __builtin_bit_cast(uint4, p1);
+        }
+        blk_nx = sload_issue(steady ? bt + (((kt_lo + jj + NS) * kChunkKeys + row_w) >> bsh)
+                                    : blk_ptr(jj + NS));   // for the next iteration's copy
 #pragma unroll
         for (int ps = 0; ps < 2; ++ps) {          // 16-key contraction steps
           const Frag<T>& pf = pfs[ps];
@@ -1304,15 +1343,27 @@ __device__ __forceinline__ void chunk_tile(const AttnArgs& a, int32_t tile, char
           __builtin_amdgcn_sched_group_barrier(0x402, 2, 0);
         }
       };
-      while (j < n_st) {
-        step(j, std::integral_constant<int, 0>{});
+      // Iteration jj is steady when stages up to jj + NS are whole (their keys all lie below
+      // kv_end) and stage jj ends at or before the block's first position.
+      const int32_t n_whole = min(n_st, max(0, kv_end / kChunkKeys - kt_lo));
+      const int32_t n_unmasked = max(0, (c + qb * a.bmq + 1) / kChunkKeys - kt_lo);
+      const int32_t n_steady = max(0, min(n_whole - NS, n_unmasked));
+      static_assert(NS == 3 || NS == 4, "ring unrolled by its depth");
+      for (; j + NS <= n_steady; j += NS) {
+        step(j, std::integral_constant<int, 0>{}, kSteady);
+        step(j + 1, std::integral_constant<int, 1>{}, kSteady);
+        step(j + 2, std::integral_constant<int, 2 % NS>{}, kSteady);
+        if constexpr (NS > 3) step(j + 3, std::integral_constant<int, 3 % NS>{}, kSteady);
+      }
+      while (j < n_st) {                             // the rest (j is a multiple of NS here)
+        step(j, std::integral_constant<int, 0>{}, kAny);
         if (++j == n_st) break;
-        step(j, std::integral_constant<int, 1>{});
+        step(j, std::integral_constant<int, 1>{}, kAny);
         if (++j == n_st) break;
-        step(j, std::integral_constant<int, 2 % NS>{});
+        step(j, std::integral_constant<int, 2 % NS>{}, kAny);
         if (++j == n_st) break;
         if constexpr (NS > 3) {
-          step(j, std::integral_constant<int, 3 % NS>{});
+          step(j, std::integral_constant<int, 3 % NS>{}, kAny);
           if (++j == n_st) break;
         }
       }

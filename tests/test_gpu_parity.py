@@ -362,8 +362,8 @@ def test_block_sizes_and_group_widths(dev):
               np.random.default_rng(16)),
         _make("edge_group32_bs128", "bf16", 64, 2, 64, 128, 120, (300, 129), ((260, 0),), 3, 3017,
               np.random.default_rng(17)),
-        # a 20-token chunk after 3000 cached tokens, no decodes: two tiles, keys split 8 ways
-        _make("edge_split8", "bf16", 2, 2, 128, 16, 20, (), ((3020, 3000),), 1, 3018,
+        # a 20-token chunk after 8200 cached tokens, no decodes: two tiles, keys split 8 ways
+        _make("edge_split8", "bf16", 2, 2, 128, 16, 20, (), ((8220, 8200),), 1, 3018,
               np.random.default_rng(18)),
     ]
     for w in cases:
