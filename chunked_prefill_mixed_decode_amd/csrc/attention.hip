@@ -1557,8 +1557,59 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a, int32_t n_dec_
     so = D;
     sml = 2;
   }
-  // The first eight partials' o are loaded up front, beside their (m, l) pairs: the weights need
-  // the reductions below, the loads do not.
+  T* orow = static_cast<T*>(a.out) + (static_cast<int64_t>(row) * a.Hq + h) * D;
+  if (P <= 8) {
+    // Up to eight partials (every chunk split, most decode rows): each lane loads every (m, l)
+    // pair (one broadcast load each) and PER adjacent elements of every partial o, all in
+    // flight together, then merges serially in partial order -- no cross-lane steps.
+    float2 ml[8];
+    float xv[8][PER];
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+      if (v < P) {
+        ml[v] = *reinterpret_cast<const float2*>(pml + v * sml);
+        if constexpr (PER == 2) {
+          const float2 t = *reinterpret_cast<const float2*>(po + v * so + 2 * lane);
+          xv[v][0] = t.x;
+          xv[v][PER - 1] = t.y;
+        } else {
+          xv[v][0] = po[v * so + lane];
+        }
+      }
+    }
+    float m = kNegInf;
+#pragma unroll
+    for (int v = 0; v < 8; ++v)
+      if (v < P) m = fmaxf(m, ml[v].x);
+    const float m_use = m == kNegInf ? 0.f : m;
+    float wv[8];
+    float Lsum = 0.f;
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+      wv[v] = v < P ? exp2f(ml[v].x - m_use) : 0.f;
+      if (v < P) Lsum += wv[v] * ml[v].y;
+    }
+    const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
+    float acc[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) acc[j] = 0.f;
+#pragma unroll
+    for (int v = 0; v < 8; ++v)
+      if (v < P)
+#pragma unroll
+        for (int j = 0; j < PER; ++j) acc[j] += (wv[v] * inv) * xv[v][j];
+    if constexpr (sizeof(T) == 2) {
+      if constexpr (PER == 2) reinterpret_cast<uint32_t*>(orow)[lane] = pack_bf16x2(acc[0], acc[PER - 1]);
+      else reinterpret_cast<uint16_t*>(orow)[lane] = f32_to_bf16_bits(acc[0]);
+    } else {
+      if constexpr (PER == 2) reinterpret_cast<float2*>(orow)[lane] = make_float2(acc[0], acc[PER - 1]);
+      else orow[lane] = acc[0];
+    }
+    return;
+  }
+  // More partials (long decode rows split over many waves).  The first eight partials' o are
+  // loaded up front, beside their (m, l) pairs: the weights need the reductions below, the loads
+  // do not.
   float x0[8][PER];
 #pragma unroll
   for (int v = 0; v < 8; ++v)
@@ -1616,7 +1667,6 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a, int32_t n_dec_
       for (int j = 0; j < PER; ++j) acc[j] += wk * pk[64 * j];
     }
   }
-  T* orow = static_cast<T*>(a.out) + (static_cast<int64_t>(row) * a.Hq + h) * D;
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
     if constexpr (sizeof(T) == 2) {
