@@ -196,7 +196,8 @@ def linear_pass(w, dev, tokens: dict, reps: int = 20):
     """The linear layers around the step (selective batching: one weight read serves every token of
     the step): the QKV projection [T, Hq D] -> [T, (Hq + 2 Hkv) D] and the output projection
     [T, Hq D] -> [T, Hq D], with seeded synthetic weights, timed with HIP events on the launch
-    stream at the decode-only and the mixed step's token counts."""
+    stream at the decode-only and the mixed step's token counts.  Beside each, the same product
+    through torch.matmul (the ROCm GEMM libraries; a reference point, never the product path)."""
     import torch
     from chunked_prefill_mixed_decode_amd import binding as cb
     from synth.values import matrix_values
@@ -220,9 +221,19 @@ def linear_pass(w, dev, tokens: dict, reps: int = 20):
             us = e0.elapsed_time(e1) / reps * 1e3
             flop = 2 * T * K * N
             wbytes = K * N * 2
+            wT = wt.t().contiguous()                  # [K, N]: the library's plain row-major operand
+            torch.matmul(x, wT)
+            e0.record()
+            for _ in range(reps):
+                torch.matmul(x, wT)
+            e1.record()
+            torch.cuda.synchronize()
+            lib_us = e0.elapsed_time(e1) / reps * 1e3
+            del wT
             res[f"{lname}_{tname}"] = {
                 "tokens": T, "K": K, "N": N, "us": us, "TFLOPs": flop / us / 1e6,
                 "frac_mfma": flop / us / 1e6 / MFMA_BF16_PEAK_TFLOPS,
+                "library_matmul_us": lib_us, "library_frac_mfma": flop / lib_us / 1e6 / MFMA_BF16_PEAK_TFLOPS,
                 "weight_GBps": wbytes / us / 1e3,
                 "flop_per_weight_byte": flop / wbytes, "k_splits": nws // (T * N * 4) if nws else 1}
             del x, y, ws

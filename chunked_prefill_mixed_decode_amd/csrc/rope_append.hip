@@ -10,6 +10,7 @@
 // float32 on its own (contraction is disabled here), then round-to-nearest-even into the element
 // type.  Memory-bound: every thread moves 2 x 8 elements of one head of one row.
 #include <cmath>
+#include <limits>
 
 #include "cb.h"
 #include "common.h"
@@ -94,6 +95,9 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 extern "C" int cb_rope_cos_sin(float* out, int32_t max_pos, int32_t D, double base) {
   if (!out || max_pos < 0 || D < 2 || (D & 1) || !(base > 0.0)) return CB_ERR_INVALID;
+  // The table is defined with x87 extended precision (64-bit significand) for the cosine and sine;
+  // a host whose long double differs would produce other bits, so it is refused.
+  if (std::numeric_limits<long double>::digits != 64) return CB_ERR_INVALID;
   const int32_t half = D / 2;
   for (int32_t i = 0; i < half; ++i) {
     const double theta = std::pow(base, (-2.0 * i) / D);

@@ -196,8 +196,10 @@ int cb_linear(void* stream, int32_t dtype, int32_t M, int32_t N, int32_t K, cons
  * rows must not restart at 0.  The variant is this library's reading (the pages fix none):
  * rotate-half over the full head dimension, theta_i = base^(-2i/D) in double precision,
  * out[p * D + i] = (float)cos(p * theta_i) and out[p * D + D/2 + i] = (float)sin(p * theta_i)
- * for 0 <= i < D/2, the angle p * theta_i a double product and cos/sin evaluated in long double
- * before one rounding to float.  out holds max_pos * D floats (host memory).  D must be even.
+ * for 0 <= i < D/2, the angle p * theta_i a double product and cos/sin evaluated in x87 extended
+ * precision (long double with a 64-bit significand) before one rounding to float.  out holds
+ * max_pos * D floats (host memory).  D must be even.  CB_ERR_INVALID on a host whose long double
+ * is another type (the table's bits would differ).
  * ------------------------------------------------------------------------------------------- */
 int cb_rope_cos_sin(float* out, int32_t max_pos, int32_t D, double base);
 

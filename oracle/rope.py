@@ -42,6 +42,8 @@ def cos_sin_table(max_pos: int, D: int, base: float = 10000.0) -> np.ndarray:
     """[max_pos, D] float32: cos in the first D/2 columns, sin in the last D/2."""
     if D % 2:
         raise ValueError("head dimension must be even")
+    if np.finfo(np.longdouble).nmant != 63:
+        raise RuntimeError("the table is defined with x87 extended precision (numpy longdouble with a 64-bit significand)")
     theta = frequencies(D, base)
     ang = (np.arange(max_pos, dtype=np.float64)[:, None] * theta[None, :]).astype(np.longdouble)
     return np.concatenate([np.cos(ang), np.sin(ang)], axis=1).astype(np.float32)
