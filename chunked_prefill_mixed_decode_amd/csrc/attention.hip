@@ -1518,7 +1518,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) =
 // ---------------------------------------------------------------------------------------------
 // Merge of split partials: m = max m_p, w_p = 2^(m_p - m), out = sum w_p o_p / sum w_p l_p.
 // ---------------------------------------------------------------------------------------------
-template <typename T, int D>
+// FEW: every item has at most eight partials (a launch without decode rows: P = nsplit <= 8), so
+// the general path and its registers are compiled out.
+template <typename T, int D, bool FEW>
 __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a, int32_t n_dec_rows, int32_t n_items) {
   constexpr int PER = D / 64;
   const int lane = threadIdx.x & 63;
@@ -1558,7 +1560,7 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a, int32_t n_dec_
     sml = 2;
   }
   T* orow = static_cast<T*>(a.out) + (static_cast<int64_t>(row) * a.Hq + h) * D;
-  if (P <= 8) {
+  if (FEW || P <= 8) {
     // Up to eight partials (every chunk split, most decode rows): each lane loads every (m, l)
     // pair (one broadcast load each) and PER adjacent elements of every partial o, all in
     // flight together, then merges serially in partial order -- no cross-lane steps.
@@ -1607,6 +1609,7 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a, int32_t n_dec_
     }
     return;
   }
+  if constexpr (FEW) return;
   // More partials (long decode rows split over many waves).  The first eight partials' o are
   // loaded up front, beside their (m, l) pairs: the weights need the reductions below, the loads
   // do not.
@@ -1747,8 +1750,10 @@ int launch_all(hipStream_t st, const AttnArgs& a, const Plan& p, void* const* ev
     const int64_t grid = (items + 3) / 4;
     if (grid > 0x7fffffff) return CB_ERR_INVALID;
     rec(4);
-    combine_kernel<T, D><<<dim3(static_cast<uint32_t>(grid)), dim3(256), 0, st>>>(
-        a, a.nd, static_cast<int32_t>(items));
+    if (a.nd == 0)
+      combine_kernel<T, D, true><<<dim3(static_cast<uint32_t>(grid)), dim3(256), 0, st>>>(a, 0, static_cast<int32_t>(items));
+    else
+      combine_kernel<T, D, false><<<dim3(static_cast<uint32_t>(grid)), dim3(256), 0, st>>>(a, a.nd, static_cast<int32_t>(items));
     if (hipGetLastError() != hipSuccess) return CB_ERR_HIP;
     rec(5);
   }
