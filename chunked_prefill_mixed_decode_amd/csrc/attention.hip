@@ -1299,10 +1299,6 @@ __device__ __forceinline__ void chunk_tile(const AttnArgs& a, int32_t tile, char
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) st[r] = fast_exp2(fmaf(st[r], a.scale_log2, -m_use));
-        float s4[4];
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) s4[q4] = (st[4 * q4] + st[4 * q4 + 1]) + (st[4 * q4 + 2] + st[4 * q4 + 3]);
-        l_run += (s4[0] + s4[1]) + (s4[2] + s4[3]);
         Frag<T> pfs[2];
 #pragma unroll
         for (int ps = 0; ps < 2; ++ps) {
@@ -1310,6 +1306,21 @@ __device__ __forceinline__ void chunk_tile(const AttnArgs& a, int32_t tile, char
 #pragma unroll
           for (int e = 0; e < 8; ++e) pv[e] = st[8 * ps + e];
           pfs[ps].set_all(pv);
+        }
+        {
+          // Row sums of the weights as rounded for the P V products (so numerator and
+          // denominator see the same weights): two chains of four bf16 pair dot products.
+          typedef __attribute__((ext_vector_type(2))) __bf16 b2;
+          const b2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
+          float la = 0.f, lb = 0.f;
+          const uint32_t* u0 = &pfs[0].u.x;
+          const uint32_t* u1 = &pfs[1].u.x;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            la = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, u0[q]), one2, la, false);
+            lb = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, u1[q]), one2, lb, false);
+          }
+          l_run += la + lb;
         }
         {
           u32x4 p0 = __builtin_bit_cast(u32x4, pfs[0].u), p1 = __builtin_bit_cast(u32x4, pfs[1].u);
