@@ -1228,6 +1228,7 @@ __device__ __forceinline__ void chunk_tile(const AttnArgs& a, int32_t tile, char
         if (2 < n_st) issue_s(2, std::integral_constant<int, 2>{}, blk0[2], kAny);
       }
       int32_t blk_nx = sload_issue(blk_ptr(NS - 1));
+      float m_use = 0.f, raw_limit = kNegInf;     // m_run is -inf until the first rescale
       wait_stage(min(NS - 2, n_st - 1));
       f32x16 s_cur = f32x16{};
       {
@@ -1278,16 +1279,18 @@ __device__ __forceinline__ void chunk_tile(const AttnArgs& a, int32_t tile, char
         // Lazy rescale: the weights are 2^(s c - m_ref) with m_ref a running maximum allowed to
         // lag the true one by up to kRescaleSlack (weights stay below 2^kRescaleSlack), so the
         // accumulator rescale and its exponential run only when some row's maximum jumps past it.
-        const float m_cand = mx * a.scale_log2;
-        if (__builtin_amdgcn_ballot_w64(m_cand > m_run + kRescaleSlack)) {
-          const float m_new = fmaxf(m_run, m_cand);
+        // The test compares raw scores with (m_ref + slack) / c, kept beside m_ref (its rounding
+        // only moves the rare rescale by an ulp).
+        if (__builtin_amdgcn_ballot_w64(mx > raw_limit)) {
+          const float m_new = fmaxf(m_run, mx * a.scale_log2);
           const float alpha = m_new == kNegInf ? 1.f : fast_exp2(m_run - m_new);
           l_run *= alpha;
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt) o[mt] *= alpha;
           m_run = m_new;
+          m_use = m_run == kNegInf ? 0.f : m_run;
+          raw_limit = (m_run + kRescaleSlack) / a.scale_log2;
         }
-        const float m_use = m_run == kNegInf ? 0.f : m_run;
 
         lds_k_ready<D>(kr);                            // K landed; V may still be in flight
         s_cur = f32x16{};

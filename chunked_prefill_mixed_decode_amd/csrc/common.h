@@ -113,9 +113,13 @@ __device__ __forceinline__ float wave_xor_sum(float v, int mask) { return v + __
 // Maximum over lanes i and i ^ 32 with gfx950's v_permlane32_swap: the two 32-lane halves trade
 // values inside the VALU (no LDS round trip, so no wait on the lane's other LDS traffic).  The
 // pair it returns is {v[i], v[i ^ 32]} in either order; the maximum does not depend on which.
+// The final maximum is one v_max_f32 from asm: the inputs are scores or -inf (never signalling
+// NaNs), so the canonicalising moves fmaxf would add are not needed.
 __device__ __forceinline__ float half_xor_max(float v) {
   const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(sw[0]), "v"(sw[1]));
+  return r;
 }
 
 constexpr float kNegInf = -__builtin_huge_valf();
