@@ -687,13 +687,19 @@ def main():
     if marg:
         m_s = sum(marg) / len(marg) / 1e3
         f = sum(mflops) / len(mflops)
+        iso_chk = {}
+        for k, t, _ in chk_raw:
+            iso_chk.setdefault(k, []).append(t)
+        alone = [sum(iso_chk[k]) / len(iso_chk[k]) for k in ev_steps if k in iso_chk and k in iso_dec]
+        alone_us = sum(alone) / len(alone) * 1e3 if alone else None
         chunk_marginal = {"us_per_step": m_s * 1e6, "chunk_flops_per_step": f,
-                          "TFLOPs": f / max(m_s, 1e-12) / 1e12,
-                          "frac_mfma": f / max(m_s, 1e-12) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                          "chunk_only_us": alone_us,
+                          "hidden_frac": (1.0 - m_s * 1e6 / alone_us) if alone_us else None,
                           "steps": len(marg),
-                          "note": "chunk FLOPs over the time they add to the mixed step (in-step attention "
-                                  "+ combine minus the warm decode-only launch of the same metadata); a step "
-                                  "cost, not the tiles' matrix-core utilisation (isolated.chunk_frac_mfma)"}
+                          "note": "time the chunk rows add to the mixed step (in-step attention + combine "
+                                  "minus the warm decode-only launch of the same metadata) against the "
+                                  "chunk-only launch of the same steps: the share of the chunk work hidden "
+                                  "under the decode rows' streaming; a step cost, not a utilisation"}
     lin = linear_pass(w, dev, {"decode_only": max(1, len(w.decode_ctx)),
                                "mixed_step": max(m.num_tokens for m in metas)}) if w.dtype == "bf16" else None
 
