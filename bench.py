@@ -509,8 +509,8 @@ def stream_graph_leg(dev, steps: int):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: every box here has one GPU and this path has no "
-              f"multi-GPU leg (--gpus {args.gpus} is not supported)", file=sys.stderr)
+        print(f"bench.py measures one GPU: this path has no multi-GPU leg (--gpus {args.gpus} is not "
+              f"supported; sharding is a design only)", file=sys.stderr)
         sys.exit(2)
     import torch
 
