@@ -120,13 +120,23 @@ def committed_traffic(kernel: str, workload: str):
 
 def isolation_pass(g, metas, qrots, outs, w, reps: int, flush=None, kinds=("decode", "chunk")):
     """Decode-only and chunk-only launches of each step's metadata, timed with HIP events on the
-    launch stream: per-kernel durations without the other kernel running beside it.  Decode
-    launches report attention + combine time.  With ``flush`` (a device tensor larger than L2 and
-    the MALL together), it is read in full (a sum) and the stream synchronised before every launch,
-    so that the caches hold none of the step's data and no dirty lines (cold cache)."""
+    launch stream: per-kernel durations without the other kernel running beside it.  The launches
+    of one kind run back to back after one untimed launch, so the device is busy when each starts
+    (as in a serving loop; a launch onto an idle device starts its workgroups over ~2 µs more).
+    Decode launches report attention + combine time.  With ``flush`` (a device tensor larger than
+    L2 and the MALL together), a read-only sum over it runs on the same stream before every timed
+    launch, so that the caches hold none of the step's data and no dirty lines (cold cache)."""
     import torch
     cb = g.cb
     dec, chk = [], []
+
+    def events(n):
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n)] for _ in range(reps)]
+        for row in evs:
+            for e in row:
+                e.record()                       # creates them (torch's record flag); calls re-record
+        return evs
+
     for k, meta in enumerate(metas):
         nd, T = meta.num_decodes, meta.num_tokens
         h = meta.host
@@ -144,46 +154,52 @@ def isolation_pass(g, metas, qrots, outs, w, reps: int, flush=None, kinds=("deco
                                                     chunk_ctx, Hq, Hkv, D)
             need.append(need_chunk)
         g.runner.ensure_workspace(max(need))
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
-        for e in ev:
-            e.record()
-        for _ in range(reps):
-            if nd > 0 and "decode" in kinds:
+
+        def decode_launch(evs):
+            cb.cb_mixed_paged_attention(
+                qrots[k][:nd], g.runner.k_cache, g.runner.v_cache, dev["cu_seqlens_q"],
+                dev["context_lens"], dev["cu_blocks"], dev["block_table"], outs[k][:nd],
+                g.runner.workspace, num_seqs=nd, num_decodes=nd, max_q_len=1,
+                max_decode_ctx=meta.max_decode_context_len, max_ctx=meta.max_decode_context_len,
+                scale=g.runner.scale, events=evs)
+
+        def chunk_launch(evs):
+            cb.cb_mixed_paged_attention(
+                qrots[k][nd:], g.runner.k_cache, g.runner.v_cache, cu_chunk,
+                dev["context_lens"][nd:], dev["cu_blocks"][nd:], dev["block_table"], outs[k][nd:],
+                g.runner.workspace, num_seqs=meta.num_seqs - nd, num_decodes=0,
+                max_q_len=meta.max_q_len, max_decode_ctx=0, max_ctx=chunk_ctx,
+                scale=g.runner.scale, events=evs)
+
+        if nd > 0 and "decode" in kinds:
+            ev = events(4)
+            torch.cuda.synchronize()
+            decode_launch(None)
+            for r in range(reps):
                 if flush is not None:
                     flush.sum()
-                    torch.cuda.synchronize()
-                cb.cb_mixed_paged_attention(
-                    qrots[k][:nd], g.runner.k_cache, g.runner.v_cache, dev["cu_seqlens_q"],
-                    dev["context_lens"], dev["cu_blocks"], dev["block_table"], outs[k][:nd],
-                    g.runner.workspace, num_seqs=nd, num_decodes=nd, max_q_len=1,
-                    max_decode_ctx=meta.max_decode_context_len, max_ctx=meta.max_decode_context_len,
-                    scale=g.runner.scale, events=[ev[0], ev[1], None, None, ev[4], ev[5]])
-                torch.cuda.synchronize()
-                dec.append((k, ev[0].elapsed_time(ev[1]) + ev[4].elapsed_time(ev[5])))
-            if T > nd and "chunk" in kinds:
-                # Two launches: one timed from the attention kernel's start to the combine's end
-                # (the launch splits keys, and so has a combine, exactly when it needs a
-                # workspace), one around the attention kernel alone.
-                split = need_chunk > 0
-                times = []
-                for slots in ((2, 5 if split else 3), (2, 3)):
+                decode_launch([ev[r][0], ev[r][1], None, None, ev[r][2], ev[r][3]])
+            torch.cuda.synchronize()
+            for r in range(reps):
+                dec.append((k, ev[r][0].elapsed_time(ev[r][1]) + ev[r][2].elapsed_time(ev[r][3])))
+        if T > nd and "chunk" in kinds:
+            # Timed twice: from the attention kernel's start to the combine's end (the launch splits
+            # keys, and so has a combine, exactly when it needs a workspace), and around the
+            # attention kernel alone.
+            end_slot = 5 if need_chunk > 0 else 3
+            whole, alone = events(2), events(2)
+            torch.cuda.synchronize()
+            chunk_launch(None)
+            for evl, (s0, s1) in ((whole, (2, end_slot)), (alone, (2, 3))):
+                for r in range(reps):
                     if flush is not None:
                         flush.sum()
-                        torch.cuda.synchronize()
-                    ce = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-                    for e in ce:
-                        e.record()                         # torch's record flag; the call re-records
                     evs6 = [None] * 6
-                    evs6[slots[0]], evs6[slots[1]] = ce
-                    cb.cb_mixed_paged_attention(
-                        qrots[k][nd:], g.runner.k_cache, g.runner.v_cache, cu_chunk,
-                        dev["context_lens"][nd:], dev["cu_blocks"][nd:], dev["block_table"], outs[k][nd:],
-                        g.runner.workspace, num_seqs=meta.num_seqs - nd, num_decodes=0,
-                        max_q_len=meta.max_q_len, max_decode_ctx=0, max_ctx=chunk_ctx,
-                        scale=g.runner.scale, events=evs6)
-                    torch.cuda.synchronize()
-                    times.append(ce[0].elapsed_time(ce[1]))
-                chk.append((k, times[0], times[1]))
+                    evs6[s0], evs6[s1] = evl[r]
+                    chunk_launch(evs6)
+            torch.cuda.synchronize()
+            for r in range(reps):
+                chk.append((k, whole[r][0].elapsed_time(whole[r][1]), alone[r][0].elapsed_time(alone[r][1])))
     return dec, chk
 
 
@@ -665,11 +681,12 @@ def main():
     print("[bench] isolated launches (warm, then cold)...", file=sys.stderr, flush=True)
     dec_raw, chk_raw = isolation_pass(g, metas, qrots, outs, w, reps=3)
     iso = summarize_isolated(dec_raw, chk_raw, metas, w, elt)
-    iso["note"] = "decode-only and chunk-only launches of the same step metadata, 3 reps per step"
+    iso["note"] = ("decode-only and chunk-only launches of the same step metadata, 3 timed per step and kind, "
+                   "back to back after one untimed launch")
     flush = torch.ones(256 << 20, dtype=torch.int32, device=dev)    # 1 GiB, written once here
     torch.cuda.synchronize()
     iso_cold = summarize_isolated(*isolation_pass(g, metas, qrots, outs, w, reps=2, flush=flush), metas, w, elt)
-    iso_cold["note"] = ("as isolated, after a read-only sweep of 1 GiB and a synchronisation before every "
+    iso_cold["note"] = ("as isolated, with a read-only sweep of 1 GiB on the stream before every timed "
                         "launch (L2 and MALL hold none of the step's data and no dirty lines)")
     del flush
     traffic = committed_traffic("attn_kernel", w.name)
