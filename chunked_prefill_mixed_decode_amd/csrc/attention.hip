@@ -7,19 +7,23 @@
 // ("Two kernels with different limiting resources"): decode rows stream the whole cache and are
 // bandwidth-bound, chunk rows are dense matrix work and compute-bound.
 //
-// Four kernels on the caller's stream:
-//   decode_prep_kernel  one workgroup: the decode work list (row, key partition).
-//   decode_kernel  rows [0, nd): persistent one-wave workgroups, each taking every n-th work
-//                  item (decode, KV head, 16-head block, key partition).  K and V rows of 32
-//                  keys go HBM -> LDS by DMA; S^T = K Q^T on 16x16x32 MFMA, online softmax in the
-//                  lane that owns the head, O^T += V^T P^T with V^T read by transposing LDS
-//                  loads.  Writes float32 partials (m, l, unnormalised o).
-//   chunk_kernel   rows [nd, T): one 256-thread workgroup per (chunk, query block, KV head,
-//                  key split).  Rows of a tile are (position, head-in-group) pairs, so all query
-//                  heads of a GQA group share one K/V tile.  K and V tiles of 32 keys staged in
-//                  LDS by DMA; S^T = K Q^T and O^T += V^T P^T on 32x32x16 MFMA; causal mask only
-//                  where a key can exceed the row's position.  One split: normalised output
-//                  written directly; several: float32 partials.
+// Kernels on the caller's stream:
+//   decode_prep_kernel  one workgroup, only when the caller brings no host-made plan: splits the
+//                  decode rows' stage line (32-key stages of every (decode row, KV head, 16-head
+//                  block) unit) into one contiguous range per decode wave, each sized by its
+//                  workgroup's expected streaming rate.
+//   attn_kernel    one launch for both kinds of rows.  The first workgroups hold four independent
+//                  decode waves each: a wave streams its stage range, K and V rows of 32 keys
+//                  HBM -> LDS by DMA, S^T = K Q^T on 16x16x32 MFMA with up to 16 query heads of
+//                  a group as the N dimension, online softmax in the lane that owns the head,
+//                  O^T += V^T P^T with V^T read by transposing LDS loads, one float32 partial
+//                  (m, l, unnormalised o) per unit its range meets.  The other workgroups are
+//                  chunk tiles, one per (chunk, query block, KV head, key split): rows of a tile
+//                  are (position, head-in-group) pairs, so all query heads of a GQA group share
+//                  one K/V stream; a 4-deep LDS ring of 32-key stages filled by DMA, software-
+//                  pipelined so stage j+1's score products (32x32x16 MFMA) run beside stage j's
+//                  softmax; causal mask only where a key can exceed a row's position.  One split:
+//                  normalised rows written directly; several: float32 partials.
 //   combine_kernel log-sum-exp merge of the partials of each (row, head) into out.
 // Softmax runs in base 2: weights are 2^(s c - m) with c = scale * log2(e) and m the running
 // maximum of s c.
@@ -1063,11 +1067,12 @@ __device__ __forceinline__ void chunk_tile(const AttnArgs& a, int32_t tile, char
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) o[mt] = f32x16{};
 
-  // Block ids come from an LDS window [win_lo, win_lo + kBlockWindow) of the block table.  K and V
-  // rows go HBM -> LDS by DMA (chunk-swizzled rows) into a ring of NS stage buffers; keys at or
-  // past kv_end repeat kv_end - 1 and are masked (probability 0).  Stage j's copy is issued
-  // during stage j - NS + 1, after the barrier that proves every wave has read the buffer it
-  // overwrites, so NS - 1 stages of matrix work cover each copy's latency.
+  // K and V rows go HBM -> LDS by DMA (chunk-swizzled rows) into a ring of NS stage buffers; keys
+  // at or past kv_end repeat kv_end - 1 and are masked (probability 0).  A copy is issued after
+  // the barrier that proves every wave has read the buffer it overwrites.  The float32 path
+  // reads block ids from an LDS window [win_lo, win_lo + kBlockWindow) of the block table and
+  // issues stage j's copy during stage j - NS + 1; the bf16 path (below) reads them by scalar
+  // loads.
   int32_t win_lo = 0;
   const int32_t n_blk = ((kv_end - 1) >> bsh) + 1;
   auto fill_window = [&](int32_t first_block) {   // all loads first, then all LDS writes
@@ -1148,9 +1153,9 @@ __device__ __forceinline__ void chunk_tile(const AttnArgs& a, int32_t tile, char
       }
   }
 
-  // Outer loop: one block-id window at a time (a window covers thousands of stages; the copy ring
-  // drains at its end).  Inner loop: the ring, with no other vector-memory operation inside, so
-  // the compiler adds no waits there.
+  // In both paths the ring loop holds no vector-memory operation of the compiler's own, so it adds
+  // no waits there.  Float32: an outer loop over block-id windows (a window covers thousands of
+  // stages; the copy ring drains at its end), the ring inside.
   const int32_t n_st = kt_hi - kt_lo;
   int32_t j = 0;
   if constexpr (sizeof(T) == 2) {
