@@ -1530,7 +1530,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) =
     // workgroup cb (the decode split accounts for it).
     const int32_t cb = b - n_dec_wg;
     const int32_t tile = static_cast<int32_t>(chunk_wg_tile(cb, per_xcd));
-    if (tile < n_tiles) chunk_tile<T, D>(a, tile, lds);
+    if (tile < n_tiles) {
+      // Chunk waves issue ahead of the decode waves that share their SIMDs (wave priority 1
+      // against 0): a decode wave needs few issue slots to keep its copies in flight, and the
+      // tiles finish sooner beside it.
+      __builtin_amdgcn_s_setprio(1);
+      chunk_tile<T, D>(a, tile, lds);
+    }
   }
 }
 
