@@ -105,7 +105,7 @@ constexpr int kChunkKeys = 32;    // keys per LDS stage of a chunk tile
 #define CB_CHUNK_STAGES 4             // chunk K/V stages in the LDS ring (copies run NS - 1 ahead)
 #endif
 constexpr int kChunkStages = CB_CHUNK_STAGES;
-static_assert(kChunkStages >= 2 && kChunkStages <= 4, "chunk ring depth");
+static_assert(kChunkStages >= 3 && kChunkStages <= 8, "chunk ring depth");
 constexpr int kDecodeKeys = 32;   // keys per decode stage
 constexpr int kMaxSplit = 8;
 constexpr int kMinBlock = 8;
@@ -403,6 +403,26 @@ __device__ __forceinline__ void wait_vm_barrier() {
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
+// wait_vm_barrier<later * PER>() for a run-time later in [0, MAXL] (larger values wait as MAXL).
+template <int PER, int MAXL>
+__device__ __forceinline__ void wait_vm_barrier_later(int32_t later) {
+  if constexpr (MAXL <= 0) {
+    wait_vm_barrier<0>();
+  } else {
+    if (later >= MAXL) wait_vm_barrier<MAXL * PER>();
+    else wait_vm_barrier_later<PER, MAXL - 1>(later);
+  }
+}
+
+// f(std::integral_constant<int, I>) for I = 0 .. N - 1, unrolled at compile time.
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
 // The operands of one 32-key chunk stage (bf16): K rows (KS ds_read_b128) and V^T (two
 // ds_read_b64_tr_b16 per 32x16 piece, the second 16 keys further down).  ka[ks] / va[2 mt + h]
 // are the LDS addresses lds_row_frag and the V^T layout above read in ring buffer 0 (piece
@@ -410,8 +430,8 @@ __device__ __forceinline__ void wait_vm_barrier() {
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 // Two asm blocks issue them without waiting: K rows (KRegs) and V^T (VRegs), in the ring buffer
-// selected by OFF.  lds_operands_ready() waits for both (lgkmcnt(0)) and passes every destination register
-// through the wait, so no use of them can be scheduled before it.
+// selected by OFF.  The waits below pass every destination register through the wait, so no use
+// of them can be scheduled before it.
 template <int D> struct KRegs;
 template <int D> struct VRegs;
 template <> struct KRegs<128> {
@@ -487,18 +507,6 @@ template <> struct VRegs<64> {
         : "v"(va[0]), "v"(va[1]), "v"(va[2]), "v"(va[3]), "n"(OFF), "n"(OFF + 2048));
   }
 };
-// Wait for this wave's LDS reads; the registers pass through the wait (data dependence).
-__device__ __forceinline__ void lds_operands_ready(KRegs<128>& kr, VRegs<128>& vr) {
-  asm volatile("s_waitcnt lgkmcnt(0)"
-               : "+v"(kr.k[0]), "+v"(kr.k[1]), "+v"(kr.k[2]), "+v"(kr.k[3]), "+v"(kr.k[4]), "+v"(kr.k[5]), "+v"(kr.k[6]), "+v"(kr.k[7]),
-                 "+v"(vr.v[0][0]), "+v"(vr.v[0][1]), "+v"(vr.v[0][2]), "+v"(vr.v[0][3]), "+v"(vr.v[0][4]), "+v"(vr.v[0][5]), "+v"(vr.v[0][6]), "+v"(vr.v[0][7]),
-                 "+v"(vr.v[1][0]), "+v"(vr.v[1][1]), "+v"(vr.v[1][2]), "+v"(vr.v[1][3]), "+v"(vr.v[1][4]), "+v"(vr.v[1][5]), "+v"(vr.v[1][6]), "+v"(vr.v[1][7]));
-}
-__device__ __forceinline__ void lds_operands_ready(KRegs<64>& kr, VRegs<64>& vr) {
-  asm volatile("s_waitcnt lgkmcnt(0)"
-               : "+v"(kr.k[0]), "+v"(kr.k[1]), "+v"(kr.k[2]), "+v"(kr.k[3]),
-                 "+v"(vr.v[0][0]), "+v"(vr.v[0][1]), "+v"(vr.v[0][2]), "+v"(vr.v[0][3]), "+v"(vr.v[1][0]), "+v"(vr.v[1][1]), "+v"(vr.v[1][2]), "+v"(vr.v[1][3]));
-}
 // Wait for the K reads of a stage issued before its V reads (LDS reads of a wave complete in
 // order, so at most the V reads may still be outstanding; the counter holds at most 15).
 template <int D>
@@ -508,6 +516,7 @@ __device__ __forceinline__ void lds_k_ready(KRegs<D>& kr) {
   else
     asm volatile("s_waitcnt lgkmcnt(8)" : "+v"(kr.k[0]), "+v"(kr.k[1]), "+v"(kr.k[2]), "+v"(kr.k[3]));
 }
+// Wait for every outstanding LDS read of the wave (K rows read with no V reads behind them).
 template <int D>
 __device__ __forceinline__ void lds_operands_ready(KRegs<D>& kr) {
   if constexpr (D == 128)
@@ -515,17 +524,7 @@ __device__ __forceinline__ void lds_operands_ready(KRegs<D>& kr) {
   else
     asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(kr.k[0]), "+v"(kr.k[1]), "+v"(kr.k[2]), "+v"(kr.k[3]));
 }
-template <int D>
-__device__ __forceinline__ void lds_operands_ready(VRegs<D>& vr) {
-  if constexpr (D == 128)
-    asm volatile("s_waitcnt lgkmcnt(0)"
-                 : "+v"(vr.v[0][0]), "+v"(vr.v[0][1]), "+v"(vr.v[0][2]), "+v"(vr.v[0][3]), "+v"(vr.v[0][4]), "+v"(vr.v[0][5]), "+v"(vr.v[0][6]), "+v"(vr.v[0][7]),
-                   "+v"(vr.v[1][0]), "+v"(vr.v[1][1]), "+v"(vr.v[1][2]), "+v"(vr.v[1][3]), "+v"(vr.v[1][4]), "+v"(vr.v[1][5]), "+v"(vr.v[1][6]), "+v"(vr.v[1][7]));
-  else
-    asm volatile("s_waitcnt lgkmcnt(0)"
-                 : "+v"(vr.v[0][0]), "+v"(vr.v[0][1]), "+v"(vr.v[0][2]), "+v"(vr.v[0][3]), "+v"(vr.v[1][0]), "+v"(vr.v[1][1]), "+v"(vr.v[1][2]), "+v"(vr.v[1][3]));
-}
-// The same wait for V, ordered after the packed weights P of the stage (they pass through it
+// The wait for V, ordered after the packed weights P of the stage (they pass through it
 // too): the scheduler may otherwise hoist the wait above the score products, so that these
 // would also wait for the V reads.
 template <int D>
@@ -1126,11 +1125,7 @@ __device__ __forceinline__ void chunk_tile(const AttnArgs& a, int32_t tile, char
   };
   // Wait for this wave's copies of the current stage (all but the `later` stages issued after
   // it), then the barrier.
-  auto wait_stage = [&](int32_t later) {
-    if (later >= 2) wait_vm_barrier<2 * CPW>();
-    else if (later == 1) wait_vm_barrier<CPW>();
-    else wait_vm_barrier<0>();
-  };
+  auto wait_stage = [&](int32_t later) { wait_vm_barrier_later<CPW, NS - 2>(later); };
 
   // Loop-invariant LDS read addresses of this lane in ring buffer 0 (bf16 operand reads; the
   // buffer is selected by an immediate offset).
@@ -1227,13 +1222,11 @@ __device__ __forceinline__ void chunk_tile(const AttnArgs& a, int32_t tile, char
       for (int p = 0; p < NS - 1; ++p) sload_ready(blk0[p]);
       constexpr std::false_type kAny{};
       constexpr std::true_type kSteady{};
-      if (0 < n_st) issue_s(0, std::integral_constant<int, 0>{}, blk0[0], kAny);
-      if (1 < n_st) issue_s(1, std::integral_constant<int, 1>{}, blk0[1], kAny);
-      if constexpr (NS > 3) {
-        if (2 < n_st) issue_s(2, std::integral_constant<int, 2>{}, blk0[2], kAny);
-      }
+      static_for<0, NS - 1>([&](auto P) {
+        if (decltype(P)::value < n_st) issue_s(decltype(P)::value, P, blk0[decltype(P)::value], kAny);
+      });
       int32_t blk_nx = sload_issue(blk_ptr(NS - 1));
-      float m_use = 0.f, raw_limit = kNegInf;     // m_run is -inf until the first rescale
+      float neg_m = 0.f, raw_limit = kNegInf;     // m_run is -inf until the first rescale
       wait_stage(min(NS - 2, n_st - 1));
       f32x16 s_cur = f32x16{};
       {
@@ -1256,7 +1249,7 @@ __device__ __forceinline__ void chunk_tile(const AttnArgs& a, int32_t tile, char
         constexpr bool steady = decltype(STEADY)::value;
         if (steady || jj + NS - 1 < n_st) sload_ready(blk_nx);   // ahead of the LDS reads, or it waits for them too
         if constexpr (steady) {
-          wait_vm_barrier<(NS - 3 >= 2 ? 2 : NS - 3) * CPW>();    // stage jj + 1 landed everywhere
+          wait_vm_barrier<(NS - 3) * CPW>();    // stage jj + 1 landed everywhere
         } else if (jj + 1 < n_st) {
           wait_stage(min(NS - 3, n_st - jj - 2));
         }
@@ -1279,21 +1272,21 @@ __device__ __forceinline__ void chunk_tile(const AttnArgs& a, int32_t tile, char
           for (int r = 0; r < 16; ++r)
             if (k0 + acc32_row(lane, r) > qpos) st[r] = kNegInf;
         }
-        float mx = max16_raw(st);
-        mx = half_xor_max(mx);
+        const float mx = max16_raw(st);   // over this lane's half of the row's keys
         // Lazy rescale: the weights are 2^(s c - m_ref) with m_ref a running maximum allowed to
         // lag the true one by up to kRescaleSlack (weights stay below 2^kRescaleSlack), so the
         // accumulator rescale and its exponential run only when some row's maximum jumps past it.
         // The test compares raw scores with (m_ref + slack) / c, kept beside m_ref (its rounding
-        // only moves the rare rescale by an ulp).
+        // only moves the rare rescale by an ulp).  The wave-wide vote sees both halves of every
+        // row, so the halves' maxima are merged only when it fires.
         if (__builtin_amdgcn_ballot_w64(mx > raw_limit)) {
-          const float m_new = fmaxf(m_run, mx * a.scale_log2);
+          const float m_new = fmaxf(m_run, half_xor_max(mx) * a.scale_log2);
           const float alpha = m_new == kNegInf ? 1.f : fast_exp2(m_run - m_new);
           l_run *= alpha;
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt) o[mt] *= alpha;
           m_run = m_new;
-          m_use = m_run == kNegInf ? 0.f : m_run;
+          neg_m = m_run == kNegInf ? 0.f : -m_run;
           raw_limit = (m_run + kRescaleSlack) / a.scale_log2;
         }
 
@@ -1306,7 +1299,7 @@ __device__ __forceinline__ void chunk_tile(const AttnArgs& a, int32_t tile, char
           mma32_k16(s_cur, kf, qf[ks]);
         }
 #pragma unroll
-        for (int r = 0; r < 16; ++r) st[r] = fast_exp2(fmaf(st[r], a.scale_log2, -m_use));
+        for (int r = 0; r < 16; ++r) st[r] = fast_exp2(fmaf(st[r], a.scale_log2, neg_m));
         Frag<T> pfs[2];
 #pragma unroll
         for (int ps = 0; ps < 2; ++ps) {
@@ -1317,18 +1310,16 @@ __device__ __forceinline__ void chunk_tile(const AttnArgs& a, int32_t tile, char
         }
         {
           // Row sums of the weights as rounded for the P V products (so numerator and
-          // denominator see the same weights): two chains of four bf16 pair dot products.
+          // denominator see the same weights): eight bf16 pair dot products into the running sum.
           typedef __attribute__((ext_vector_type(2))) __bf16 b2;
           const b2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
-          float la = 0.f, lb = 0.f;
           const uint32_t* u0 = &pfs[0].u.x;
           const uint32_t* u1 = &pfs[1].u.x;
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            la = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, u0[q]), one2, la, false);
-            lb = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, u1[q]), one2, lb, false);
+            l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, u0[q]), one2, l_run, false);
+            l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, u1[q]), one2, l_run, false);
           }
-          l_run += la + lb;
         }
         {
           u32x4 p0 = __builtin_bit_cast(u32x4, pfs[0].u), p1 = __builtin_bit_cast(u32x4, pfs[1].u);
@@ -1367,24 +1358,17 @@ __device__ __forceinline__ void chunk_tile(const AttnArgs& a, int32_t tile, char
       const int32_t n_whole = min(n_st, max(0, kv_end / kChunkKeys - kt_lo));
       const int32_t n_unmasked = max(0, (c + qb * a.bmq + 1) / kChunkKeys - kt_lo);
       const int32_t n_steady = max(0, min(n_whole - NS, n_unmasked));
-      static_assert(NS == 3 || NS == 4, "ring unrolled by its depth");
-      for (; j + NS <= n_steady; j += NS) {
-        step(j, std::integral_constant<int, 0>{}, kSteady);
-        step(j + 1, std::integral_constant<int, 1>{}, kSteady);
-        step(j + 2, std::integral_constant<int, 2 % NS>{}, kSteady);
-        if constexpr (NS > 3) step(j + 3, std::integral_constant<int, 3 % NS>{}, kSteady);
-      }
+      // Unrolled by the ring depth, so each stage's buffer is a compile-time constant.
+      for (; j + NS <= n_steady; j += NS)
+        static_for<0, NS>([&](auto B) { step(j + decltype(B)::value, B, kSteady); });
       while (j < n_st) {                             // the rest (j is a multiple of NS here)
-        step(j, std::integral_constant<int, 0>{}, kAny);
-        if (++j == n_st) break;
-        step(j, std::integral_constant<int, 1>{}, kAny);
-        if (++j == n_st) break;
-        step(j, std::integral_constant<int, 2 % NS>{}, kAny);
-        if (++j == n_st) break;
-        if constexpr (NS > 3) {
-          step(j, std::integral_constant<int, 3 % NS>{}, kAny);
-          if (++j == n_st) break;
-        }
+        bool done = false;
+        static_for<0, NS>([&](auto B) {
+          if (!done) {
+            step(j, B, kAny);
+            done = ++j == n_st;
+          }
+        });
       }
       sload_ready(blk_nx);                             // nothing left in flight
     }
