@@ -1527,9 +1527,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) =
 // ---------------------------------------------------------------------------------------------
 // Merge of split partials: m = max m_p, w_p = 2^(m_p - m), out = sum w_p o_p / sum w_p l_p.
 // ---------------------------------------------------------------------------------------------
-// FEW: every item has at most eight partials (a launch without decode rows: P = nsplit <= 8), so
-// the general path and its registers are compiled out.
-template <typename T, int D, bool FEW>
+// One wave per (row, head) item of a launch with decode rows; combine_split_kernel below merges
+// the key splits of a launch without them.
+template <typename T, int D>
 __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a, int32_t n_dec_rows, int32_t n_items) {
   constexpr int PER = D / 64;
   const int lane = threadIdx.x & 63;
@@ -1569,7 +1569,7 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a, int32_t n_dec_
     sml = 2;
   }
   T* orow = static_cast<T*>(a.out) + (static_cast<int64_t>(row) * a.Hq + h) * D;
-  if (FEW || P <= 8) {
+  if (P <= 8) {
     // Up to eight partials (every chunk split, most decode rows): each lane loads every (m, l)
     // pair (one broadcast load each) and PER adjacent elements of every partial o, all in
     // flight together, then merges serially in partial order -- no cross-lane steps.
@@ -1618,7 +1618,6 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a, int32_t n_dec_
     }
     return;
   }
-  if constexpr (FEW) return;
   // More partials (long decode rows split over many waves).  The first eight partials' o are
   // loaded up front, beside their (m, l) pairs: the weights need the reductions below, the loads
   // do not.
@@ -1689,6 +1688,65 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a, int32_t n_dec_
   }
 }
 
+// Key splits of a launch without decode rows (at most kMaxSplit partials per item, contiguous):
+// half a wave per (row, head) item, each lane D / 32 adjacent elements of every partial in one
+// load, so a launch has half the waves of one-item waves with twice the bytes each in flight.
+// Same merge, in the same order, as combine_kernel's path for up to eight partials.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void combine_split_kernel(AttnArgs a, int32_t n_items) {
+  constexpr int E = D / 32;
+  static_assert(E == 2 || E == 4, "head dim 64 or 128");
+  typedef __attribute__((ext_vector_type(E))) float fxE;
+  const int lane = threadIdx.x & 31;
+  const int64_t w = static_cast<int64_t>(blockIdx.x) * 8 + (threadIdx.x >> 5);
+  if (w >= n_items) return;
+  const int32_t P = a.nsplit;
+  const float* po = a.chk_o + w * P * D + E * lane;     // item w = (row - nd) Hq + head
+  const float* pml = a.chk_ml + w * P * 2;
+  float2 ml[kMaxSplit];
+  fxE xv[kMaxSplit];
+#pragma unroll
+  for (int v = 0; v < kMaxSplit; ++v) {
+    if (v < P) {
+      ml[v] = *reinterpret_cast<const float2*>(pml + 2 * v);
+      xv[v] = *reinterpret_cast<const fxE*>(po + v * D);
+    }
+  }
+  float m = kNegInf;
+#pragma unroll
+  for (int v = 0; v < kMaxSplit; ++v)
+    if (v < P) m = fmaxf(m, ml[v].x);
+  const float m_use = m == kNegInf ? 0.f : m;
+  float wv[kMaxSplit];
+  float Lsum = 0.f;
+#pragma unroll
+  for (int v = 0; v < kMaxSplit; ++v) {
+    wv[v] = v < P ? exp2f(ml[v].x - m_use) : 0.f;
+    if (v < P) Lsum += wv[v] * ml[v].y;
+  }
+  const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
+  float acc[E];
+#pragma unroll
+  for (int j = 0; j < E; ++j) acc[j] = 0.f;
+#pragma unroll
+  for (int v = 0; v < kMaxSplit; ++v)
+    if (v < P)
+#pragma unroll
+      for (int j = 0; j < E; ++j) acc[j] += (wv[v] * inv) * xv[v][j];
+  T* orow = static_cast<T*>(a.out) + (static_cast<int64_t>(a.nd) * a.Hq + w) * D + E * lane;
+  if constexpr (sizeof(T) == 2) {
+    if constexpr (E == 4)
+      *reinterpret_cast<uint2*>(orow) = make_uint2(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]));
+    else
+      *reinterpret_cast<uint32_t*>(orow) = pack_bf16x2(acc[0], acc[1]);
+  } else {
+    if constexpr (E == 4)
+      *reinterpret_cast<float4*>(orow) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    else
+      *reinterpret_cast<float2*>(orow) = make_float2(acc[0], acc[1]);
+  }
+}
+
 // Compute units of the device that owns the stream (cached per device).
 int compute_units(hipStream_t st) {
   static std::atomic<int> cached[64] = {};      // 0 = not looked up yet; any thread may fill it
@@ -1756,13 +1814,13 @@ int launch_all(hipStream_t st, const AttnArgs& a, const Plan& p, void* const* ev
   const int32_t n_chunk_rows = a.nsplit > 1 ? a.T - a.nd : 0;
   const int64_t items = static_cast<int64_t>(a.nd + n_chunk_rows) * a.Hq;
   if (items > 0) {
-    const int64_t grid = (items + 3) / 4;
+    const int64_t grid = a.nd == 0 ? (items + 7) / 8 : (items + 3) / 4;
     if (grid > 0x7fffffff) return CB_ERR_INVALID;
     rec(4);
     if (a.nd == 0)
-      combine_kernel<T, D, true><<<dim3(static_cast<uint32_t>(grid)), dim3(256), 0, st>>>(a, 0, static_cast<int32_t>(items));
+      combine_split_kernel<T, D><<<dim3(static_cast<uint32_t>(grid)), dim3(256), 0, st>>>(a, static_cast<int32_t>(items));
     else
-      combine_kernel<T, D, false><<<dim3(static_cast<uint32_t>(grid)), dim3(256), 0, st>>>(a, a.nd, static_cast<int32_t>(items));
+      combine_kernel<T, D><<<dim3(static_cast<uint32_t>(grid)), dim3(256), 0, st>>>(a, a.nd, static_cast<int32_t>(items));
     if (hipGetLastError() != hipSuccess) return CB_ERR_HIP;
     rec(5);
   }
