@@ -2,8 +2,9 @@
 
 Bar: every compared element within oracle.linear.bound (float32 accumulation in any order plus
 one rounding to bfloat16) -- a rigorous per-element bound rather than a fixed tolerance.  Small
-shapes are compared in full (several 128 x 128 tiles, ragged M, K of one and many stages); the
-full-size QKV and output projections of the budget-512 7B-like layer on sampled rows.
+shapes are compared in full (every tile shape -- 64 x 64 with K splits, 64 x 128, 128 x 192 and
+128 x 128 -- with ragged M, K of one and many stages); the full-size QKV and output projections
+of the budget-512 7B-like layer on sampled rows.
 """
 import numpy as np
 import pytest
@@ -52,7 +53,9 @@ def _check(x, w, y, rows=None):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 128, 64), (37, 256, 192), (130, 384, 64), (300, 128, 1024),
-                                   (257, 256, 4096)])
+                                   (257, 256, 4096),
+                                   (500, 12288, 128),     # 128 x 192 tiles, ragged last row tile
+                                   (1030, 4096, 128)])    # 128 x 128 tiles, ragged last row tile
 def test_linear_small_every_element(dev, M, N, K):
     x, w = _inputs(M, N, K, dev)
     y = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=dev)
