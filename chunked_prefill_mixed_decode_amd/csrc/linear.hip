@@ -20,10 +20,13 @@
 // compute-bound mixed step's rows, whose waves then hide one another's barrier and read latency;
 // four for a decode-only step's few rows, where the weight stream is the whole cost.  Tiles are
 // ordered so that the workgroups sharing one weight tile run on one XCD (workgroup b runs on XCD
-// b mod 8) and read it through that XCD's L2.  A layer with few tiles (a decode-only step's rows)
-// splits K so that at least 256 workgroups stream the weights: each split writes float32
-// partials and a second kernel sums them in split order (the split depends on the shape alone,
-// so results do not depend on the device).
+// b mod 8) and read it through that XCD's L2.  Few rows of a wide layer (the decode-only QKV
+// projection) take 64 x 32..64 tiles over all of K in 8-wave workgroups that split each stage's
+// depth between two wave halves and add the halves in LDS at the end, so 256 workgroups stream
+// the weights with no second kernel.  Other layers with few tiles split K so that at least 256
+// workgroups stream the weights: each split writes float32 partials and a second kernel sums them
+// in split order.  Either way the summation order depends on the shape alone, so results do not
+// depend on the device.
 #include <algorithm>
 #include <type_traits>
 
@@ -263,6 +266,119 @@ __global__ __launch_bounds__(64 * WM * WN) void linear_kernel(const bf16_t* __re
     }
 }
 
+// Few rows (M <= 64) of a layer wide enough for kMinWorkgroups tiles of 64 x BN: one 8-wave
+// workgroup per tile over all of K, so no K split and no second kernel.  A stage's 64 x rows and
+// BN weight rows are 8 + BN / 8 one-KB copies: wave v copies x rows 8 v .. 8 v + 7 and, for
+// v < BN / 8, weight rows 8 v .. 8 v + 7, into a ring of NS buffers with NS - 1 stages in flight.
+// Wave v multiplies row block v % 4 of x against the tile's BN / 16 column blocks over the 32-deep
+// half v / 4 of each stage (v_mfma_f32_16x16x32_bf16); at the end the second half's sums meet the
+// first's in LDS (first + second), so the result depends on the shape alone.
+template <int BN, int NS>
+__global__ __launch_bounds__(512) void linear_rows64_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict__ w,
+                                                            bf16_t* __restrict__ y, int32_t M, int32_t N, int32_t K) {
+  constexpr int NJ = BN / 16;                        // 16-column blocks of the tile
+  constexpr int WCP = BN / 8;                        // waves that also copy weight rows
+  static_assert(NJ * 16 == BN && WCP >= 1 && WCP <= 8 && NS >= 2, "tile width and ring depth");
+  constexpr int XBYTES = 64 * kRowBytes;             // copy c of a stage sits at 1024 c (x: c < 8)
+  constexpr int SBYTES = XBYTES + BN * kRowBytes;
+  __shared__ __attribute__((aligned(1024))) char lds[NS * SBYTES];
+  const int32_t n0 = blockIdx.x * BN;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const bool wcopy = wave < WCP;
+  const int32_t nk = K / kBK;
+  const uint32_t row_bytes = static_cast<uint32_t>(K) * 2u;
+  const int r = 8 * wave + (lane >> 3);              // tile row of this lane's copies
+  const uint32_t vx = static_cast<uint32_t>(min(r, M - 1)) * row_bytes + 16u * swz(lane & 7, r);
+  const uint32_t vw = static_cast<uint32_t>(r) * row_bytes + 16u * swz(lane & 7, r);
+  const char* xb = reinterpret_cast<const char*>(x);
+  const char* wb = reinterpret_cast<const char*>(w + static_cast<int64_t>(n0) * K);
+  const uint32_t l0 = __builtin_amdgcn_readfirstlane(lds_addr(lds));
+  auto issue = [&](int32_t kt, int buf) {
+    const uint32_t d = l0 + static_cast<uint32_t>(buf * SBYTES);
+    dma16_s(xb + static_cast<int64_t>(kt) * kRowBytes, vx, d + 1024u * wave);
+    if (wcopy) dma16_s(wb + static_cast<int64_t>(kt) * kRowBytes, vw, d + XBYTES + 1024u * wave);
+  };
+  // Wait for this wave's copies of the current stage (`later` stages issued after it may stay
+  // outstanding), then the barrier.
+  auto wait = [&](int32_t later) {
+    if (wcopy) wait_copies_barrier<2, NS - 2>(later);
+    else wait_copies_barrier<1, NS - 2>(later);
+  };
+
+  const int q = wave & 3, h = wave >> 2;
+  const int lr = lane & 15;
+  const int chunk = 4 * h + (lane >> 4);             // 16-byte chunk: K slots 32 h + 8 (l / 16) .. + 7
+  f32x4 acc[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int p = 0; p < NS - 1; ++p)
+    if (p < nk) issue(p, p);
+  int32_t s = 0;
+  auto stage = [&](auto B) {
+    constexpr int buf = decltype(B)::value;
+    wait(min(NS - 2, nk - 1 - s));                   // stage s landed everywhere; stage s - 1 read by all
+    if (s + NS - 1 < nk) issue(s + NS - 1, (buf + NS - 1) % NS);
+    const char* xt = lds + buf * SBYTES;
+    const char* wt = xt + XBYTES;
+    Frag<bf16_t> a, bw[NJ];
+    const int ra = 16 * q + lr;
+    a.u = *reinterpret_cast<const uint4*>(xt + ra * kRowBytes + 16 * swz(chunk, ra));
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int rb = 16 * j + lr;
+      bw[j].u = *reinterpret_cast<const uint4*>(wt + rb * kRowBytes + 16 * swz(chunk, rb));
+    }
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) mma16_k32(acc[j], a, bw[j]);
+  };
+  while (s < nk) {
+    bool done = false;
+    static_for<0, NS>([&](auto B) {
+      if (!done) {
+        stage(B);
+        done = ++s == nk;
+      }
+    });
+  }
+
+  // acc[j] register i: row 16 q + acc16_row(lane, i), column 16 j + lane % 16.  The ring is idle
+  // (every copy waited for, every read returned before the last barrier), so its first bytes hold
+  // the second half's sums.
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  float* red = reinterpret_cast<float*>(lds);
+  if (h == 1) {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[(16 * q + acc16_row(lane, i)) * BN + 16 * j + lr] = acc[j][i];
+  }
+  __syncthreads();
+  if (h == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int32_t row = 16 * q + acc16_row(lane, i);
+      if (row >= M) continue;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const float v = acc[j][i] + red[row * BN + 16 * j + lr];
+        reinterpret_cast<uint16_t*>(y)[static_cast<int64_t>(row) * N + n0 + 16 * j + lr] = f32_to_bf16_bits(v);
+      }
+    }
+  }
+}
+
+// Tile width of the few-rows kernel: the widest of 64, 48, 32 that divides N and gives at least
+// kMinWorkgroups tiles; 0 when none does (then 64 x 64 tiles with a K split).  Narrower tiles
+// would read x from L2 more than four times per weight byte (the budget-512 layer's output
+// projection with 64 x 16 tiles: 14.3 against 12.0 us split).
+int rows64_bn(int32_t M, int32_t N) {
+  if (M > 64) return 0;
+  for (int bn : {64, 48, 32})
+    if (N % bn == 0 && N / bn >= kMinWorkgroups) return bn;
+  return 0;
+}
+
 // y = the splits' partials summed in split order, rounded once to bfloat16 (4 outputs a thread).
 __global__ __launch_bounds__(256) void linear_reduce_kernel(const float* __restrict__ part, bf16_t* __restrict__ y,
                                                             int64_t n4, int64_t stride, int32_t splits) {
@@ -282,6 +398,7 @@ __global__ __launch_bounds__(256) void linear_reduce_kernel(const float* __restr
 extern "C" size_t cb_linear_workspace_bytes(int32_t M, int32_t N, int32_t K) {
   using namespace cb;
   if (M < 1 || N < 1 || K < 1 || N % kNAlign || K % kBK || K > kMaxK) return 0;
+  if (rows64_bn(M, N)) return 0;
   const TileShape ts = tile_shape(M, N);
   const int64_t tiles = ((static_cast<int64_t>(M) + ts.bm - 1) / ts.bm) * (N / ts.bn);
   const int32_t s = k_splits(tiles, K);
@@ -297,6 +414,16 @@ extern "C" int cb_linear(void* stream, int32_t dtype, int32_t M, int32_t N, int3
   if (!x || !w || !y) return CB_ERR_INVALID;
   for (const void* p : {x, w, static_cast<const void*>(y)})
     if (reinterpret_cast<uintptr_t>(p) & 15u) return CB_ERR_INVALID;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (const int bn = rows64_bn(M, N)) {
+    // Four stage buffers (three stages in flight): the budget-512 layer's QKV projection 19.4-20.2
+    // us, against 20.3-21.7 with three, five or eight and 34 with two.
+    auto k64 = bn == 64 ? linear_rows64_kernel<64, 4> : bn == 48 ? linear_rows64_kernel<48, 4>
+                        : linear_rows64_kernel<32, 4>;
+    k64<<<dim3(static_cast<uint32_t>(N / bn)), dim3(512), 0, st>>>(static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(w),
+                                                                     static_cast<bf16_t*>(y), M, N, K);
+    return hipGetLastError() == hipSuccess ? CB_OK : CB_ERR_HIP;
+  }
   const TileShape ts = tile_shape(M, N);
   const int64_t m_tiles = (static_cast<int64_t>(M) + ts.bm - 1) / ts.bm;
   const int64_t tiles = m_tiles * (N / ts.bn);
@@ -308,7 +435,6 @@ extern "C" int cb_linear(void* stream, int32_t dtype, int32_t M, int32_t N, int3
   const int64_t items = tiles * splits;
   const int64_t per_xcd = (items + 7) / 8;
   if (per_xcd * 8 > 0x7fffffff) return CB_ERR_INVALID;
-  hipStream_t st = static_cast<hipStream_t>(stream);
   float* part = static_cast<float*>(workspace);
   auto kernel = ts.bm == 64 && ts.bn == 64 ? linear_kernel<64, 64, 3, 2, 2>
                 : ts.bm == 64              ? linear_kernel<64, 128, 3, 2, 4>

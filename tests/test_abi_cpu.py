@@ -290,12 +290,15 @@ def test_workspace_grows_with_context_and_rows():
 
 def test_linear_workspace_depends_on_the_shape_only():
     f = cb.cb_linear_workspace_bytes
-    # enough 128 x 128 tiles: no split, no workspace
-    assert f(512, 12288, 4096) == 0
+    # enough tiles: no split, no workspace
+    assert f(512, 12288, 4096) == 0 and f(512, 4096, 4096) == 0
+    # few rows of a wide layer: 256 tiles of 64 x 48 or 64 x 32 over all of K, no workspace
+    assert f(64, 12288, 4096) == 0 and f(64, 8192, 4096) == 0 and f(17, 8192, 64) == 0
+    assert f(64, 4096, 4096) > 0                            # 64 x 16 tiles would re-read x too often
     # few tiles: K splits (a power of two dividing the 64-deep stages, >= 4 stages each)
-    s = f(64, 4096, 4096) // (64 * 4096 * 4)
-    assert s in (2, 4, 8, 16) and f(64, 4096, 4096) == s * 64 * 4096 * 4
-    assert f(64, 4096, 64 * 34) % (64 * 4096 * 4) == 0 and (34 % (f(64, 4096, 64 * 34) // (64 * 4096 * 4) or 1)) == 0
+    s = f(64, 2048, 4096) // (64 * 2048 * 4)
+    assert s in (2, 4, 8, 16) and f(64, 2048, 4096) == s * 64 * 2048 * 4
+    assert f(64, 2048, 64 * 34) % (64 * 2048 * 4) == 0 and (34 % (f(64, 2048, 64 * 34) // (64 * 2048 * 4) or 1)) == 0
     assert f(1, 128, 64) == 0                               # one stage: nothing to split
     for bad in ((0, 128, 64), (4, 100, 64), (4, 128, 96)):
         assert f(*bad) == 0

@@ -2,8 +2,9 @@
 
 Bar: every compared element within oracle.linear.bound (float32 accumulation in any order plus
 one rounding to bfloat16) -- a rigorous per-element bound rather than a fixed tolerance.  Small
-shapes are compared in full (every tile shape -- 64 x 64 with K splits, 64 x 128, 128 x 192 and
-128 x 128 -- with ragged M, K of one and many stages); the full-size QKV and output projections
+shapes are compared in full (every tile shape -- 64 x 64 with K splits, the few-rows tiles 64 x 32,
+48 and 64 over all of K, 64 x 128, 128 x 192 and 128 x 128 -- with ragged M, K of one and many
+stages); the full-size QKV and output projections
 of the budget-512 7B-like layer on sampled rows.
 """
 import numpy as np
@@ -54,6 +55,10 @@ def _check(x, w, y, rows=None):
 
 @pytest.mark.parametrize("M,N,K", [(1, 128, 64), (37, 256, 192), (130, 384, 64), (300, 128, 1024),
                                    (257, 256, 4096),
+                                   (64, 2048, 4096),      # 64 x 64 tiles, K split in eight
+                                   (1, 8192, 64), (37, 8192, 1024),   # 64 x 32 tiles over all of K
+                                   (50, 12288, 1088),     # 64 x 48 tiles
+                                   (9, 16384, 192),       # 64 x 64 tiles over all of K
                                    (500, 12288, 128),     # 128 x 192 tiles, ragged last row tile
                                    (1030, 4096, 128)])    # 128 x 128 tiles, ragged last row tile
 def test_linear_small_every_element(dev, M, N, K):
@@ -101,10 +106,10 @@ def test_linear_edge_cases(dev):
                                       yy.data_ptr() + 2, None, 0), "cb_linear")
     assert e.value.status == cb.CB_ERR_INVALID
     # a shape that splits K needs its workspace: too small -> CB_ERR_CAPACITY, nothing launched
-    need = cb.cb_linear_workspace_bytes(64, 4096, 4096)
+    need = cb.cb_linear_workspace_bytes(64, 2048, 4096)
     assert need > 0
-    x2, w2 = _inputs(64, 4096, 4096, dev)
-    y2 = torch.empty((64, 4096), dtype=torch.bfloat16, device=dev)
+    x2, w2 = _inputs(64, 2048, 4096, dev)
+    y2 = torch.empty((64, 2048), dtype=torch.bfloat16, device=dev)
     small = torch.empty(need - 16, dtype=torch.uint8, device=dev)
     with pytest.raises(cb.CbError) as e:
         cb.cb_linear(x2, w2, y2, small)
