@@ -180,8 +180,9 @@ int cb_copy_host_to_device(void* stream, const void* src, void* dst, size_t nbyt
  * e.g. hidden states before the QKV projection or attention outputs before the output
  * projection), w [N, K] (out_features x in_features), y [M, N]; row-major bfloat16 device
  * memory, float32 accumulation, one rounding to bfloat16 per output.  dtype must be CB_BF16;
- * M >= 0 (0 = nothing to do), N a multiple of 128, K a multiple of 64; x, w and y 16-byte aligned
- * and y not overlapping x or w.  A shape with few output tiles splits K over several workgroups:
+ * M >= 0 (0 = nothing to do), N a multiple of 128, K a multiple of 64 and at most 2^22; x, w and y
+ * 16-byte aligned and y not overlapping x or w.  A shape with few output tiles and no tile width
+ * that covers a wide layer's few rows (M <= 64) over all of K splits K over several workgroups:
  * their float32 partials go to the caller's device workspace (16-byte aligned, at least
  * cb_linear_workspace_bytes(M, N, K) bytes; NULL when that is 0) and are summed in a fixed order,
  * so results are bitwise reproducible and depend on the shape only.  Asynchronous on the stream;
