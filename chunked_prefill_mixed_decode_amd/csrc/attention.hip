@@ -126,6 +126,29 @@ struct Plan {
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
+// Chunk tiling of a launch for tiles of `rows` query rows: positions per query block, query blocks
+// per chunk, tiles before the key split, and the split: keys are split (and merged by the combine)
+// until the launch has CB_CHUNK_MIN_TILES 128-row tiles' worth of waves (CB_CHUNK_MIN_TILES_MIXED
+// beside decode rows) while each split keeps CB_CHUNK_SPLIT_KEYS keys of the longest context
+// (CB_CHUNK_SPLIT_KEYS_MIXED beside decode rows).
+struct ChunkSplit {
+  int32_t bmq = 1, q_blocks = 0, nsplit = 1;
+  int64_t tiles = 0;
+};
+ChunkSplit chunk_split(int32_t n_chunk, int32_t Hkv, int32_t G, int32_t rows, int32_t nd, int32_t max_q_len,
+                       int32_t max_ctx) {
+  ChunkSplit c;
+  c.bmq = rows / G;
+  if (n_chunk <= 0) return c;
+  c.q_blocks = (std::max(max_q_len, 1) + c.bmq - 1) / c.bmq;
+  c.tiles = static_cast<int64_t>(n_chunk) * c.q_blocks * Hkv;
+  const int64_t min_tiles = static_cast<int64_t>(nd > 0 ? CB_CHUNK_MIN_TILES_MIXED : CB_CHUNK_MIN_TILES) * kChunkRows / rows;
+  const int32_t min_keys = nd > 0 ? CB_CHUNK_SPLIT_KEYS_MIXED : CB_CHUNK_SPLIT_KEYS;
+  while (c.nsplit < kMaxSplit && c.tiles * c.nsplit < min_tiles && max_ctx / (2 * c.nsplit) >= min_keys)
+    c.nsplit *= 2;
+  return c;
+}
+
 // Partitioning decisions, shared by the workspace query and the launch so they always agree.
 // Decode partials: one slot per (unit, wave) pair that shares stages, at most units + waves
 // slots of hw heads each (a unit is a decode row's KV head and 16-head block).
@@ -136,16 +159,11 @@ Plan make_plan(int32_t num_seqs, int32_t nd, int32_t T, int32_t max_q_len, int32
   p.head_blocks = (p.G + 15) / 16;
   p.hw = std::min(16, p.G);
   p.ups = Hkv * p.head_blocks;
-  p.bmq = kChunkRows / p.G;
   p.n_chunk = num_seqs - nd;
-  if (p.n_chunk > 0) {
-    p.q_blocks = (std::max(max_q_len, 1) + p.bmq - 1) / p.bmq;
-    const int64_t tiles = static_cast<int64_t>(p.n_chunk) * p.q_blocks * Hkv;
-    const int64_t min_tiles = nd > 0 ? CB_CHUNK_MIN_TILES_MIXED : CB_CHUNK_MIN_TILES;
-    const int32_t min_keys = nd > 0 ? CB_CHUNK_SPLIT_KEYS_MIXED : CB_CHUNK_SPLIT_KEYS;
-    while (p.nsplit < kMaxSplit && tiles * p.nsplit < min_tiles && max_ctx / (2 * p.nsplit) >= min_keys)
-      p.nsplit *= 2;
-  }
+  const ChunkSplit cs = chunk_split(p.n_chunk, Hkv, p.G, kChunkRows, nd, max_q_len, max_ctx);
+  p.bmq = cs.bmq;
+  p.q_blocks = cs.q_blocks;
+  p.nsplit = cs.nsplit;
   size_t off = 0;
   const size_t dec_slots = nd > 0 ? static_cast<size_t>(nd) * p.ups + kMaxDecodeWaves : 0;
   p.dec_o = off;  off = align256(off + dec_slots * p.hw * D * sizeof(float));
@@ -183,6 +201,7 @@ struct AttnArgs {
   int32_t num_seqs, nd, T, Hq, Hkv, G, bs, bs_shift;
   int32_t head_blocks, hw, ups;
   int32_t bmq, q_blocks, n_chunk, nsplit;
+  int32_t max_q_len, max_ctx;
   float scale_log2;
 };
 
@@ -1003,14 +1022,19 @@ struct ChunkLds {
   static constexpr int BYTES = BLK + kBlockWindow * 4;
 };
 
-template <typename T, int D>
+// NWT waves (32 query rows each) per tile: 4 in every launch with decode rows, 8 (256 rows sharing
+// one K/V ring) in some launches without them.
+template <typename T, int D, int NWT = 4>
 __device__ __forceinline__ void chunk_tile(const AttnArgs& a, int32_t tile, char* lds) {
   constexpr int KS = D / 16;          // 16-slot contraction steps over the head dimension
   constexpr int MT = D / 32;          // 32-dim output tiles
   constexpr int ROW = D * sizeof(T);  // bytes per key row in LDS
   constexpr int RPI = 1024 / ROW;     // key rows per 1 KB copy instruction
-  constexpr int NCPW = kChunkKeys / RPI / 4;    // copy instructions per wave per tensor
-  static_assert(RPI <= kMinBlock && kChunkKeys % (4 * RPI) == 0, "a copy instruction's rows share a block");
+  constexpr int RPW = kChunkKeys / NWT;         // key rows each wave copies per stage
+  constexpr int NCPW = RPW / RPI;               // copy instructions per wave per tensor
+  constexpr int NT = 64 * NWT;                  // threads of the tile
+  static_assert(NCPW >= 1 && NCPW * RPI == RPW, "a wave's copies cover whole instructions");
+  static_assert(RPI <= kMinBlock && RPW <= kMinBlock, "a copy instruction's rows (and a wave's) share a block");
   constexpr int CPW = 2 * NCPW;                 // copy instructions per wave per stage
   constexpr int NS = ChunkLds<T, D>::NS;
   constexpr int STAGE = ChunkLds<T, D>::STAGE;  // bytes of K (and of V) per stage
@@ -1077,13 +1101,13 @@ __device__ __forceinline__ void chunk_tile(const AttnArgs& a, int32_t tile, char
   auto fill_window = [&](int32_t first_block) {   // all loads first, then all LDS writes
     win_lo = first_block;
     const int32_t n = min(kBlockWindow, n_blk - first_block);
-    int32_t ids[kBlockWindow / 256];
+    int32_t ids[kBlockWindow / NT];
 #pragma unroll
-    for (int u = 0; u < kBlockWindow / 256; ++u)
-      if (tid + 256 * u < n) ids[u] = btab[first_block + tid + 256 * u];
+    for (int u = 0; u < kBlockWindow / NT; ++u)
+      if (tid + NT * u < n) ids[u] = btab[first_block + tid + NT * u];
 #pragma unroll
-    for (int u = 0; u < kBlockWindow / 256; ++u)
-      if (tid + 256 * u < n) sBlk[tid + 256 * u] = ids[u];
+    for (int u = 0; u < kBlockWindow / NT; ++u)
+      if (tid + NT * u < n) sBlk[tid + NT * u] = ids[u];
     __builtin_amdgcn_s_waitcnt(0x0F70);   // no load left pending on any path (see below)
   };
   const int32_t k_last = kv_end - 1;
@@ -1161,14 +1185,13 @@ __device__ __forceinline__ void chunk_tile(const AttnArgs& a, int32_t tile, char
     // free once every wave has passed iteration jj's barrier (it read V of jj - 1 and K of jj in
     // iteration jj - 1), so stage jj + NS - 1's copy goes there: NS - 2 stages of work cover it.
     //
-    // Each wave copies 8 consecutive key rows of a stage (8 <= block size, 8-aligned), so they
-    // lie in one cache block: one block id per wave and stage, read by a scalar load one
+    // Each wave copies RPW consecutive key rows of a stage (RPW <= block size, RPW-aligned), so
+    // they lie in one cache block: one block id per wave and stage, read by a scalar load one
     // iteration before its copy is issued.  Rows past kv_end repeat kv_end - 1, which lies in the
     // same block as the wave's first real row.
     static_assert(NS >= 3, "pipelined ring needs three buffers");
-    static_assert(NCPW * RPI == 8, "each wave copies 8 rows of a stage");
     if (n_st > 0) {
-      const int32_t row_w = 8 * wave;
+      const int32_t row_w = RPW * wave;
       const int32_t* bt = btab;
       auto blk_ptr = [&](int32_t jj) { return bt + (min((kt_lo + jj) * kChunkKeys + row_w, k_last) >> bsh); };
       // LDS spans of this wave's copies in ring buffer 0 (wave-uniform integers).
@@ -1187,8 +1210,8 @@ __device__ __forceinline__ void chunk_tile(const AttnArgs& a, int32_t tile, char
           dk[jc] = dk0 + buf * STAGE + jc * 1024;
           dv[jc] = dv0 + buf * STAGE + jc * 1024;
         }
-        if (decltype(FULL)::value || k0 + row_w + 7 <= k_last) {   // the wave's rows are all real keys
-          // Its 8 rows are 8-aligned in one block: copy jc starts RPI jc rows further.
+        if (decltype(FULL)::value || k0 + row_w + RPW - 1 <= k_last) {   // the wave's rows are all real keys
+          // Its RPW rows are RPW-aligned in one block: copy jc starts RPI jc rows further.
           const int64_t roff = static_cast<int64_t>((k0 + row_w) & bmask) * ROW;
           const char* kb[NCPW];
           const char* vb[NCPW];
@@ -1524,6 +1547,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) =
   }
 }
 
+// Chunk tiles of NWT waves alone (a launch without decode rows that takes 256-row tiles).
+template <typename T, int D, int NWT>
+__global__ __launch_bounds__(64 * NWT) __attribute__((amdgpu_waves_per_eu(2))) void chunk_only_kernel(
+    AttnArgs a, int32_t n_tiles, int32_t per_xcd) {
+  __shared__ __attribute__((aligned(1024))) char lds[ChunkLds<T, D>::BYTES];
+  const int32_t tile = static_cast<int32_t>(chunk_wg_tile(blockIdx.x, per_xcd));
+  if (tile < n_tiles) chunk_tile<T, D, NWT>(a, tile, lds);
+}
+
 // ---------------------------------------------------------------------------------------------
 // Merge of split partials: m = max m_p, w_p = 2^(m_p - m), out = sum w_p o_p / sum w_p l_p.
 // ---------------------------------------------------------------------------------------------
@@ -1785,10 +1817,29 @@ int32_t decode_waves(hipStream_t st, bool has_chunks) {
 // a host-made plan, which a.dec_seq / dec_wave / dec_par then point into), the attention kernel
 // (decode waves and chunk tiles together) and the combine.
 template <typename T, int D>
-int launch_all(hipStream_t st, const AttnArgs& a, const Plan& p, void* const* events, bool planned) {
+int launch_all(hipStream_t st, const AttnArgs& a0, const Plan& p, void* const* events, bool planned) {
   auto rec = [&](int i) {
     if (events && events[i]) (void)hipEventRecord(static_cast<hipEvent_t>(events[i]), st);
   };
+  AttnArgs a = a0;
+  // A launch without decode rows (bf16, head dim 128) takes 8-wave tiles of 256 rows when its
+  // longest chunk fills one and the tiles give every compute unit a workgroup without a key
+  // split: one K/V ring then serves twice the rows (long-context chunk-only launch 15.2 -> 14.8
+  // ms).  Where keys must be split (the budget-512 layer's chunks) they measured no faster, so
+  // those keep 4-wave tiles.  No split needs no chunk partials, so the workspace sized by the
+  // 4-wave plan suffices.
+  bool wide = false;
+  if constexpr (sizeof(T) == 2 && D == 128) {
+    if (a.nd == 0 && a.n_chunk > 0) {
+      const ChunkSplit w8 = chunk_split(a.n_chunk, a.Hkv, a.G, 2 * kChunkRows, 0, a.max_q_len, a.max_ctx);
+      if (a.max_q_len >= w8.bmq && w8.nsplit == 1 && w8.tiles >= compute_units(st)) {
+        wide = true;
+        a.bmq = w8.bmq;
+        a.q_blocks = w8.q_blocks;
+        a.nsplit = w8.nsplit;
+      }
+    }
+  }
   const TileGrid tg = tile_grid(a.nd, a.Hkv, a.n_chunk, a.q_blocks, a.nsplit, a.bmq);
   const int64_t n_tiles = tg.n_tiles, per_xcd = tg.per_xcd;
   int32_t n_dec_wg = 0;
@@ -1804,9 +1855,16 @@ int launch_all(hipStream_t st, const AttnArgs& a, const Plan& p, void* const* ev
   if (grid > 0) {
     rec(0);
     rec(2);
-    attn_kernel<T, D><<<dim3(static_cast<uint32_t>(grid)), dim3(256), 0, st>>>(
-        a, a.dec_seq, a.dec_wave, a.dec_pos, a.dec_par, a.ctx_lens, a.cu_blocks, n_dec_wg,
-        static_cast<int32_t>(n_tiles), static_cast<int32_t>(per_xcd));
+    if constexpr (sizeof(T) == 2 && D == 128) {
+      if (wide)
+        chunk_only_kernel<T, D, 8><<<dim3(static_cast<uint32_t>(grid)), dim3(512), 0, st>>>(
+            a, static_cast<int32_t>(n_tiles), static_cast<int32_t>(per_xcd));
+    }
+    if (!wide) {
+      attn_kernel<T, D><<<dim3(static_cast<uint32_t>(grid)), dim3(256), 0, st>>>(
+          a, a.dec_seq, a.dec_wave, a.dec_pos, a.dec_par, a.ctx_lens, a.cu_blocks, n_dec_wg,
+          static_cast<int32_t>(n_tiles), static_cast<int32_t>(per_xcd));
+    }
     if (hipGetLastError() != hipSuccess) return CB_ERR_HIP;
     rec(1);
     rec(3);
@@ -1974,6 +2032,7 @@ extern "C" int cb_mixed_paged_attention_timed(
   a.bs_shift = __builtin_ctz(static_cast<unsigned>(block_size));
   a.head_blocks = p.head_blocks; a.hw = p.hw; a.ups = p.ups;
   a.bmq = p.bmq; a.q_blocks = p.q_blocks; a.n_chunk = p.n_chunk; a.nsplit = p.nsplit;
+  a.max_q_len = max_q_len; a.max_ctx = max_ctx;
   a.scale_log2 = scale * 1.4426950408889634f;
 
   hipStream_t st = static_cast<hipStream_t>(stream);

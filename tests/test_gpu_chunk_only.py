@@ -5,8 +5,9 @@ tiles), so its tiles and its combine differ from those of the mixed launch the s
 part in.  Each step of a workload runs as usual; then the step's chunk rows are launched alone
 (the cache holds every key they see by then) and compared with the oracle's fp64 attention of the
 same rows: every chunk row of the scaled-down bfloat16 workloads (GQA groups, head dim 64, several
-chunks per launch, prefill-only steps), and at the budget-512 layer every step (128 to 512 tiles,
-unsplit, two-, four- and eight-way splits) on the first 64, the last 64 and 128 seeded random
+chunks per launch, prefill-only steps), at the budget-512 layer every step (128 to 512 tiles,
+unsplit, two-, four- and eight-way splits), and a 1024-row GQA-8 chunk whose launch takes 256
+unsplit 8-wave tiles of 256 rows, these two on the first 64, the last 64 and 128 seeded random
 chunk rows.
 """
 import numpy as np
@@ -97,6 +98,17 @@ def test_small_chunk_rows_alone(dev, i):
         step += 1
 
 
+def sampled_rows(nd: int, T: int, seed: int):
+    """The first 64, the last 64 and 128 seeded random chunk rows."""
+    rng = np.random.default_rng(seed)
+    chunk = np.arange(nd, T)
+    rows = set(chunk[:64].tolist()) | set(chunk[-64:].tolist())
+    rest = chunk[64:-64]
+    if len(rest):
+        rows |= set(rng.choice(rest, size=min(128, len(rest)), replace=False).tolist())
+    return rows
+
+
 def test_budget512_chunk_rows_alone(dev):
     w = workloads.get(2)
     g = DeviceRun(w, dev)
@@ -106,10 +118,25 @@ def test_budget512_chunk_rows_alone(dev):
         meta, dm, q_rot = run_step(g)
         nd, T = meta.num_decodes, meta.num_tokens
         out_c = chunk_only(g, meta, dm, q_rot)
-        rng = np.random.default_rng(100 + step)
-        chunk = np.arange(nd, T)
-        rows = set(chunk[:64].tolist()) | set(chunk[-64:].tolist())
-        rest = chunk[64:-64]
-        if len(rest):
-            rows |= set(rng.choice(rest, size=min(128, len(rest)), replace=False).tolist())
-        check(ora, plan, out_c, nd, rows, f"[{w.name}] step {step} ({tiles_of(w, meta)} tiles)", w.dtype)
+        check(ora, plan, out_c, nd, sampled_rows(nd, T, 100 + step),
+              f"[{w.name}] step {step} ({tiles_of(w, meta)} tiles)", w.dtype)
+
+
+def test_wide_tiles_chunk_rows_alone(dev):
+    """64 query / 8 KV heads, head dim 128, block 32: two decodes and a 1024-row chunk after 256
+    cached tokens.  Launched alone, the chunk fills 32 x 8 = 256 tiles of 256 rows (32 positions x
+    8 heads) without a key split, which a 256-compute-unit device runs as 8-wave tiles."""
+    rng = np.random.Generator(np.random.PCG64(2010))
+    ctx = rng.integers(100, 600, size=2, endpoint=True)
+    w = workloads._make("wide_gqa8_chunk1024_bf16", "bf16", 64, 8, 128, 32, 1026, ctx, ((1280, 256),), 1,
+                        2010, rng)
+    g = DeviceRun(w, dev)
+    ora = OracleRun(w, value_device=dev)
+    plan = ora.build()
+    meta, dm, q_rot = run_step(g)
+    nd, T = meta.num_decodes, meta.num_tokens
+    assert T - nd == 1024
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    say(f"  256-row tiles: {-(-1024 // 32) * 8}, compute units: {cus}")
+    out_c = chunk_only(g, meta, dm, q_rot)
+    check(ora, plan, out_c, nd, sampled_rows(nd, T, 110), f"[{w.name}] (256 unsplit 256-row tiles)", w.dtype)
