@@ -18,7 +18,7 @@
 // operands while the current step's products run, and the stage barrier sits before a stage's
 // last step, so the next stage's first reads overlap it.  Eight waves (two per SIMD) for the
 // compute-bound mixed step's rows, whose waves then hide one another's barrier and read latency;
-// four for a decode-only step's few rows, where the weight stream is the whole cost.  Tiles are
+// four for the 64 x 64 tiles of few rows whose K is split (below).  Tiles are
 // ordered so that the workgroups sharing one weight tile run on one XCD (workgroup b runs on XCD
 // b mod 8) and read it through that XCD's L2.  Few rows of a wide layer (the decode-only QKV
 // projection) take 64 x 32..64 tiles over all of K in 8-wave workgroups that split each stage's
