@@ -122,13 +122,15 @@ def test_budget512_chunk_rows_alone(dev):
               f"[{w.name}] step {step} ({tiles_of(w, meta)} tiles)", w.dtype)
 
 
-def test_wide_tiles_chunk_rows_alone(dev):
-    """64 query / 8 KV heads, head dim 128, block 32: two decodes and a 1024-row chunk after 256
-    cached tokens.  Launched alone, the chunk fills 32 x 8 = 256 tiles of 256 rows (32 positions x
-    8 heads) without a key split, which a 256-compute-unit device runs as 8-wave tiles."""
+@pytest.mark.parametrize("bs", [8, 32, 256])
+def test_wide_tiles_chunk_rows_alone(dev, bs):
+    """64 query / 8 KV heads, head dim 128, blocks of 8, 32 or 256 tokens: two decodes and a
+    1024-row chunk after 256 cached tokens.  Launched alone, the chunk fills 32 x 8 = 256 tiles of
+    256 rows (32 positions x 8 heads) without a key split, which a 256-compute-unit device runs as
+    8-wave tiles (each wave copies 4 key rows of a stage, inside one block of any size)."""
     rng = np.random.Generator(np.random.PCG64(2010))
     ctx = rng.integers(100, 600, size=2, endpoint=True)
-    w = workloads._make("wide_gqa8_chunk1024_bf16", "bf16", 64, 8, 128, 32, 1026, ctx, ((1280, 256),), 1,
+    w = workloads._make(f"wide_gqa8_chunk1024_bs{bs}_bf16", "bf16", 64, 8, 128, bs, 1026, ctx, ((1280, 256),), 1,
                         2010, rng)
     g = DeviceRun(w, dev)
     ora = OracleRun(w, value_device=dev)
