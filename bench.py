@@ -19,8 +19,9 @@ measured with HIP events on the launch stream over every launch of a dedicated p
 cycles after the timed loop (at least 20 launches).  ``isolated`` times decode-only and
 chunk-only launches of the same metadata, warm and with L2 and MALL evicted by a read-only sweep.
 ``graph_replay`` times the same steps replayed from HIP graphs (one per step shape, and with
-padded token buckets), on this workload and on a serving-like stream whose token count changes
-every step.  ``cpu_baseline`` times the CPU oracle (reference builder + rotary embedding + fp64
+padded token buckets), on this workload, on a serving-like stream whose token count changes
+every step, and on a scaled-down workload whose short device steps leave the host's launches
+setting the step time.  ``cpu_baseline`` times the CPU oracle (reference builder + rotary embedding + fp64
 full-prefill attention) on every step of the cycle: all decode rows and a fixed subset of each
 step's chunk rows, extrapolated to whole steps.
 """
@@ -522,6 +523,28 @@ def stream_graph_leg(dev, steps: int):
     return res
 
 
+def launch_bound_graph_leg(dev, steps: int):
+    """graph_legs on a scaled-down workload whose device step (tens of microseconds) is shorter
+    than the host's build and launches (5 query heads, 4 decodes at 300 cached tokens and a
+    600-token prompt in 128-token chunks, a 6-step cycle): there the host's launch cost sets the
+    step time, the regime in which replaying a captured step saves time."""
+    from synth import workloads
+    from tests.gpu_harness import DeviceRun
+    w = workloads.small(3)
+    g = DeviceRun(w, dev, sentinel=False)
+    cb = g.cb
+    snap = cb.cb_sched_clone(g.sched)
+    probe = cb.cb_sched_clone(snap)
+    bufs = cb.StepBuffers(*g.runner.bufs[0].cap)
+    inputs = []
+    for _ in range(w.steps):
+        meta = cb.cb_build_step(probe, w.budget, bufs)
+        inputs.append(g.step_inputs(meta))
+    res = graph_legs(g, w, snap, inputs, w.steps, steps)
+    res["tokens_per_step_range"] = [min(x[0].shape[0] for x in inputs), max(x[0].shape[0] for x in inputs)]
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -667,6 +690,7 @@ def main():
         print("[bench] graph replay legs...", file=sys.stderr, flush=True)
         graph_rep = graph_legs(g, w, snapshot, inputs, cb_steps, args.steps)
         graph_rep["varying"] = stream_graph_leg(dev, args.steps)
+        graph_rep["launch_bound"] = launch_bound_graph_leg(dev, args.steps)
         state["sched"], state["k"] = cb.cb_sched_clone(snapshot), 0
 
     # End-to-end latency: host wall time from cb_build_step to stream sync after attention.
