@@ -17,7 +17,8 @@ waves stream the cache, bound by HBM): algorithmic bytes per launch (K and V of 
 context and of every chunk's visible keys, plus q and out) divided by its average duration,
 measured with HIP events on the launch stream over every launch of a dedicated pass of whole
 cycles after the timed loop (at least 20 launches).  ``isolated`` times decode-only and
-chunk-only launches of the same metadata, warm and with L2 and MALL evicted by a read-only sweep.
+chunk-only launches of the same metadata, warm and with L2 and MALL evicted by a read-only sweep,
+and beside them the same chunks through torch's attention library (a reference point).
 ``graph_replay`` times the same steps replayed from HIP graphs (one per step shape, and with
 padded token buckets), on this workload, on a serving-like stream whose token count changes
 every step, and on a scaled-down workload whose short device steps leave the host's launches
@@ -282,6 +283,53 @@ def summarize_isolated(dec, chk, metas, w, elt):
            "chunk_TFLOPs_per_step": {str(k): chunk_flops(metas[k], w) / (sum(v) / len(v) / 1e3) / 1e12
                                      for k, v in sorted(per_step.items())}}
     return out
+
+
+def library_attention(metas, w, dev, reps: int = 3, max_keys: int = 65536):
+    """The chunk rows of each step through torch's scaled_dot_product_attention (the ROCm
+    attention libraries; a reference point, never the product path): per chunk, contiguous
+    [1, H, len, D] query, key and value tensors of random bf16 values with a bottom-right causal
+    mask (row i of a chunk after c cached keys sees keys 0..c + i), timed with HIP events over
+    ``reps`` calls per step after one untimed call.  The library reads contiguous keys, not the
+    paged cache.  None when a chunk sees more than ``max_keys`` keys."""
+    import torch
+    from torch.nn.attention.bias import causal_lower_right
+    steps, flops = [], 0
+    for k, meta in enumerate(metas):
+        nd, S = meta.num_decodes, meta.num_seqs
+        cu = meta.host["cu_seqlens_q"]
+        ctx = meta.host["context_lens"]
+        shapes = [(int(cu[s + 1] - cu[s]), int(ctx[s])) for s in range(nd, S)]
+        if not shapes:
+            continue
+        if max(c for _, c in shapes) > max_keys:
+            return None
+        ts = []
+        for d, c in shapes:
+            q = torch.randn(1, w.Hq, d, w.D, dtype=torch.bfloat16, device=dev)
+            kv = [torch.randn(1, w.Hkv, c, w.D, dtype=torch.bfloat16, device=dev) for _ in range(2)]
+            mask = causal_lower_right(d, c)
+
+            def call():
+                return torch.nn.functional.scaled_dot_product_attention(q, kv[0], kv[1], attn_mask=mask,
+                                                                        enable_gqa=w.Hq != w.Hkv)
+            call()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                call()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) / reps * 1e3)
+        steps.append(sum(ts))
+        flops += chunk_flops(meta, w)
+    if not steps:
+        return None
+    tot = sum(steps)
+    return {"us_per_step": tot / len(steps), "TFLOPs": flops / tot / 1e6,
+            "frac_mfma": flops / tot / 1e6 / MFMA_BF16_PEAK_TFLOPS,
+            "note": "torch scaled_dot_product_attention on each step's chunks (contiguous K/V, bottom-right "
+                    "causal mask, random bf16 values); a library reference point beside chunk_frac_mfma"}
 
 
 def cpu_baseline(w, n_steps: int, chunk_rows: int, decode_rows: int):
@@ -707,6 +755,7 @@ def main():
     iso = summarize_isolated(dec_raw, chk_raw, metas, w, elt)
     iso["note"] = ("decode-only and chunk-only launches of the same step metadata, 3 timed per step and kind, "
                    "back to back after one untimed launch")
+    iso["library_chunk_attention"] = library_attention(metas, w, dev)
     flush = torch.ones(256 << 20, dtype=torch.int32, device=dev)    # 1 GiB, written once here
     torch.cuda.synchronize()
     iso_cold = summarize_isolated(*isolation_pass(g, metas, qrots, outs, w, reps=2, flush=flush), metas, w, elt)
