@@ -5,7 +5,9 @@ block size (8 to 256), the element type (bf16, or float32 one time in five), 0 t
 decodes with contexts U[1, 1500], 1 to 3 prompts of U[1, 900] tokens (some with a cached prefix)
 and a token budget that leaves room for a chunk beside the decodes, then runs the workload until
 every prompt has had its last chunk.  Every step: metadata and every written K/V slot bit-exact,
-the rotated queries bit-exact, every output row within the tolerance of its element type.
+the rotated queries bit-exact, every output row within the tolerance of its element type; then
+the step's chunk rows launched alone (their own key split and combine), every row again.  Beside
+them, random shapes through cb_linear against its rigorous bound.
 """
 import numpy as np
 import pytest
@@ -13,6 +15,7 @@ import torch
 
 from synth import workloads
 from tests.harness import DeviceRun, OracleRun
+from tests.test_gpu_chunk_only import chunk_only
 from tests.test_gpu_parity import check_metadata, check_outputs, check_q_rot, check_step_kv, say
 
 pytestmark = pytest.mark.gpu
@@ -41,6 +44,21 @@ def fuzz_workload(seed: int) -> workloads.Workload:
                            prompts, None, 5000 + seed, rng, max_steps=32)
 
 
+def run_step(g: DeviceRun):
+    """One step (build, pull, rope + append, attention); returns the metadata, its device views,
+    the output and the rotated queries."""
+    g.arrive(g.step_index)
+    g.step_index += 1
+    meta = g.runner.build(g.sched, g.w.budget)
+    dm = g.runner.upload(meta)
+    q, k, v = g.step_inputs(meta)
+    q_rot, out = torch.empty_like(q), torch.empty_like(q)
+    g.runner.append(dm, q, k, v, q_rot)
+    g.runner.attend(meta, dm, q_rot, out)
+    g.written += meta.num_tokens
+    return meta, dm, out, q_rot
+
+
 @pytest.fixture(scope="module")
 def dev():
     assert torch.cuda.is_available(), "the gpu tests need a GPU"
@@ -58,12 +76,38 @@ def test_fuzz_workload_every_row_every_step(dev, seed):
     step = 0
     while ora.b.pending_prompts() > 0:
         plan = ora.build()
-        meta, out, q_rot = gpu.step()
+        meta, dm, out, q_rot = run_step(gpu)
         torch.cuda.synchronize()
         check_metadata(meta, plan)
         rows = set(range(plan["num_tokens"]))
         check_step_kv(gpu, ora, plan, rows)
         check_q_rot(gpu, ora, plan, q_rot, rows)
         check_outputs(gpu, ora, plan, out, None, f"step {step}")
+        nd, T = plan["num_decodes"], plan["num_tokens"]
+        if T > nd and nd > 0:                 # (without decodes the step itself was chunk-only)
+            alone = torch.zeros_like(out)
+            alone[nd:] = chunk_only(gpu, meta, dm, q_rot)
+            check_outputs(gpu, ora, plan, alone, set(range(nd, T)), f"step {step}, chunk rows alone")
         step += 1
         assert step <= w.max_steps
+
+
+LINEAR_CASES = 8
+
+
+@pytest.mark.parametrize("seed", range(LINEAR_CASES))
+def test_fuzz_linear_shapes(dev, seed):
+    from chunked_prefill_mixed_decode_amd import binding as cb
+    from tests.test_gpu_linear import _check, _inputs, _ws
+    rng = np.random.default_rng(7000 + seed)
+    while True:
+        M = int(rng.integers(1, 1100, endpoint=True))
+        N = 128 * int(rng.integers(1, 96, endpoint=True))
+        K = 64 * int(rng.integers(1, 64, endpoint=True))
+        if M * N * K <= 2_000_000_000:
+            break
+    x, w = _inputs(M, N, K, dev, seed=20 + seed)
+    y = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=dev)
+    cb.cb_linear(x, w, y, _ws(M, N, K, dev))
+    torch.cuda.synchronize()
+    _check(x, w, y)
