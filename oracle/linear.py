@@ -34,11 +34,13 @@ def bound(x, w) -> np.ndarray:
     gamma_K * sum_k |x w| for the accumulation (Higham, "Accuracy and Stability of Numerical
     Algorithms", 2nd ed., §3.1, with gamma_K = K u / (1 - K u)) plus the final rounding's half ulp
     of the accumulated value."""
-    x = np.abs(np.asarray(x, dtype=np.float64))
-    w = np.abs(np.asarray(w, dtype=np.float64))
+    x = np.asarray(x, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
     K = x.shape[1]
     gamma = K * F32_UNIT / (1.0 - K * F32_UNIT)
-    acc = gamma * (x @ w.T)
+    acc = gamma * (np.abs(x) @ np.abs(w).T)           # float32 accumulation error, any order
+    # The accumulated value s satisfies |s| <= |exact| + acc; rounding it to bf16 moves it by at
+    # most half an ulp of |s|.
     return BF16_HALF_ULP * (np.abs(linear(x, w)) + acc) + acc
 
 

@@ -50,6 +50,25 @@ def test_bound_holds_for_a_float32_sum_rounded_to_bf16():
     assert not np.all(np.abs((exact + 4 * lim) - exact) <= lim)
 
 
+def test_bound_sees_one_bf16_ulp():
+    # The final rounding's term scales with the accumulated value, not with sum |x w|: with random
+    # signs |exact| ~ sqrt(K) while sum |x w| ~ K.  At a depth where the accumulation term is small
+    # (K = 256) an output moved by 1.5 bf16 ulps of the exact value leaves the bound wherever the
+    # value is not tiny (a half ulp of |s| is bounded by 2^-8 |s|, up to one ulp at the top of a
+    # binade); a rounding term built on sum |x w| would have hidden it.
+    K = 256
+    x = bf16_round(matrix_values(6, "hidden", 16, K).numpy())
+    w = bf16_round(matrix_values(6, "w_qkv", 32, K, scale=K ** -0.5).numpy())
+    exact = olin.linear(x, w)
+    lim = olin.bound(x, w)
+    big = np.abs(exact) > 0.5
+    assert big.sum() > 100
+    ulp = 2.0 ** (np.floor(np.log2(np.abs(exact[big]))) - 7)       # bf16 ulp of each value
+    assert np.all(1.5 * ulp > lim[big])
+    sabs = olin.linear(np.abs(x), np.abs(w))
+    assert np.mean(2.0 ** -8 * sabs[big] > 1.5 * ulp) > 0.9         # the wider term admits most
+
+
 def test_flops_and_weight_intensity():
     # "Splitting Prefill From Decode Inside a Step": 2 N T operations for N parameters and T tokens;
     # with 2-byte weights read once that is T FLOP per weight byte (512 for a 512-token chunk, the
