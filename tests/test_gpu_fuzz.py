@@ -92,6 +92,53 @@ def test_fuzz_workload_every_row_every_step(dev, seed):
         assert step <= w.max_steps
 
 
+POLICY_CASES = 16
+
+
+def fuzz_policy(seed: int) -> dict:
+    """A random builder configuration: the priority order (decode-first, prefill-first, fair share
+    with a random decode share), and sometimes a per-request chunk cap, a prefill floor, a cap on
+    partial prefills per step and a prefill quota."""
+    rng = np.random.Generator(np.random.PCG64(6000 + seed))
+    cfg = {"policy": int(rng.integers(0, 2, endpoint=True))}
+    if cfg["policy"] == 2:
+        cfg["decode_share_pct"] = int(rng.integers(10, 60, endpoint=True))
+    if rng.random() < 0.5:
+        cfg["max_chunk"] = int(rng.integers(16, 200, endpoint=True))
+    if rng.random() < 0.5:
+        cfg["prefill_floor"] = int(rng.integers(8, 64, endpoint=True))
+    if rng.random() < 0.3:
+        cfg["max_partial_prefills"] = int(rng.integers(1, 3, endpoint=True))
+    if cfg["policy"] == 0 and rng.random() < 0.4:
+        cfg["prefill_quota_pct"] = int(rng.integers(10, 50, endpoint=True))
+    return cfg
+
+
+@pytest.mark.parametrize("seed", range(POLICY_CASES))
+def test_fuzz_policies_every_row_every_step(dev, seed):
+    """The random workloads under random builder configurations (deferred decodes, several partial
+    prefills per step, capped chunks): every row of every step against the oracle builder run
+    with the same configuration."""
+    w = fuzz_workload(100 + seed)
+    cfg = fuzz_policy(seed)
+    say(f"[{w.name}] {cfg}, decodes {list(w.decode_ctx)}, prompts {list(w.prompts)}, budget {w.budget}")
+    gpu = DeviceRun(w, dev, sched_cfg=cfg)
+    ora = OracleRun(w, value_device=dev, sched_cfg=cfg)
+    step = 0
+    while ora.b.pending_prompts() > 0:
+        plan = ora.build()
+        meta, dm, out, q_rot = run_step(gpu)
+        torch.cuda.synchronize()
+        check_metadata(meta, plan)
+        if plan["num_tokens"]:
+            rows = set(range(plan["num_tokens"]))
+            check_step_kv(gpu, ora, plan, rows)
+            check_q_rot(gpu, ora, plan, q_rot, rows)
+            check_outputs(gpu, ora, plan, out, None, f"step {step}")
+        step += 1
+        assert step <= w.max_steps
+
+
 LINEAR_CASES = 8
 
 
