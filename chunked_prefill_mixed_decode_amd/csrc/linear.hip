@@ -212,9 +212,13 @@ __global__ __launch_bounds__(64 * WM * WN) void linear_kernel(const bf16_t* __re
     for (int i = 0; i < MI; ++i)
 #pragma unroll
       for (int j = 0; j < NJ; ++j) mma32_k16(acc[i][j], o.a[i], o.b[j]);
-    // The next step's operand reads (issued just before) go ahead of these products.
-    __builtin_amdgcn_sched_group_barrier(0x100, MI + NJ, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, MI * NJ, 0);
+    // With one product per step, the next step's operand reads (issued just before) are put ahead
+    // of it (the 64 x 128 tiles: 2% faster); wider wave blocks measured faster without the hint
+    // (128 x 192: 3%).
+    if constexpr (MI * NJ == 1) {
+      __builtin_amdgcn_sched_group_barrier(0x100, MI + NJ, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, MI * NJ, 0);
+    }
   };
 
   const int32_t pro = min(NS, nk);
