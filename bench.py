@@ -51,10 +51,6 @@ def parse():
     ap.add_argument("--config", type=int, default=2, help="workload index (default: the budget-512 layer)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--json-out", default=None)
-    ap.add_argument("--event-every", type=int, default=7,
-                    help="record the per-kernel and per-step HIP events on every n-th timed step "
-                         "(each event record costs the GPU a few microseconds; 7 is coprime with "
-                         "the ten-step cycle, so every step kind is sampled)")
     ap.add_argument("--no-graphs", action="store_true",
                     help="skip the HIP-graph legs (replays of the same steps, exact shapes and "
                          "padded buckets, on this workload and on the serving-like stream)")
@@ -687,47 +683,35 @@ def main():
         print(json.dumps(res), flush=True)
         return
 
-    # Per-step phase events on a sample of the timed steps (created and touched once so the
-    # runtime objects exist).
-    every = max(1, args.event_every)
-    sampled = [i for i in range(args.steps) if i % every == every // 2] or [args.steps - 1]   # short runs: the last
-    evs = {i: [torch.cuda.Event(enable_timing=True) for _ in range(8)] for i in sampled}
-    for e8 in evs.values():
-        for e in e8:
-            e.record()
-    torch.cuda.synchronize()
-
+    # The timed loop records no events: each record costs the GPU time of its own.
     tokens = 0
-    step_ids = []
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        e8 = evs.get(i)
-        n, k = one_step(e8[:6] if e8 else None, e8[6:] if e8 else None)
+    for _ in range(args.steps):
+        n, _ = one_step()
         tokens += n
-        step_ids.append(k)
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
-
-    dev_step_ms = [e8[6].elapsed_time(e8[7]) for e8 in evs.values()]
     elt = 2
 
-    # Roofline pass: whole cycles (at least 20 steps) with HIP events around every attention
-    # launch and its combine, after the timed loop, so the timed figures carry no extra records.
+    # Event pass: whole cycles (at least 20 steps) with HIP events around every attention launch,
+    # its combine and the whole step, after the timed loop: the roofline figure and the device
+    # step latency (which therefore carries the records' own cost, a few µs a step).
     n_ev = cb_steps * max(2, -(-20 // cb_steps))
-    ev_pass = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(n_ev)]
-    for e6 in ev_pass:
-        for e in e6:
+    ev_pass = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(n_ev)]
+    for e8 in ev_pass:
+        for e in e8:
             e.record()
     torch.cuda.synchronize()
     state["sched"], state["k"] = cb.cb_sched_clone(snapshot), 0
     ev_steps = []
-    for e6 in ev_pass:
-        _, k = one_step(e6)
+    for e8 in ev_pass:
+        _, k = one_step(e8[:6], e8[6:])
         ev_steps.append(k)
     torch.cuda.synchronize()
-    dec_ms = [e6[0].elapsed_time(e6[1]) for e6 in ev_pass]      # the attention kernel
-    cmb_ms = [e6[4].elapsed_time(e6[5]) for e6 in ev_pass]
+    dec_ms = [e8[0].elapsed_time(e8[1]) for e8 in ev_pass]      # the attention kernel
+    dev_step_ms = [e8[6].elapsed_time(e8[7]) for e8 in ev_pass]
+    cmb_ms = [e8[4].elapsed_time(e8[5]) for e8 in ev_pass]
     abytes = [decode_bytes(metas[k], w, elt) + chunk_bytes(metas[k], w, elt) for k in ev_steps]
     attn_avg_s = sum(dec_ms) / len(dec_ms) / 1e3
     achieved = sum(abytes) / len(abytes) / attn_avg_s / 1e9
@@ -764,14 +748,14 @@ def main():
     del flush
     traffic = committed_traffic("attn_kernel", w.name)
     # What the chunk rows add to a mixed step: the in-step attention + combine minus the warm
-    # decode-only launch of the same step's metadata, per sampled step with chunk rows.
+    # decode-only launch of the same step's metadata, per event-pass step with chunk rows.
     iso_dec = {}
     for k, t in dec_raw:
         iso_dec.setdefault(k, []).append(t)
     marg, mflops = [], []
-    for e6, k in zip(ev_pass, ev_steps):
+    for e8, k in zip(ev_pass, ev_steps):
         if k in iso_dec and chunk_flops(metas[k], w) > 0:
-            marg.append(e6[0].elapsed_time(e6[1]) + e6[4].elapsed_time(e6[5]) - sum(iso_dec[k]) / len(iso_dec[k]))
+            marg.append(e8[0].elapsed_time(e8[1]) + e8[4].elapsed_time(e8[5]) - sum(iso_dec[k]) / len(iso_dec[k]))
             mflops.append(chunk_flops(metas[k], w))
     chunk_marginal = None
     if marg:
@@ -823,8 +807,7 @@ def main():
         "device_step_us": sum(dev_step_ms) / len(dev_step_ms) * 1e3,
         "device_step_us_p10_p50_p90": [pct(dev_step_ms, q) * 1e3 for q in (0.1, 0.5, 0.9)],
         "end_to_end_ms_p10_p50_p90": [pct(e2e, q) for q in (0.1, 0.5, 0.9)],
-        "event_sampled_steps": len(sampled),
-        "roofline_pass_launches": len(dec_ms),
+        "event_pass_steps": len(dec_ms),
         "graph_replay": graph_rep,
     }
     if not args.no_cpu_baseline:

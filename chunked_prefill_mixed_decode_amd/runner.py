@@ -13,6 +13,7 @@ over a process's long-lived objects takes about a millisecond.  A serving loop s
 """
 from __future__ import annotations
 
+import ctypes
 import math
 
 import torch
@@ -20,6 +21,51 @@ import torch
 from . import binding as cb
 
 SENTINEL_BITS = {torch.bfloat16: -1, torch.float32: -1}   # all-ones: a NaN that no write produces
+
+
+class PullMark:
+    """Tells the host when the metadata pull from one pinned buffer has finished.
+
+    A HIP event created without timing and without the system-scope fence (the HIP runtime's
+    hipEventDisableTiming | hipEventDisableSystemFence): the host only needs to know that the pull
+    kernel has read the buffer before rewriting it, and no device write has to become visible to
+    the host, so the record needs no system-scope release (a device-wide cache writeback each
+    time).  Measured on the budget-512 step loop: 420.1 us per step with a default event recorded
+    after each pull, 418.5-418.7 with this one.  The calls go to the HIP runtime libcb.so is linked
+    against, through its handle."""
+
+    _FLAGS = 0x2 | 0x20000000
+
+    def __init__(self):
+        hip = cb._lib()
+        for name, args in (("hipEventCreateWithFlags", [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]),
+                           ("hipEventRecord", [ctypes.c_void_p, ctypes.c_void_p]),
+                           ("hipEventSynchronize", [ctypes.c_void_p]),
+                           ("hipEventDestroy", [ctypes.c_void_p])):
+            fn = getattr(hip, name)
+            fn.restype, fn.argtypes = ctypes.c_int, args
+        self._hip = hip
+        self._ev = ctypes.c_void_p()
+        self._call("hipEventCreateWithFlags", ctypes.byref(self._ev), self._FLAGS)
+
+    def _call(self, name, *args):
+        rc = getattr(self._hip, name)(*args)
+        if rc != 0:
+            raise RuntimeError(f"{name} failed with HIP error {rc}")
+
+    def record(self, stream: torch.cuda.Stream):
+        self._call("hipEventRecord", self._ev, ctypes.c_void_p(stream.cuda_stream))
+
+    def synchronize(self):
+        self._call("hipEventSynchronize", self._ev)
+
+    def __del__(self):
+        ev = getattr(self, "_ev", None)
+        if ev is not None and ev.value:
+            try:
+                self._hip.hipEventDestroy(ev)
+            except Exception:       # interpreter shutdown
+                pass
 
 
 def round_up(x: int, step: int) -> int:
@@ -69,7 +115,8 @@ class MixedStepRunner:
         # order); host buffer i is rewritten (step n + 2) only after that kernel has finished.
         self.bufs = [cb.StepBuffers(cap_seqs, cap_tokens, cap_blocks, plan_ints=plan_ints) for _ in range(2)]
         self.dev_flat = [torch.empty_like(b.flat, device=self.device) for b in self.bufs]
-        self.copied = [None, None]                 # kernel reading host buffer i finished
+        self.marks = [None, None]                  # PullMarks, made at the first pull (host-only use needs none)
+        self.copied = [None, None]                 # mark of the last pull from host buffer i
         self.ring = 0
         self.workspace = torch.empty(0, dtype=torch.uint8, device=self.device)
 
@@ -133,10 +180,14 @@ class MixedStepRunner:
         return views
 
     def mark_pulled(self, meta: cb.StepMeta):
-        """Record that the pinned buffer of ``meta`` may be rewritten once the stream gets here."""
-        ev = torch.cuda.Event()
-        ev.record(torch.cuda.current_stream(self.device))
-        self.copied[meta.buf_index] = ev
+        """Record that the pinned buffer of ``meta`` may be rewritten once the stream gets here.
+        (A mark re-recorded before anyone waited for it only moves later in the stream, which
+        keeps the wait in ``build`` correct.)"""
+        mark = self.marks[meta.buf_index]
+        if mark is None:
+            mark = self.marks[meta.buf_index] = PullMark()
+        mark.record(torch.cuda.current_stream(self.device))
+        self.copied[meta.buf_index] = mark
 
     # ---- device work ---------------------------------------------------------------------------
     def append(self, dev: dict, q, k, v, q_out):
