@@ -129,10 +129,10 @@ def isolation_pass(g, metas, qrots, outs, w, reps: int, flush=None, kinds=("deco
     dec, chk = [], []
 
     def events(n):
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n)] for _ in range(reps)]
+        evs = [[timing_event() for _ in range(n)] for _ in range(reps)]
         for row in evs:
             for e in row:
-                e.record()                       # creates them (torch's record flag); calls re-record
+                e.record()                       # touched once before the timed launches
         return evs
 
     for k, meta in enumerate(metas):
@@ -201,6 +201,14 @@ def isolation_pass(g, metas, qrots, outs, w, reps: int, flush=None, kinds=("deco
     return dec, chk
 
 
+def timing_event():
+    """A HIP timing event recorded without the system-scope fence (``runner.HipEvent``): a default
+    event's record writes back the device's caches before it completes, time that lands inside the
+    interval it brackets."""
+    from chunked_prefill_mixed_decode_amd.runner import HipEvent
+    return HipEvent(timing=True)
+
+
 def pct(xs, q):
     xs = sorted(xs)
     return xs[min(len(xs) - 1, max(0, int(round(q * (len(xs) - 1)))))]
@@ -226,7 +234,7 @@ def linear_pass(w, dev, tokens: dict, reps: int = 20):
             nws = cb.cb_linear_workspace_bytes(T, N, K)
             ws = torch.empty(nws, dtype=torch.uint8, device=dev) if nws else None
             cb.cb_linear(x, wt, y, ws)
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0, e1 = timing_event(), timing_event()
             e0.record()
             for _ in range(reps):
                 cb.cb_linear(x, wt, y, ws)
@@ -310,7 +318,7 @@ def library_attention(metas, w, dev, reps: int = 3, max_keys: int = 65536):
                 return torch.nn.functional.scaled_dot_product_attention(q, kv[0], kv[1], attn_mask=mask,
                                                                         enable_gqa=w.Hq != w.Hkv)
             call()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0, e1 = timing_event(), timing_event()
             e0.record()
             for _ in range(reps):
                 call()
@@ -698,7 +706,7 @@ def main():
     # its combine and the whole step, after the timed loop: the roofline figure and the device
     # step latency (which therefore carries the records' own cost, a few µs a step).
     n_ev = cb_steps * max(2, -(-20 // cb_steps))
-    ev_pass = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(n_ev)]
+    ev_pass = [[timing_event() for _ in range(8)] for _ in range(n_ev)]
     for e8 in ev_pass:
         for e in e8:
             e.record()

@@ -23,41 +23,59 @@ from . import binding as cb
 SENTINEL_BITS = {torch.bfloat16: -1, torch.float32: -1}   # all-ones: a NaN that no write produces
 
 
-class PullMark:
-    """Tells the host when the metadata pull from one pinned buffer has finished.
+class HipEvent:
+    """A HIP event recorded without the system-scope fence (the runtime's
+    hipEventDisableSystemFence), with or without timing.
 
-    A HIP event created without timing and without the system-scope fence (the HIP runtime's
-    hipEventDisableTiming | hipEventDisableSystemFence): the host only needs to know that the pull
-    kernel has read the buffer before rewriting it, and no device write has to become visible to
-    the host, so the record needs no system-scope release (a device-wide cache writeback each
-    time).  Measured on the budget-512 step loop: 420.1 us per step with a default event recorded
-    after each pull, 418.5-418.7 with this one.  The calls go to the HIP runtime libcb.so is linked
-    against, through its handle."""
+    A default event's record ends in a system-scope release: a writeback of the device's caches
+    before the event completes, which the work behind it waits for.  Neither use here needs it:
+    the pull marks (``MixedStepRunner.mark_pulled``) only tell the host that a pull kernel has
+    read its pinned buffer -- no device write has to become visible to the host -- and timing
+    events only take timestamps.  Measured on the budget-512 step loop: 420.1 us per step with a
+    default event after each pull, 418.5-418.7 with this one.  Duck-typed as ``torch.cuda.Event``
+    for ``record``, ``synchronize``, ``elapsed_time`` and ``cuda_event`` (the handle the timed
+    attention call records).  The calls go to the HIP runtime libcb.so is linked against, through
+    its handle."""
 
-    _FLAGS = 0x2 | 0x20000000
+    _DISABLE_TIMING, _NO_SYSTEM_FENCE = 0x2, 0x20000000
+    _SIGS = (("hipEventCreateWithFlags", [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]),
+             ("hipEventRecord", [ctypes.c_void_p, ctypes.c_void_p]),
+             ("hipEventSynchronize", [ctypes.c_void_p]),
+             ("hipEventElapsedTime", [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]),
+             ("hipEventDestroy", [ctypes.c_void_p]))
 
-    def __init__(self):
+    def __init__(self, timing: bool = False):
         hip = cb._lib()
-        for name, args in (("hipEventCreateWithFlags", [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]),
-                           ("hipEventRecord", [ctypes.c_void_p, ctypes.c_void_p]),
-                           ("hipEventSynchronize", [ctypes.c_void_p]),
-                           ("hipEventDestroy", [ctypes.c_void_p])):
+        for name, args in self._SIGS:
             fn = getattr(hip, name)
             fn.restype, fn.argtypes = ctypes.c_int, args
         self._hip = hip
         self._ev = ctypes.c_void_p()
-        self._call("hipEventCreateWithFlags", ctypes.byref(self._ev), self._FLAGS)
+        flags = self._NO_SYSTEM_FENCE | (0 if timing else self._DISABLE_TIMING)
+        self._call("hipEventCreateWithFlags", ctypes.byref(self._ev), flags)
 
     def _call(self, name, *args):
         rc = getattr(self._hip, name)(*args)
         if rc != 0:
             raise RuntimeError(f"{name} failed with HIP error {rc}")
 
-    def record(self, stream: torch.cuda.Stream):
+    @property
+    def cuda_event(self) -> int:
+        return self._ev.value
+
+    def record(self, stream: torch.cuda.Stream | None = None):
+        if stream is None:
+            stream = torch.cuda.current_stream()
         self._call("hipEventRecord", self._ev, ctypes.c_void_p(stream.cuda_stream))
 
     def synchronize(self):
         self._call("hipEventSynchronize", self._ev)
+
+    def elapsed_time(self, end: "HipEvent") -> float:
+        """Milliseconds from this event to ``end`` (both recorded with timing and complete)."""
+        ms = ctypes.c_float()
+        self._call("hipEventElapsedTime", ctypes.byref(ms), self._ev, end._ev)
+        return ms.value
 
     def __del__(self):
         ev = getattr(self, "_ev", None)
@@ -115,7 +133,7 @@ class MixedStepRunner:
         # order); host buffer i is rewritten (step n + 2) only after that kernel has finished.
         self.bufs = [cb.StepBuffers(cap_seqs, cap_tokens, cap_blocks, plan_ints=plan_ints) for _ in range(2)]
         self.dev_flat = [torch.empty_like(b.flat, device=self.device) for b in self.bufs]
-        self.marks = [None, None]                  # PullMarks, made at the first pull (host-only use needs none)
+        self.marks = [None, None]                  # HipEvents, made at the first pull (host-only use needs none)
         self.copied = [None, None]                 # mark of the last pull from host buffer i
         self.ring = 0
         self.workspace = torch.empty(0, dtype=torch.uint8, device=self.device)
@@ -185,7 +203,7 @@ class MixedStepRunner:
         keeps the wait in ``build`` correct.)"""
         mark = self.marks[meta.buf_index]
         if mark is None:
-            mark = self.marks[meta.buf_index] = PullMark()
+            mark = self.marks[meta.buf_index] = HipEvent()
         mark.record(torch.cuda.current_stream(self.device))
         self.copied[meta.buf_index] = mark
 
